@@ -1,0 +1,319 @@
+"""Benchmark of the ConvRot packed-INT4 linear on one MI355X.
+
+Headline step: the W4A8 ConvRot decode linear at M = 1, K = 3840, N = 10240,
+G = 64, per-group (64) bf16 weight scales -- rotate-quant of the activation row
+followed by the weight-streaming GEMV, i.e. exactly the two launches
+ck_w4a8_linear makes (issued here through ck_rotate_quant and ck_w4_gemv so
+that HIP events can bracket the GEMV).  The metric is packed-weight bandwidth:
+N * K / 2 bytes per step over the step time.  Inputs are resident in HBM before
+timing starts; the step cycles through enough weight copies (> 512 MiB) that
+every step reads its weights from HBM, not from the 256 MiB Infinity Cache.
+
+After the timed region the other metric figures are measured the same way
+(ConvRot linear microseconds and int8 TOPS at M = 8192, the decode GEMV at
+M = 4 and 8, standalone rotate-quant, the AWQ W4A16 GEMV) and reported under
+"also"; the CPU oracle is timed on a bounded sample under "cpu_baseline".
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POPS)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_decode_gemv_m1_k3840_n10240_traffic.txt")
+GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_skinny.hip", "packed_int4_convrot_amd/csrc/ck_device.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=32, help="weight copies cycled through (cold cache)")
+    return ap.parse_args()
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch_alg):
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, or None
+    when the kernel sources changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.loads(f.read().split("JSON:", 1)[1])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("sources_sha") != sources_sha(GEMV_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path, run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import packed_int4_convrot_amd as ck
+    import workloads
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------------------ headline
+    name = "w4a8_decode_gemv_k3840_n10240_g64"
+    w = workloads.WORKLOADS[name]
+    M, K, N, G = 1, w["K"], w["N"], w["G"]
+    inp = workloads.workload_inputs(name, M=M)
+    log("bench: generating %d weight copies of %.1f MB" % (args.copies, N * K / 2 / 1e6))
+    x = bf16(inp["x"])
+    packed0 = u8(inp["packed"])
+    scales0 = bf16(inp["w_scales"])
+    packs = [packed0] + [packed0.clone() for _ in range(args.copies - 1)]
+    scls = [scales0] + [scales0.clone() for _ in range(args.copies - 1)]
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    rs = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        ck.rotate_quant(x, G, 8, codes, rs)
+        if ev is not None:
+            ev[0].record(stream)
+        ck.gemv(codes, rs, packs[i % args.copies], scls[i % args.copies], True, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    packed_bytes = N * K // 2
+    value = packed_bytes / (ms_step * 1e-3) / 1e9
+
+    alg_bytes = packed_bytes + (K // 64) * N * 2 + M * K + M * 4 + M * N * 2
+    achieved = alg_bytes / (gemv_ms * 1e-3) / 1e9
+    traffic = measured_traffic(alg_bytes)
+    log("bench: step %.2f us (wall %.2f us), GEMV %.2f us, %.0f GB/s packed" %
+        (ms_step * 1e3, wall / args.steps * 1e6, gemv_ms * 1e3, value))
+
+    # the same step through the single whole-linear entry point, for comparison
+    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(args.steps):
+        ck.linear(x, G, 8, packs[i % args.copies], scls[i % args.copies], True, out=out, workspace=ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    linear_us = a.elapsed_time(b) / args.steps * 1e3
+
+    result = {
+        "metric": "ConvRot linear us + int8 TOPS (M=8192) and packed-weight GB/s (M=1 GEMV)",
+        "value": round(value, 1),
+        "unit": "GB/s (packed weight, M=1 W4A8 ConvRot decode linear)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,1) activations with x20 outlier columns, uniform uint4 codes, "
+                "uniform [0.002,0.02] bf16 group scales)",
+        "config": {"workload": "w4a8_convrot_decode_linear", "M": M, "K": K, "N": N, "G": G,
+                   "weight_scales": "per-group (64), bf16", "weight_copies_cycled": args.copies,
+                   "step": "ck_rotate_quant + ck_w4_gemv (the launches of ck_w4a8_linear)"},
+        "roofline": {"bound": "hbm", "kernel": "w4_skinny_kernel (decode GEMV)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(gemv_ms * 1e3, 3)},
+        "whole_linear_entry_us": round(linear_us, 3),
+    }
+
+    # ------------------------------------------------------------ extras
+    if not args.no_extras:
+        result["also"] = extras(ck, workloads, torch, dev, bf16, u8, stream)
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(workloads, inp, G, packed_bytes)
+
+    print(json.dumps(result), flush=True)
+
+
+def _time(fn, stream, iters, warmup=3):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(iters):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e3  # us
+
+
+def extras(ck, workloads, torch, dev, bf16, u8, stream):
+    res = {}
+    # decode GEMV at M = 4, 8 (cold weights)
+    name = "w4a8_decode_gemv_k3840_n10240_g64"
+    w = workloads.WORKLOADS[name]
+    K, N = w["K"], w["N"]
+    base = workloads.workload_inputs(name, M=8)
+    packs = [u8(base["packed"]) for _ in range(32)]
+    scl = bf16(base["w_scales"])
+    for M in (4, 8):
+        x = bf16(base["x"][:M])
+        codes, rs = ck.rotate_quant(x, 64, 8)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = _time(lambda i: ck.gemv(codes, rs, packs[i % 32], scl, True, out=out), stream, 100)
+        lin = _time(lambda i: ck.linear(x, 64, 8, packs[i % 32], scl, True, out=out), stream, 100)
+        res["w4a8_decode_gemv_m%d" % M] = {"gemv_us": round(us, 3), "linear_us": round(lin, 3),
+                                          "packed_GBps": round(N * K / 2 / us / 1e3, 1)}
+    del packs
+    log("bench: decode extras done")
+
+    # M = 32 W4A8 linear (per-group scales)
+    name = "w4a8_linear_m32_k3840_n3840_g64"
+    w = workloads.WORKLOADS[name]
+    inp = workloads.workload_inputs(name)
+    x = bf16(inp["x"])
+    packs = [u8(inp["packed"]) for _ in range(64)]
+    scl = bf16(inp["w_scales"])
+    out = torch.empty((32, w["N"]), dtype=torch.bfloat16, device=dev)
+    us = _time(lambda i: ck.linear(x, 64, 8, packs[i % 64], scl, True, out=out), stream, 100)
+    res["w4a8_linear_m32_k3840_n3840_g64"] = {"linear_us": round(us, 3)}
+    del packs
+    log("bench: M=32 done")
+
+    # M = 8192 W4A4 linears (per-channel scales): rotate-quant + GEMM
+    for name in ("w4a4_linear_m8192_k3840_n3840_g64", "w4a4_linear_m8192_k10240_n3840_g256"):
+        w = workloads.WORKLOADS[name]
+        inp = workloads.workload_inputs(name)
+        M, K, N, G = w["M"], w["K"], w["N"], w["G"]
+        x = bf16(inp["x"])
+        packed = u8(inp["packed"])
+        scl = bf16(inp["w_scales"])
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        codes, rs = ck.rotate_quant(x, G, 4)
+        lin = _time(lambda i: ck.linear(x, G, 4, packed, scl, False, out=out), stream, 20)
+        rq = _time(lambda i: ck.rotate_quant(x, G, 4, codes, rs), stream, 20)
+        gm = _time(lambda i: ck.gemm_q(codes, rs, packed, scl, False, out=out), stream, 20)
+        ops = 2.0 * M * N * K
+        rq_bytes = M * K * 2 + M * K + M * 4
+        res[name] = {"linear_us": round(lin, 2), "rotate_quant_us": round(rq, 2), "gemm_us": round(gm, 2),
+                     "gemm_int8_TOPS": round(ops / gm / 1e6, 1),
+                     "gemm_frac_int8_peak": round(ops / gm / 1e6 / INT8_PEAK_TOPS, 4),
+                     "linear_int8_TOPS": round(ops / lin / 1e6, 1),
+                     "rotate_quant_GBps": round(rq_bytes / rq / 1e3, 1),
+                     "rotate_quant_frac_hbm": round(rq_bytes / rq / 1e3 / HBM_PEAK_GBS, 4)}
+        del x, packed, out, codes
+        log("bench: %s done" % name)
+
+    # standalone rotate-quant, strided [8192, 10240] in [8192, 10752]
+    name = "rotate_quant_m8192_k10240_ld10752"
+    w = workloads.WORKLOADS[name]
+    M, K = w["M"], w["K"]
+    xs = [bf16(workloads.workload_inputs(name)["x"])]
+    xs.append(xs[0].clone())  # two copies: 2 x 176 MB > the 256 MB Infinity Cache
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    rs = torch.empty((M,), dtype=torch.float32, device=dev)
+    rq_bytes = M * K * 2 + M * K + M * 4
+    for G in w["Gs"]:
+        us = _time(lambda i: ck.rotate_quant(xs[i % 2][:, :K], G, 8, codes, rs), stream, 20)
+        res["rotate_quant_m8192_k10240_ld10752_g%d" % G] = {
+            "us": round(us, 2), "GBps": round(rq_bytes / us / 1e3, 1),
+            "frac_hbm": round(rq_bytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del xs
+    log("bench: rotate-quant done")
+
+    # AWQ W4A16 GEMV
+    name = "awq_w4a16_gemv_m1_k3072_n18432"
+    w = workloads.WORKLOADS[name]
+    d = workloads.workload_inputs(name)
+    x = bf16(d["x"])
+    packs = [u8(d["packed"]) for _ in range(24)]
+    s, z = bf16(d["scales"]), bf16(d["zeros"])
+    out = torch.empty((1, w["N"]), dtype=torch.bfloat16, device=dev)
+    us = _time(lambda i: ck.w4a16_gemv(x, packs[i % 24], s, z, out=out), stream, 100)
+    pb = w["N"] * w["K"] // 2
+    total = pb + 2 * 2 * (w["K"] // 64) * w["N"] + w["K"] * 2 + w["N"] * 2
+    res[name] = {"us": round(us, 3), "packed_GBps": round(pb / us / 1e3, 1),
+                 "total_GBps": round(total / us / 1e3, 1), "frac_hbm": round(total / us / 1e3 / HBM_PEAK_GBS, 4)}
+    log("bench: awq done")
+    return res
+
+
+def cpu_baseline(workloads, inp, G, packed_bytes):
+    """The oracle (single-threaded C, fp64 sums) on the same M = 1 decode step, repeated
+    for a bounded ~10 s of host time."""
+    import oracle
+    oracle.build()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.linear(inp["x"], G, 8, inp["packed"], inp["w_scales"], True)
+        n += 1
+        if time.perf_counter() - t0 > 10.0 or n >= 200:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(packed_bytes / dt / 1e9, 4), "unit": "GB/s (packed weight, M=1 step)",
+            "cores": 1, "kind": "oracle",
+            "sample": "%d full M=1 steps (rotation by explicit H_64 product, quantisation, unpack, "
+                      "exact integer sums, fp64 epilogue), %.3f s each" % (n, dt)}
+
+
+if __name__ == "__main__":
+    main()

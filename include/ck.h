@@ -1,0 +1,211 @@
+/*
+ * ck.h - C ABI of the ConvRot packed-INT4 linear for AMD Instinct MI355X (gfx950).
+ *
+ * The library (libck.so) implements one hot path with hand-written HIP kernels:
+ *
+ *   x (bf16 [M,K])
+ *     -> group-wise Walsh-Hadamard rotation (contiguous groups of G columns,
+ *        H_G / sqrt(G), Sylvester natural order)
+ *     -> rowwise absmax quantisation to int8 (qmax 127, "W4A8") or int4
+ *        (qmax 7, "W4A4"; one value per byte)
+ *     -> integer matmul with packed uint4 weights, int32 accumulation
+ *     -> scale epilogue (row scale x weight scale), bf16 out.
+ *
+ * Sources (page titles):
+ *  [RQ]   "[PR #155] [Feat][Ascend] Add fused RotateQuant backend", section
+ *         "What this PR does": quantize_and_rotate_rowwise fuses the rotation
+ *         matmul and the dynamic rowwise quantisation; group sizes 16, 64 and
+ *         256; non-contiguous inputs; unsupported shapes are declined; the
+ *         public API keeps scales positive (all-zero rows).
+ *  [AWQ]  "comfy_kitchen/tensor/awq_w4a16.py", module docstring and
+ *         dequantize(): qweight (N, K//2) packed uint4, bits 0..3 = column
+ *         2j, bits 4..7 = column 2j+1, value = code - 8; per-group scales and
+ *         zeros of shape (K // G, N); W = (q - 8) * s + z.
+ *  [GEMV] "[PR #182] HIP port of #176: W4A8 decode GEMV and fused
+ *         GatedDeltaNet decode", description: register-side int4 decode feeding
+ *         integer dot products, rowwise x weight-scale epilogue.
+ *  [SD]   "feat: support packed INT4 convrot models" (stable-diffusion.cpp),
+ *         summary: W4A4 and W4A8 packed-INT4 ConvRot matmul with optional bias
+ *         and input scale; 64-element ConvRot groups.
+ *  [W4A4] "[PR #212] [Perf][Ascend] Reuse unpacked W4A4 weights within an
+ *         explicit scope", summary: the public ConvRot W4A4 Linear dispatcher;
+ *         packed weights may be int8 or uint8 tensors and may be strided.
+ *
+ * Conventions for every entry point:
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees, copies to the host or synchronises; work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the null stream) and inputs
+ *    must stay alive until that work completes.  Outputs are fully written.
+ *  - Matrices are row-major with explicit row strides in ELEMENTS (bytes for
+ *    the packed weights, whose element is a byte holding two codes).
+ *  - Arguments are validated before anything is enqueued.  A failed check
+ *    returns a status and enqueues nothing; ck_last_error_msg() then gives a
+ *    thread-local description.  Faults inside a kernel surface at the
+ *    caller's next synchronisation.
+ *  - M == 0 is a valid no-op.
+ *  - Shape limits (CK_ERR_UNSUPPORTED otherwise): G in {16, 64, 256};
+ *    bits in {8, 4}; K % 64 == 0 and 64 <= K <= 32768 (K % G != 0 is
+ *    CK_ERR_INVALID_ARG: a row must split into whole groups);
+ *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales.
+ *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
+ *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
+ *    ldw % 16 == 0; out 4-byte aligned with ldo % 2 == 0.
+ */
+#ifndef CK_H
+#define CK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CK_OK = 0,
+    CK_ERR_INVALID_ARG = 1, /* null pointer, bad stride/alignment, overlap, K%G, ... */
+    CK_ERR_UNSUPPORTED = 2, /* valid request outside the shapes this build serves   */
+    CK_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required   */
+    CK_ERR_HIP = 4          /* the HIP runtime refused a launch                      */
+} ck_status;
+
+/* Weight-scale kinds.
+ * CK_WS_PER_CHANNEL: bf16 [N], one scale per output column.
+ * CK_WS_PER_GROUP:   bf16 [K/Gw, N] (N contiguous), one scale per (K-group, n),
+ *                    Gw = 64; same layout as the per-group scales in [AWQ]. */
+typedef enum { CK_WS_PER_CHANNEL = 0, CK_WS_PER_GROUP = 1 } ck_wscale_kind;
+
+/* Static string for a status code. */
+const char *ck_status_str(int status);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char *ck_last_error_msg(void);
+
+/* Library version, e.g. "ck 0.1 gfx950". */
+const char *ck_version(void);
+
+/*
+ * ck_rotate_quant  [RQ]
+ * Rotate each contiguous group of G columns of every row of x by H_G/sqrt(G)
+ * and quantise the row by its absolute maximum a (over the whole row):
+ *   row_scales[m] = a / qmax, codes[m,k] = round_half_even(xr[m,k] * qmax / a)
+ * with qmax = 127 (bits 8) or 7 (bits 4); the multiply uses the fp32
+ * reciprocal qmax/a and the codes never exceed +-qmax.  An all-zero row gets
+ * codes 0 and row_scales[m] = 1.0 (positive-scale contract of [RQ]).
+ *   x          bf16 [M, ldx]; the first K columns of each row are read
+ *   codes      int8 [M, ldq]; the first K columns are written (int4 codes are
+ *              stored one value per byte, range [-7, 7])
+ *   row_scales fp32 [M]
+ * codes/row_scales must not overlap x.
+ */
+int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                    int32_t bits, int8_t *codes, int64_t ldq, float *row_scales,
+                    void *stream);
+
+/*
+ * ck_w4_gemm_q  [GEMV] [AWQ] [SD]
+ * Matmul half of the linear, for activations that are already rotated and
+ * quantised (for example by ck_rotate_quant, or reused across linears that
+ * share an input as [SD] does with its activation cache):
+ *   acc[m,n]    = sum_k codes[m,k] * (q[n,k] - 8)               (exact int32)
+ *   per channel: out[m,n] = row_scales[m] * w_scales[n] * acc[m,n]
+ *   per group:   out[m,n] = row_scales[m] * sum_g w_scales[g,n] * acc_g[m,n]
+ *   (+ bias[n] when bias != NULL), rounded to bf16 (nearest even).
+ *   codes      int8 [M, ldq] (int8 or int4 values)
+ *   row_scales fp32 [M]
+ *   packed     uint8 [N, ldw]: byte j of row n holds column 2j in bits 0..3
+ *              and column 2j+1 in bits 4..7; code q in [0,15] means q - 8
+ *   w_scales   bf16, layout given by scale_kind (ck_wscale_kind); Gw = 64
+ *   bias       bf16 [N] or NULL
+ *   out        bf16 [M, ldo]; must not overlap any input
+ * Any M >= 0.  Small M (<= 64, with K small enough for the activations to
+ * stay in registers) runs the weight-streaming kernel of ck_w4_gemv; every
+ * other shape runs the tiled MFMA GEMM.
+ */
+int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
+                 int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                 int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                 uint16_t *out, int64_t ldo, void *stream);
+
+/*
+ * ck_w4_gemv  [GEMV]
+ * Decode form of ck_w4_gemm_q for 1 <= M <= 8 and K <= 8192
+ * (CK_ERR_UNSUPPORTED otherwise): the same arithmetic, run by the kernel that
+ * streams the packed weights once.
+ */
+int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
+               int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+               int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+               uint16_t *out, int64_t ldo, void *stream);
+
+/* Bytes of workspace ck_w4a8_linear / ck_w4a4_linear need for M rows of K
+ * columns: the int8 codes [M, K] plus the fp32 row scales, each 256-byte
+ * aligned inside the workspace. */
+size_t ck_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * ck_w4a8_linear  [SD] [RQ] [GEMV]
+ * Whole ConvRot linear with int8 activations:
+ *   ck_rotate_quant(x, G, bits = 8) into `ws`, then ck_w4_gemm_q on `ws`,
+ * both on `stream`.  x_scale (> 0, finite; 1.0 for none) is the input-scale
+ * factor of [SD]: the result is the linear of x_scale * x, obtained by
+ * multiplying each row scale by x_scale (the codes of x_scale * x equal those
+ * of x whenever x_scale is a power of two).
+ *   ws        device workspace of at least ck_linear_workspace_bytes(M, K)
+ *             bytes, 256-byte aligned; CK_ERR_WORKSPACE if smaller or NULL
+ *             (with M > 0).  Its contents are scratch.
+ */
+int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                   int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                   float x_scale, uint16_t *out, int64_t ldo, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/*
+ * ck_w4a4_linear  [W4A4] [SD]
+ * As ck_w4a8_linear with int4 activations (qmax 7, symmetric).
+ */
+int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                   int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                   float x_scale, uint16_t *out, int64_t ldo, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/*
+ * ck_w4a16_gemv  [AWQ]
+ * AWQ W4A16 product with fp activations (no activation quantisation):
+ *   W[n,k]   = (q[n,k] - 8) * scales[k/Gw, n] + zeros[k/Gw, n]
+ *   out[m,n] = sum_k x[m,k] * W[n,k]  (+ bias[n]), fp32 arithmetic, bf16 out.
+ *   x       bf16 [M, ldx], 1 <= M <= 8 and K <= 4096 (CK_ERR_UNSUPPORTED
+ *           otherwise)
+ *   packed  uint8 [N, ldw] as in ck_w4_gemm_q
+ *   scales, zeros  bf16 [K/Gw, N], Gw = 64
+ *   bias    bf16 [N] or NULL;  out bf16 [M, ldo]
+ * The weight is never materialised; it is decoded in registers.
+ */
+int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                  const uint8_t *packed, int64_t ldw, const uint16_t *scales,
+                  const uint16_t *zeros, int32_t Gw, int64_t N, const uint16_t *bias,
+                  uint16_t *out, int64_t ldo, void *stream);
+
+/* ---------------------------------------------------------------- test hooks
+ * Same device code paths as above with a debug epilogue, so that each stage
+ * can be compared exactly with the oracle. */
+
+/* The rotation of ck_rotate_quant as held in registers, divided by sqrt(G)
+ * (exact, sqrt(G) is a power of two): xr fp32 [M, ldr]. */
+int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                       float *xr, int64_t ldr, void *stream);
+
+/* The integer accumulators of ck_w4_gemm_q (kernel chosen by M exactly as
+ * there): acc int32 [M, lda], acc[m,n] = sum_k codes[m,k] * (q[n,k] - 8). */
+int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,
+                     const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,
+                     int64_t lda, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CK_H */

@@ -1,0 +1,222 @@
+"""Python binding of libck, the MI355X ConvRot packed-INT4 linear.
+
+Argument marshalling only: tensors are checked for dtype, device and layout,
+their pointers and strides are handed to the C ABI (include/ck.h) together with
+torch's current HIP stream, and a status other than CK_OK becomes an exception
+(ValueError for invalid arguments, RuntimeError otherwise).  Every step of the
+computation runs in the HIP kernels of libck.so; there is no other code path.
+Importing this package fails if libck.so has not been built
+(``python -m packed_int4_convrot_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libck.so")
+
+CK_OK, CK_ERR_INVALID_ARG, CK_ERR_UNSUPPORTED, CK_ERR_WORKSPACE, CK_ERR_HIP = range(5)
+CK_WS_PER_CHANNEL, CK_WS_PER_GROUP = 0, 1
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "ck_status_str": ([_i32], ctypes.c_char_p),
+    "ck_last_error_msg": ([], ctypes.c_char_p),
+    "ck_version": ([], ctypes.c_char_p),
+    "ck_rotate_quant": ([_p, _i64, _i64, _i64, _i32, _i32, _p, _i64, _p, _p], ctypes.c_int),
+    "ck_w4_gemm_q": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i32, _i64, _p, _p, _i64, _p],
+                     ctypes.c_int),
+    "ck_w4_gemv": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i32, _i64, _p, _p, _i64, _p],
+                   ctypes.c_int),
+    "ck_linear_workspace_bytes": ([_i64, _i64], _sz),
+    "ck_w4a8_linear": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p, _f32, _p,
+                        _i64, _p, _sz, _p], ctypes.c_int),
+    "ck_w4a4_linear": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p, _f32, _p,
+                        _i64, _p, _sz, _p], ctypes.c_int),
+    "ck_w4a16_gemv": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _i64, _p, _p, _i64, _p],
+                      ctypes.c_int),
+    "ck_test_rotate_f32": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p], ctypes.c_int),
+    "ck_test_gemm_i32": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+}
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libck.so is not built (expected at %s); run `python -m packed_int4_convrot_amd.build`"
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load_library()
+
+
+class CKError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (lib.ck_status_str(status).decode(), msg))
+        self.status = status
+
+
+class CKInvalidArgument(CKError, ValueError):
+    pass
+
+
+def last_error() -> str:
+    return lib.ck_last_error_msg().decode()
+
+
+def version() -> str:
+    return lib.ck_version().decode()
+
+
+def _check(status: int):
+    if status == CK_OK:
+        return
+    if status == CK_ERR_INVALID_ARG:
+        raise CKInvalidArgument(status, last_error())
+    raise CKError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _matrix(t, name, dtypes):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError("%s must be a 2-D tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit column stride" % name)
+    return t
+
+
+def _ld(t):
+    """Row stride in elements (a single row may report any stride; use at least its length)."""
+    return max(t.stride(0), t.shape[1])
+
+
+def _weights(packed, w_scales, per_group, K):
+    _matrix(packed, "packed", (torch.uint8, torch.int8))
+    if packed.shape[1] != K // 2:
+        raise ValueError("packed has %d bytes per row, expected K/2 = %d" % (packed.shape[1], K // 2))
+    if w_scales is not None and w_scales.dtype != torch.bfloat16:
+        raise ValueError("weight scales must be bf16")
+    return packed.shape[0]
+
+
+def workspace_bytes(M: int, K: int) -> int:
+    return int(lib.ck_linear_workspace_bytes(M, K))
+
+
+def rotate_quant(x, G: int, bits: int, codes=None, row_scales=None):
+    """codes int8 [M, K] and fp32 row scales [M] of a bf16 [M, K] (possibly strided) input."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if row_scales is None:
+        row_scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib.ck_rotate_quant(_ptr(x), M, K, _ld(x), G, bits, _ptr(codes), _ld(codes),
+                               _ptr(row_scales), _stream(x)))
+    return codes, row_scales
+
+
+def rotated_f32(x, G: int):
+    """Rotated rows as the rotate-quant kernel holds them (divided by sqrt(G)), fp32 [M, K]."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    xr = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _check(lib.ck_test_rotate_f32(_ptr(x), M, K, _ld(x), G, _ptr(xr), _ld(xr), _stream(x)))
+    return xr
+
+
+def gemm_q(codes, row_scales, packed, w_scales, per_group: bool, bias=None, out=None,
+           gemv: bool = False):
+    """bf16 [M, N] matmul + scale epilogue on already quantised activations."""
+    _matrix(codes, "codes", (torch.int8,))
+    M, K = codes.shape
+    N = _weights(packed, w_scales, per_group, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=codes.device)
+    fn = lib.ck_w4_gemv if gemv else lib.ck_w4_gemm_q
+    _check(fn(_ptr(codes), _ld(codes), _ptr(row_scales), M, K, _ptr(packed), _ld(packed),
+              _ptr(w_scales), CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N,
+              _ptr(bias), _ptr(out), _ld(out), _stream(codes)))
+    return out
+
+
+def gemv(codes, row_scales, packed, w_scales, per_group: bool, bias=None, out=None):
+    """Decode form of gemm_q (1 <= M <= 8)."""
+    return gemm_q(codes, row_scales, packed, w_scales, per_group, bias, out, gemv=True)
+
+
+def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
+           x_scale: float = 1.0, out=None, workspace=None):
+    """Whole ConvRot linear: bf16 [M, N] = rotate-quant(x) @ W4^T with the scale epilogue."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    N = _weights(packed, w_scales, per_group, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    fn = lib.ck_w4a8_linear if bits == 8 else lib.ck_w4a4_linear
+    if bits not in (8, 4):
+        raise ValueError("bits must be 8 or 4")
+    _check(fn(_ptr(x), M, K, _ld(x), G, _ptr(packed), _ld(packed), _ptr(w_scales),
+              CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N, _ptr(bias), x_scale,
+              _ptr(out), _ld(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream(x)))
+    return out
+
+
+def w4a8_linear(x, G, packed, w_scales, per_group, **kw):
+    return linear(x, G, 8, packed, w_scales, per_group, **kw)
+
+
+def w4a4_linear(x, G, packed, w_scales, per_group, **kw):
+    return linear(x, G, 4, packed, w_scales, per_group, **kw)
+
+
+def w4a16_gemv(x, packed, scales, zeros, bias=None, out=None):
+    """AWQ W4A16 product, bf16 [M, N] (1 <= M <= 8)."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    N = _weights(packed, scales, True, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib.ck_w4a16_gemv(_ptr(x), M, K, _ld(x), _ptr(packed), _ld(packed), _ptr(scales),
+                             _ptr(zeros), 64, N, _ptr(bias), _ptr(out), _ld(out), _stream(x)))
+    return out
+
+
+def accumulators_i32(codes, packed):
+    """int32 [M, N] accumulators sum_k codes[m,k] * (q[n,k] - 8) from the matmul kernels."""
+    _matrix(codes, "codes", (torch.int8,))
+    M, K = codes.shape
+    N = _weights(packed, None, False, K)
+    acc = torch.empty((M, N), dtype=torch.int32, device=codes.device)
+    _check(lib.ck_test_gemm_i32(_ptr(codes), _ld(codes), M, K, _ptr(packed), _ld(packed), N,
+                                _ptr(acc), _ld(acc), _stream(codes)))
+    return acc

@@ -1,0 +1,418 @@
+// C ABI of libck: argument validation and dispatch.  Pure host C++: nothing
+// here touches the GPU until every check has passed, so the error paths can be
+// exercised on a machine without a GPU.  Semantics of each entry point are
+// documented in include/ck.h.
+#include "../../include/ck.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return CK_OK;
+}
+
+int hip_status(int e, const char *what)
+{
+    if (e != 0)
+        return fail(CK_ERR_HIP, "%s: HIP launch failed (hipError_t %d)", what, e);
+    return ok();
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte range [lo, hi) spanned by `rows` rows of `cols` elements of `esize`
+// bytes with row stride `ld` elements.
+struct Range {
+    uintptr_t lo = 0, hi = 0;
+};
+Range span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t esize)
+{
+    Range r;
+    if (!p || rows <= 0 || cols <= 0)
+        return r;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * esize);
+    return r;
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+constexpr int64_t kMaxK = 32768;
+constexpr int64_t kMaxRows = 2147483647;
+
+int check_k(const char *fn, int64_t K)
+{
+    if (K <= 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: K must be positive (got %lld)", fn, (long long)K);
+    if (K % 64 != 0 || K > kMaxK)
+        return fail(CK_ERR_UNSUPPORTED, "%s: K must be a multiple of 64 and at most %lld (got %lld)",
+                    fn, (long long)kMaxK, (long long)K);
+    return CK_OK;
+}
+
+int check_g(const char *fn, int32_t G, int64_t K)
+{
+    if (G != 16 && G != 64 && G != 256)
+        return fail(CK_ERR_UNSUPPORTED, "%s: rotation group G must be 16, 64 or 256 (got %d)", fn, G);
+    if (K % G != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: K (%lld) is not a multiple of G (%d)", fn, (long long)K, G);
+    return CK_OK;
+}
+
+int check_m(const char *fn, int64_t M)
+{
+    if (M < 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: M must be >= 0 (got %lld)", fn, (long long)M);
+    if (M > kMaxRows)
+        return fail(CK_ERR_UNSUPPORTED, "%s: M above %lld", fn, (long long)kMaxRows);
+    return CK_OK;
+}
+
+int check_x(const char *fn, const uint16_t *x, int64_t K, int64_t ldx)
+{
+    if (!x)
+        return fail(CK_ERR_INVALID_ARG, "%s: x is NULL", fn);
+    if (ldx < K || ldx % 8 != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: ldx (%lld) must be >= K and a multiple of 8", fn,
+                    (long long)ldx);
+    if (!aligned(x, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", fn);
+    return CK_OK;
+}
+
+int check_codes(const char *fn, const void *codes, int64_t K, int64_t ldq)
+{
+    if (!codes)
+        return fail(CK_ERR_INVALID_ARG, "%s: codes is NULL", fn);
+    if (ldq < K || ldq % 16 != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: ldq (%lld) must be >= K and a multiple of 16", fn,
+                    (long long)ldq);
+    if (!aligned(codes, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: codes must be 16-byte aligned", fn);
+    return CK_OK;
+}
+
+struct Weights {
+    const uint8_t *packed;
+    int64_t ldw;
+    const uint16_t *scales;
+    int32_t kind, Gw;
+    int64_t N;
+};
+
+int check_weights(const char *fn, const Weights &w, int64_t K, bool need_scales)
+{
+    if (!w.packed)
+        return fail(CK_ERR_INVALID_ARG, "%s: packed weights are NULL", fn);
+    if (w.N <= 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: N must be positive (got %lld)", fn, (long long)w.N);
+    if (w.N % 16 != 0 || w.N > kMaxRows)
+        return fail(CK_ERR_UNSUPPORTED, "%s: N must be a multiple of 16 (got %lld)", fn, (long long)w.N);
+    if (w.ldw < K / 2 || w.ldw % 16 != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: ldw (%lld) must be >= K/2 and a multiple of 16", fn,
+                    (long long)w.ldw);
+    if (!aligned(w.packed, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: packed weights must be 16-byte aligned", fn);
+    if (need_scales) {
+        if (!w.scales)
+            return fail(CK_ERR_INVALID_ARG, "%s: weight scales are NULL", fn);
+        if (w.kind != CK_WS_PER_CHANNEL && w.kind != CK_WS_PER_GROUP)
+            return fail(CK_ERR_INVALID_ARG, "%s: unknown weight-scale kind %d", fn, w.kind);
+        if (w.kind == CK_WS_PER_GROUP && w.Gw != 64)
+            return fail(CK_ERR_UNSUPPORTED, "%s: per-group weight scales need Gw == 64 (got %d)", fn, w.Gw);
+        if (!aligned(w.scales, 2))
+            return fail(CK_ERR_INVALID_ARG, "%s: weight scales must be 2-byte aligned", fn);
+    }
+    return CK_OK;
+}
+
+Range scales_span(const Weights &w, int64_t K)
+{
+    if (w.kind == CK_WS_PER_GROUP)
+        return span(w.scales, K / 64, w.N, w.N, 2);
+    return span(w.scales, 1, w.N, w.N, 2);
+}
+
+int check_out(const char *fn, const void *out, int64_t N, int64_t ldo, size_t esize)
+{
+    if (!out)
+        return fail(CK_ERR_INVALID_ARG, "%s: output is NULL", fn);
+    if (ldo < N || ldo % 2 != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: output stride (%lld) must be >= N and even", fn,
+                    (long long)ldo);
+    if (!aligned(out, 4))
+        return fail(CK_ERR_INVALID_ARG, "%s: output must be 4-byte aligned", fn);
+    (void)esize;
+    return CK_OK;
+}
+
+#define CK_TRY(expr)            \
+    do {                        \
+        int _st = (expr);       \
+        if (_st != CK_OK)       \
+            return _st;         \
+    } while (0)
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Dispatch of the integer matmul + epilogue by M.
+int run_gemm(const char *fn, const int8_t *codes, int64_t ldq, const float *rs, int64_t M, int64_t K,
+             const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
+             int32_t *acc, int64_t lda, void *stream)
+{
+    const bool pg = w.kind == CK_WS_PER_GROUP;
+    int e;
+    if (M <= 64 && ck::w4_skinny_supports(M, K))
+        e = ck::launch_w4_skinny(codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
+                                 (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
+    else
+        e = ck::launch_w4_gemm(codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
+                               (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
+    return hip_status(e, fn);
+}
+
+int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, const float *rs,
+                  int64_t M, int64_t K, const Weights &w, const uint16_t *bias, uint16_t *out,
+                  int64_t ldo, void *stream)
+{
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_weights(fn, w, K, true));
+    if (gemv && (M > 8 || !ck::w4_skinny_supports(M < 1 ? 1 : M, K)))
+        return fail(CK_ERR_UNSUPPORTED, "%s: decode GEMV takes 1 <= M <= 8 and K <= 8192 (M=%lld, K=%lld)",
+                    fn, (long long)M, (long long)K);
+    if (M == 0)
+        return ok();
+    CK_TRY(check_codes(fn, codes, K, ldq));
+    if (!rs)
+        return fail(CK_ERR_INVALID_ARG, "%s: row_scales is NULL", fn);
+    if (!aligned(rs, 4))
+        return fail(CK_ERR_INVALID_ARG, "%s: row_scales must be 4-byte aligned", fn);
+    if (bias && !aligned(bias, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
+    CK_TRY(check_out(fn, out, w.N, ldo, 2));
+    const Range ro = span(out, M, w.N, ldo, 2);
+    if (overlap(ro, span(codes, M, K, ldq, 1)) || overlap(ro, span(rs, 1, M, M, 4)) ||
+        overlap(ro, span(w.packed, w.N, K / 2, w.ldw, 1)) || overlap(ro, scales_span(w, K)) ||
+        overlap(ro, span(bias, 1, w.N, w.N, 2)))
+        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    return run_gemm(fn, codes, ldq, rs, M, K, w, bias, 1.0f, out, ldo, nullptr, 0, stream);
+}
+
+int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                  int32_t G, const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out,
+                  int64_t ldo, void *ws, size_t ws_bytes, void *stream)
+{
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_g(fn, G, K));
+    CK_TRY(check_weights(fn, w, K, true));
+    if (!(x_scale > 0.f) || !std::isfinite(x_scale))
+        return fail(CK_ERR_INVALID_ARG, "%s: x_scale must be positive and finite", fn);
+    if (M == 0)
+        return ok();
+    CK_TRY(check_x(fn, x, K, ldx));
+    if (bias && !aligned(bias, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
+    CK_TRY(check_out(fn, out, w.N, ldo, 2));
+    const size_t need = ck_linear_workspace_bytes(M, K);
+    if (!ws || ws_bytes < need)
+        return fail(CK_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, ws_bytes,
+                    ws ? "" : ", NULL");
+    if (!aligned(ws, kWsAlign))
+        return fail(CK_ERR_WORKSPACE, "%s: workspace must be %zu-byte aligned", fn, kWsAlign);
+    const Range ro = span(out, M, w.N, ldo, 2);
+    const Range rw = span(ws, 1, (int64_t)need, (int64_t)need, 1);
+    const Range rx = span(x, M, K, ldx, 2);
+    if (overlap(ro, rx) || overlap(ro, span(w.packed, w.N, K / 2, w.ldw, 1)) ||
+        overlap(ro, scales_span(w, K)) || overlap(ro, span(bias, 1, w.N, w.N, 2)) || overlap(ro, rw))
+        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input or the workspace", fn);
+    if (overlap(rw, rx) || overlap(rw, span(w.packed, w.N, K / 2, w.ldw, 1)) ||
+        overlap(rw, scales_span(w, K)) || overlap(rw, span(bias, 1, w.N, w.N, 2)))
+        return fail(CK_ERR_WORKSPACE, "%s: workspace overlaps an input", fn);
+
+    int8_t *codes = static_cast<int8_t *>(ws);
+    float *rs = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round_up((size_t)(M * K), kWsAlign));
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, bits == 8 ? 127 : 7, codes, K, rs,
+                                          nullptr, 0, stream);
+    if (e != 0)
+        return hip_status(e, fn);
+    return run_gemm(fn, codes, K, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ck_status_str(int status)
+{
+    switch (status) {
+    case CK_OK: return "CK_OK";
+    case CK_ERR_INVALID_ARG: return "CK_ERR_INVALID_ARG";
+    case CK_ERR_UNSUPPORTED: return "CK_ERR_UNSUPPORTED";
+    case CK_ERR_WORKSPACE: return "CK_ERR_WORKSPACE";
+    case CK_ERR_HIP: return "CK_ERR_HIP";
+    default: return "CK_ERR_UNKNOWN";
+    }
+}
+
+const char *ck_last_error_msg(void) { return g_last_error.c_str(); }
+
+const char *ck_version(void) { return "ck 0.1 gfx950"; }
+
+size_t ck_linear_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0)
+        return 0;
+    return round_up((size_t)(M * K), kWsAlign) + round_up((size_t)M * sizeof(float), kWsAlign);
+}
+
+int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, int32_t bits,
+                    int8_t *codes, int64_t ldq, float *row_scales, void *stream)
+{
+    const char *fn = "ck_rotate_quant";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_g(fn, G, K));
+    if (bits != 8 && bits != 4)
+        return fail(CK_ERR_UNSUPPORTED, "%s: bits must be 8 or 4 (got %d)", fn, bits);
+    if (M == 0)
+        return ok();
+    CK_TRY(check_x(fn, x, K, ldx));
+    CK_TRY(check_codes(fn, codes, K, ldq));
+    if (!row_scales || !aligned(row_scales, 4))
+        return fail(CK_ERR_INVALID_ARG, "%s: row_scales must be a non-NULL 4-byte aligned pointer", fn);
+    const Range rx = span(x, M, K, ldx, 2);
+    if (overlap(rx, span(codes, M, K, ldq, 1)) || overlap(rx, span(row_scales, 1, M, M, 4)) ||
+        overlap(span(codes, M, K, ldq, 1), span(row_scales, 1, M, M, 4)))
+        return fail(CK_ERR_INVALID_ARG, "%s: codes, row_scales and x must not overlap", fn);
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, bits == 8 ? 127 : 7, codes, ldq,
+                                          row_scales, nullptr, 0, stream);
+    return hip_status(e, fn);
+}
+
+int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, float *xr,
+                       int64_t ldr, void *stream)
+{
+    const char *fn = "ck_test_rotate_f32";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_g(fn, G, K));
+    if (M == 0)
+        return ok();
+    CK_TRY(check_x(fn, x, K, ldx));
+    if (!xr || ldr < K || ldr % 4 != 0 || !aligned(xr, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: xr must be 16-byte aligned with ldr >= K, ldr %% 4 == 0", fn);
+    if (overlap(span(x, M, K, ldx, 2), span(xr, M, K, ldr, 4)))
+        return fail(CK_ERR_INVALID_ARG, "%s: xr overlaps x", fn);
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, 127, nullptr, 0, nullptr, xr, ldr, stream);
+    return hip_status(e, fn);
+}
+
+int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,
+                 const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
+                 int32_t Gw, int64_t N, const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    return gemm_q_common("ck_w4_gemm_q", false, codes, ldq, row_scales, M, K, w, bias, out, ldo, stream);
+}
+
+int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,
+               const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
+               int32_t Gw, int64_t N, const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    return gemm_q_common("ck_w4_gemv", true, codes, ldq, row_scales, M, K, w, bias, out, ldo, stream);
+}
+
+int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
+                   int32_t Gw, int64_t N, const uint16_t *bias, float x_scale, uint16_t *out,
+                   int64_t ldo, void *ws, size_t ws_bytes, void *stream)
+{
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    return linear_common("ck_w4a8_linear", 8, x, M, K, ldx, G, w, bias, x_scale, out, ldo, ws,
+                         ws_bytes, stream);
+}
+
+int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
+                   int32_t Gw, int64_t N, const uint16_t *bias, float x_scale, uint16_t *out,
+                   int64_t ldo, void *ws, size_t ws_bytes, void *stream)
+{
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    return linear_common("ck_w4a4_linear", 4, x, M, K, ldx, G, w, bias, x_scale, out, ldo, ws,
+                         ws_bytes, stream);
+}
+
+int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
+                  int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int32_t Gw, int64_t N,
+                  const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    const char *fn = "ck_w4a16_gemv";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    const Weights w{packed, ldw, scales, CK_WS_PER_GROUP, Gw, N};
+    CK_TRY(check_weights(fn, w, K, true));
+    if (!zeros || !aligned(zeros, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: zeros must be a non-NULL 2-byte aligned pointer", fn);
+    if (M > 8 || !ck::w4a16_supports(K))
+        return fail(CK_ERR_UNSUPPORTED, "%s: takes 1 <= M <= 8 and K <= 4096 (M=%lld, K=%lld)", fn,
+                    (long long)M, (long long)K);
+    if (M == 0)
+        return ok();
+    CK_TRY(check_x(fn, x, K, ldx));
+    if (bias && !aligned(bias, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
+    CK_TRY(check_out(fn, out, N, ldo, 2));
+    const Range ro = span(out, M, N, ldo, 2);
+    if (overlap(ro, span(x, M, K, ldx, 2)) || overlap(ro, span(packed, N, K / 2, ldw, 1)) ||
+        overlap(ro, span(scales, K / 64, N, N, 2)) || overlap(ro, span(zeros, K / 64, N, N, 2)) ||
+        overlap(ro, span(bias, 1, N, N, 2)))
+        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    const int e = ck::launch_w4a16_gemv(x, (int)M, (int)K, ldx, packed, ldw, scales, zeros, (int)N,
+                                        bias, out, ldo, stream);
+    return hip_status(e, fn);
+}
+
+int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, const uint8_t *packed,
+                     int64_t ldw, int64_t N, int32_t *acc, int64_t lda, void *stream)
+{
+    const char *fn = "ck_test_gemm_i32";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    const Weights w{packed, ldw, nullptr, CK_WS_PER_CHANNEL, 64, N};
+    CK_TRY(check_weights(fn, w, K, false));
+    if (M == 0)
+        return ok();
+    CK_TRY(check_codes(fn, codes, K, ldq));
+    CK_TRY(check_out(fn, acc, N, lda, 4));
+    const Range ra = span(acc, M, N, lda, 4);
+    if (overlap(ra, span(codes, M, K, ldq, 1)) || overlap(ra, span(packed, N, K / 2, ldw, 1)))
+        return fail(CK_ERR_INVALID_ARG, "%s: acc overlaps an input", fn);
+    return run_gemm(fn, codes, ldq, nullptr, M, K, w, nullptr, 1.0f, nullptr, 0, acc, lda, stream);
+}
+
+}  // extern "C"

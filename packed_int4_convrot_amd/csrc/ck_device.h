@@ -1,0 +1,90 @@
+// Device-side helpers shared by the gfx950 kernels of libck.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ck {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Streaming (non-temporal) global loads for data read exactly once.
+__device__ __forceinline__ u32x4 load_nt16(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 load_nt8(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Byte permute of the 8 bytes {hi:lo}: selector byte values 0..3 pick bytes of
+// `lo`, 4..7 bytes of `hi`, 0x0c gives 0x00.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Packed-uint4 decode used by every int8 MFMA kernel.
+// One packed dword holds 8 codes: byte j = (code of k=2j) | (code of k=2j+1) << 4.
+// Flipping bit 3 of every nibble turns the code q into the 4-bit two's
+// complement of q - 8; moving that nibble into the high half of a byte gives
+// the int8 value 16 * (q - 8).  The result is two dwords of int8 lanes:
+//   lo: k = 0, 2, 4, 6     hi: k = 1, 3, 5, 7   (each value is 16 * (q - 8))
+// so an int32 MFMA accumulates exactly 16x the true sum (|sum| stays far below
+// 2^31 for K <= 65536).  Operands on the other side are permuted to the same k
+// order by act_perm16().
+__device__ __forceinline__ void w4_decode_x16(uint32_t d, uint32_t &lo, uint32_t &hi)
+{
+    const uint32_t e = d ^ 0x88888888u;
+    lo = (e << 4) & 0xf0f0f0f0u;
+    hi = e & 0xf0f0f0f0u;
+}
+
+// Reorder 16 consecutive int8 values k = 0..15 (four dwords) into the order
+// produced by w4_decode_x16 on two packed dwords:
+//   [0,2,4,6] [1,3,5,7] [8,10,12,14] [9,11,13,15]
+__device__ __forceinline__ v4i act_perm16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
+{
+    v4i r;
+    r[0] = (int)perm(w1, w0, 0x06040200u);
+    r[1] = (int)perm(w1, w0, 0x07050301u);
+    r[2] = (int)perm(w3, w2, 0x06040200u);
+    r[3] = (int)perm(w3, w2, 0x07050301u);
+    return r;
+}
+
+__device__ __forceinline__ v4i w4_operand_x16(uint32_t d0, uint32_t d1)
+{
+    uint32_t l0, h0, l1, h1;
+    w4_decode_x16(d0, l0, h0);
+    w4_decode_x16(d1, l1, h1);
+    v4i r;
+    r[0] = (int)l0;
+    r[1] = (int)h0;
+    r[2] = (int)l1;
+    r[3] = (int)h1;
+    return r;
+}
+
+}  // namespace ck

@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (ck_api.cpp) and the kernels.
+// Every function assumes its arguments were validated by the caller and
+// returns the hipError_t of the launch as an int (0 = success).
+#pragma once
+
+#include <stdint.h>
+
+namespace ck {
+
+int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax,
+                        int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
+                        void *stream);
+
+// Skinny path: M <= 64, weights streamed once, activations held in registers.
+// acc_out != nullptr selects the int32 test epilogue.
+int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
+                     const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                     bool per_group, int N, const uint16_t *bias, float x_scale,
+                     uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
+bool w4_skinny_supports(int64_t M, int64_t K);
+
+// Tiled MFMA GEMM for larger M.
+int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,
+                   int N, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
+                   int32_t *acc_out, int64_t lda, void *stream);
+
+int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed,
+                      int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int N,
+                      const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream);
+bool w4a16_supports(int64_t K);
+
+}  // namespace ck

@@ -1,0 +1,260 @@
+// Fused group-wise Walsh-Hadamard rotation + rowwise absmax quantisation.
+//
+// Follows the fused RotateQuant operator of "[PR #155] [Feat][Ascend] Add
+// fused RotateQuant backend" (section "What this PR does"): the rotation
+// x_g . H_G / sqrt(G) of every contiguous G-column group (G = 16, 64, 256) and
+// the dynamic per-row quantisation happen in one pass over x, so the rotated
+// tensor is never written out.
+//
+// Work layout (one workgroup per row):
+//   * thread t owns chunks c = t, t + BLOCK, ... of 8 consecutive bf16 (16 B),
+//     loaded with one coalesced 16-byte load each;
+//   * a group of G columns is G/8 chunks held by G/8 neighbouring lanes of one
+//     wave (groups never straddle a wave or a chunk round);
+//   * the first three butterfly stages (strides 1, 2, 4) run inside the
+//     thread's 8 registers, the remaining log2(G/8) stages across lanes
+//     (DPP quad permutes for lane distance 1 and 2, ds_swizzle for 4..16);
+//   * the fp32 values stay in registers until the row absmax is known
+//     (wave reduction, then LDS across waves); then every thread quantises and
+//     stores its own 8 codes with one 8-byte store.
+// The transform is kept unnormalised (y = sqrt(G) * xr).  Because sqrt(G) is a
+// power of two, fp32(qmax / max|y|) * y equals fp32(qmax / max|xr|) * xr
+// exactly, so the codes match the normalised definition bit for bit; the row
+// scale is max|y| / qmax divided by sqrt(G) (also exact).
+#include "ck_device.h"
+#include "launch.h"
+
+namespace ck {
+namespace {
+
+// Value held by the lane whose index differs in bit log2(MASK).
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float v)
+{
+    int i = __float_as_int(v);
+    if constexpr (MASK == 1)
+        i = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    else if constexpr (MASK == 2)
+        i = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    else
+        i = __builtin_amdgcn_ds_swizzle(i, 0x1F | (MASK << 10));      // bitmask mode: lane ^ MASK
+    return __int_as_float(i);
+}
+
+// One cross-lane butterfly stage: the lower lane of each pair keeps u + v,
+// the upper lane v' = u - v (written as fma(v, -1, u), same rounding).
+template <int MASK, int CPT>
+__device__ __forceinline__ void lane_stage(float (&v)[CPT][8], float sgn)
+{
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float p = lane_xor<MASK>(v[i][r]);
+            v[i][r] = __builtin_fmaf(v[i][r], sgn, p);
+        }
+}
+
+template <int G, int CPT>
+__device__ __forceinline__ void fht(float (&v)[CPT][8], int lane)
+{
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if ((r & h) == 0) {
+                    const float a = v[i][r], b = v[i][r + h];
+                    v[i][r] = a + b;
+                    v[i][r + h] = a - b;
+                }
+    }
+    if constexpr (G >= 16) lane_stage<1, CPT>(v, (lane & 1) ? -1.f : 1.f);
+    if constexpr (G >= 32) lane_stage<2, CPT>(v, (lane & 2) ? -1.f : 1.f);
+    if constexpr (G >= 64) lane_stage<4, CPT>(v, (lane & 4) ? -1.f : 1.f);
+    if constexpr (G >= 128) lane_stage<8, CPT>(v, (lane & 8) ? -1.f : 1.f);
+    if constexpr (G >= 256) lane_stage<16, CPT>(v, (lane & 16) ? -1.f : 1.f);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, lane_xor<1>(v));
+    v = fmaxf(v, lane_xor<2>(v));
+    v = fmaxf(v, lane_xor<4>(v));
+    v = fmaxf(v, lane_xor<8>(v));
+    v = fmaxf(v, lane_xor<16>(v));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    return fmaxf(a, b);
+}
+
+// Low byte of fp32(t) + 1.5 * 2^23 is the two's-complement of rne(t) for
+// |t| < 2^22 (the add rounds to an integer, ties to even).
+__device__ __forceinline__ uint32_t rne_byte(float t) { return __float_as_uint(t + 12582912.0f); }
+
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
+{
+    const uint32_t p01 = perm(b1, b0, 0x0C0C0400u);
+    const uint32_t p23 = perm(b3, b2, 0x0C0C0400u);
+    return perm(p23, p01, 0x05040100u);
+}
+
+template <int G, int BLOCK, int CPT, bool F32OUT>
+__global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, int K, float qmax, int8_t *__restrict__ codes,
+    int64_t ldq, float *__restrict__ row_scales, float *__restrict__ xr, int64_t ldr)
+{
+    constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
+    static_assert(G == 16 || G == 64 || G == 256, "G");
+    __shared__ float wmax[BLOCK / kWave];
+
+    const int64_t m = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int nchunk = K >> 3;
+    const uint16_t *xrow = x + m * ldx;
+
+    u32x4 raw[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = t + i * BLOCK;
+        raw[i] = c < nchunk ? load_nt16(xrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float v[CPT][8];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const uint32_t w[4] = {raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[i][2 * j] = __uint_as_float(w[j] << 16);
+            v[i][2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+
+    fht<G, CPT>(v, lane);
+
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            am = fmaxf(am, fabsf(v[i][r]));
+    am = wave_max(am);
+    if (lane == 0)
+        wmax[t / kWave] = am;
+    __syncthreads();
+    am = wmax[0];
+#pragma unroll
+    for (int w = 1; w < BLOCK / kWave; ++w)
+        am = fmaxf(am, wmax[w]);
+
+    if constexpr (F32OUT) {
+        float *orow = xr + m * ldr;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = t + i * BLOCK;
+            if (c < nchunk) {
+                float4 *o = reinterpret_cast<float4 *>(orow + 8 * c);
+                o[0] = make_float4(v[i][0] * kInvSqrtG, v[i][1] * kInvSqrtG, v[i][2] * kInvSqrtG,
+                                   v[i][3] * kInvSqrtG);
+                o[1] = make_float4(v[i][4] * kInvSqrtG, v[i][5] * kInvSqrtG, v[i][6] * kInvSqrtG,
+                                   v[i][7] * kInvSqrtG);
+            }
+        }
+    } else {
+        // am == 0 (all-zero row): inv = 0 makes every code 0; the scale is 1.
+        const float inv = am > 0.f ? qmax / am : 0.f;
+        int8_t *crow = codes + m * ldq;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = t + i * BLOCK;
+            uint32_t b[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                b[r] = rne_byte(v[i][r] * inv);
+            if (c < nchunk) {
+                uint2 o;
+                o.x = pack4(b[0], b[1], b[2], b[3]);
+                o.y = pack4(b[4], b[5], b[6], b[7]);
+                reinterpret_cast<uint2 *>(crow)[c] = o;
+            }
+        }
+        if (t == 0)
+            row_scales[m] = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;
+    }
+}
+
+// BLOCK threads, CPT chunks of 8 columns per thread.  CPT is capped so that
+// the row stays in VGPRs without spilling: 8 at 256 threads, 4 at 1024.
+template <int G, int BLOCK, bool F32OUT>
+hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_t ldx, int K,
+                    float qmax, int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr)
+{
+    constexpr int kMaxCpt = BLOCK >= 1024 ? 4 : 8;
+    if (cpt < 1 || cpt > kMaxCpt)
+        return hipErrorInvalidValue;
+#define CK_RQ_CASE(C)                                                                         \
+    case C:                                                                                   \
+        if constexpr (C <= kMaxCpt)                                                           \
+            hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, F32OUT>), grid, dim3(BLOCK), 0, \
+                               s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);                  \
+        break;
+    switch (cpt) {
+        CK_RQ_CASE(1)
+        CK_RQ_CASE(2)
+        CK_RQ_CASE(3)
+        CK_RQ_CASE(4)
+        CK_RQ_CASE(5)
+        CK_RQ_CASE(6)
+        CK_RQ_CASE(7)
+        CK_RQ_CASE(8)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef CK_RQ_CASE
+    return hipGetLastError();
+}
+
+template <int G, bool F32OUT>
+hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t ldx, float qmax,
+                     int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr)
+{
+    const int nchunk = K / 8;
+    const dim3 grid((unsigned)M);
+    if (nchunk <= 256 * 8) {
+        const int cpt = (nchunk + 255) / 256;
+        return launch_g<G, 256, F32OUT>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
+    }
+    const int cpt = (nchunk + 1023) / 1024;
+    return launch_g<G, 1024, F32OUT>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
+}
+
+}  // namespace
+
+int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax,
+                        int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
+                        void *stream)
+{
+    if (M <= 0)
+        return 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const float q = (float)qmax;
+    hipError_t e;
+    if (xr) {
+        switch (G) {
+        case 16: e = launch_rq<16, true>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
+        case 64: e = launch_rq<64, true>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
+        default: e = launch_rq<256, true>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
+        }
+    } else {
+        switch (G) {
+        case 16: e = launch_rq<16, false>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
+        case 64: e = launch_rq<64, false>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
+        default: e = launch_rq<256, false>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
+        }
+    }
+    return (int)e;
+}
+
+}  // namespace ck

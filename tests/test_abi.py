@@ -1,0 +1,162 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before anything is enqueued.
+
+The fake device pointers below are never dereferenced: every call here fails
+validation, which runs entirely on the host before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ck.h")
+
+ck = pytest.importorskip("packed_int4_convrot_amd")
+lib = ck.lib
+
+P = 0x10000000  # 256-byte aligned fake device address (never dereferenced)
+P2 = 0x20000000
+P3 = 0x30000000
+P4 = 0x40000000
+P5 = 0x50000000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ck_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), "libck.so does not export %s" % n
+        assert n in ck.SIGNATURES, "binding lacks a signature for %s" % n
+
+
+def test_status_strings_and_version():
+    assert lib.ck_status_str(0) == b"CK_OK"
+    assert lib.ck_status_str(3) == b"CK_ERR_WORKSPACE"
+    assert lib.ck_version().startswith(b"ck ")
+
+
+def test_workspace_bytes():
+    assert lib.ck_linear_workspace_bytes(0, 3840) == 0
+    ws = lib.ck_linear_workspace_bytes(32, 3840)
+    assert ws >= 32 * 3840 + 32 * 4 and ws % 256 == 0
+    assert lib.ck_linear_workspace_bytes(8192, 10240) == 8192 * 10240 + 32768
+
+
+def rq(x=P, M=4, K=256, ldx=256, G=64, bits=8, codes=P2, ldq=256, rs=P3):
+    return lib.ck_rotate_quant(x, M, K, ldx, G, bits, codes, ldq, rs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=32), ck.CK_ERR_UNSUPPORTED),
+    (dict(G=128), ck.CK_ERR_UNSUPPORTED),
+    (dict(bits=6), ck.CK_ERR_UNSUPPORTED),
+    (dict(K=0), ck.CK_ERR_INVALID_ARG),
+    (dict(K=96, ldx=96, ldq=96), ck.CK_ERR_UNSUPPORTED),         # K % 64
+    (dict(K=320, ldx=320, ldq=320, G=256), ck.CK_ERR_INVALID_ARG),  # K % G
+    (dict(K=65536, ldx=65536, ldq=65536), ck.CK_ERR_UNSUPPORTED),
+    (dict(M=-1), ck.CK_ERR_INVALID_ARG),
+    (dict(x=None), ck.CK_ERR_INVALID_ARG),
+    (dict(codes=None), ck.CK_ERR_INVALID_ARG),
+    (dict(rs=None), ck.CK_ERR_INVALID_ARG),
+    (dict(ldx=200), ck.CK_ERR_INVALID_ARG),
+    (dict(ldx=260), ck.CK_ERR_INVALID_ARG),      # not a multiple of 8
+    (dict(ldq=264), ck.CK_ERR_INVALID_ARG),      # not a multiple of 16
+    (dict(x=P + 8), ck.CK_ERR_INVALID_ARG),      # misaligned
+    (dict(codes=P + 512), ck.CK_ERR_INVALID_ARG),  # overlaps x
+])
+def test_rotate_quant_rejects(kw, status):
+    assert rq(**kw) == status
+    assert lib.ck_last_error_msg() != b""
+
+
+def test_zero_rows_is_noop():
+    assert rq(M=0, x=None, codes=None, rs=None) == ck.CK_OK
+
+
+def gq(fn=None, codes=P, ldq=256, rs=P2, M=4, K=256, packed=P3, ldw=128, ws=P4, kind=1, Gw=64,
+       N=64, bias=None, out=P5, ldo=64):
+    fn = fn or lib.ck_w4_gemm_q
+    return fn(codes, ldq, rs, M, K, packed, ldw, ws, kind, Gw, N, bias, out, ldo, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=40), ck.CK_ERR_UNSUPPORTED),
+    (dict(N=0), ck.CK_ERR_INVALID_ARG),
+    (dict(Gw=128), ck.CK_ERR_UNSUPPORTED),
+    (dict(kind=5), ck.CK_ERR_INVALID_ARG),
+    (dict(ldw=100), ck.CK_ERR_INVALID_ARG),
+    (dict(packed=P3 + 4), ck.CK_ERR_INVALID_ARG),
+    (dict(ws=None), ck.CK_ERR_INVALID_ARG),
+    (dict(out=None), ck.CK_ERR_INVALID_ARG),
+    (dict(ldo=32), ck.CK_ERR_INVALID_ARG),
+    (dict(out=P3), ck.CK_ERR_INVALID_ARG),       # overlaps the packed weights
+    (dict(out=P + 128), ck.CK_ERR_INVALID_ARG),  # overlaps the codes
+    (dict(rs=None), ck.CK_ERR_INVALID_ARG),
+])
+def test_gemm_q_rejects(kw, status):
+    assert gq(**kw) == status
+
+
+def test_gemv_rejects_large_m():
+    assert gq(fn=lib.ck_w4_gemv, M=9) == ck.CK_ERR_UNSUPPORTED
+    assert gq(fn=lib.ck_w4_gemv, M=0) == ck.CK_OK
+
+
+def lin(fn=None, x=P, M=4, K=256, ldx=256, G=64, packed=P3, ldw=128, ws_=P4, kind=0, Gw=64, N=64,
+        bias=None, xs=1.0, out=P5, ldo=64, work=P2, wsb=1 << 20):
+    fn = fn or lib.ck_w4a8_linear
+    return fn(x, M, K, ldx, G, packed, ldw, ws_, kind, Gw, N, bias, xs, out, ldo, work, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(work=None), ck.CK_ERR_WORKSPACE),
+    (dict(wsb=100), ck.CK_ERR_WORKSPACE),
+    (dict(work=P2 + 16), ck.CK_ERR_WORKSPACE),   # not 256-byte aligned
+    (dict(work=P), ck.CK_ERR_WORKSPACE),         # workspace overlaps x
+    (dict(xs=0.0), ck.CK_ERR_INVALID_ARG),
+    (dict(xs=float("inf")), ck.CK_ERR_INVALID_ARG),
+    (dict(G=8), ck.CK_ERR_UNSUPPORTED),
+    (dict(out=P2), ck.CK_ERR_INVALID_ARG),       # output overlaps the workspace
+])
+def test_linear_rejects(kw, status):
+    assert lin(**kw) == status
+    assert lin(fn=lib.ck_w4a4_linear, **kw) == status
+
+
+def test_awq_rejects():
+    f = lib.ck_w4a16_gemv
+    assert f(P, 9, 256, 256, P3, 128, P4, P2, 64, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
+    assert f(P, 1, 256, 256, P3, 128, P4, None, 64, 64, None, P5, 64, None) == ck.CK_ERR_INVALID_ARG
+    assert f(P, 1, 256, 256, P3, 128, P4, P2, 32, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
+    assert f(P, 1, 8192, 8192, P3, 4096, P4, P2, 64, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
+
+
+def test_test_hooks_reject():
+    assert lib.ck_test_rotate_f32(P, 4, 256, 256, 64, P2 + 4, 256, None) == ck.CK_ERR_INVALID_ARG
+    assert lib.ck_test_gemm_i32(P, 256, 4, 256, P3, 128, 64, P3, 64, None) == ck.CK_ERR_INVALID_ARG
+
+
+def test_error_message_is_thread_local():
+    import threading
+    rq(G=32)
+    msgs = []
+    t = threading.Thread(target=lambda: msgs.append(lib.ck_last_error_msg()))
+    t.start()
+    t.join()
+    assert msgs == [b""]
+    assert b"G must be" in lib.ck_last_error_msg()
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ck.rotate_quant(x, 64, 8)

@@ -1,0 +1,228 @@
+"""GPU parity: every HIP entry point against the CPU oracle, called through the C ABI.
+
+Acceptance (stated with the method): integer codes and int32 accumulators are
+bit-exact given identical inputs; rotation codes from the same bf16 x agree on
+>= 99.99% of the elements and differ by at most 1 elsewhere (the kernel's fp32
+butterflies round differently from the oracle's exact sum); bf16 outputs
+satisfy max |err| <= 1e-2 (|ref| + 1) against the oracle's fp64 result from the
+GPU's own codes and row scales.  Sizes cover several tiles and a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import DEV, assert_codes_close, assert_output_close, bf16_dev, host, i8_dev, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+ck = pytest.importorskip("packed_int4_convrot_amd")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# --------------------------------------------------------------- rotate-quant
+
+
+@pytest.mark.parametrize("G", [16, 64, 256])
+@pytest.mark.parametrize("M,K", [(37, 768), (5, 3840), (3, 10240)])
+def test_rotation_matches_oracle(G, M, K):
+    x = workloads.activations(M, K, seed=G + K, outliers=max(1, K // 100), zero_rows=(1,))
+    xr = host(ck.rotated_f32(bf16_dev(x), G))
+    ref = oracle.rotate(x, G)
+    xf = np.abs(workloads.bf16_bits_to_f32(x).astype(np.float64)).reshape(M, K // G, G)
+    tol = 1e-6 * np.repeat(xf.sum(-1), G, axis=1).reshape(M, K) / np.sqrt(G) + 1e-30
+    assert (np.abs(xr.astype(np.float64) - ref) <= tol).all()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("G", [16, 64, 256])
+def test_codes_bit_exact_given_rotation(G, bits):
+    M, K = 67, 3840
+    x = workloads.activations(M, K, seed=3 * G + bits, outliers=38, zero_rows=(0, 66))
+    xd = bf16_dev(x)
+    codes, scales = ck.rotate_quant(xd, G, bits)
+    xr = host(ck.rotated_f32(xd, G))
+    ref_codes, ref_scales = oracle.quantize(xr, bits)
+    assert np.array_equal(host(codes), ref_codes)
+    assert np.array_equal(host(scales), ref_scales)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("G", [16, 64, 256])
+def test_rotate_quant_matches_oracle(G, bits):
+    M, K = 96, 3840
+    x = workloads.activations(M, K, seed=G * bits, outliers=38, zero_rows=(7, 95))
+    codes, scales = ck.rotate_quant(bf16_dev(x), G, bits)
+    ref_codes, ref_scales = oracle.rotate_quant(x, G, bits)
+    assert_codes_close(host(codes), ref_codes)
+    s = host(scales)
+    assert np.all(np.abs(s - ref_scales) <= 2.0 ** -20 * ref_scales)
+    assert s[7] == 1.0 and s[95] == 1.0 and not host(codes)[[7, 95]].any()
+
+
+def test_rotate_quant_strided_input_ignores_padding():
+    M, K, ld = 9, 1024, 1152  # padding columns hold NaN
+    x = workloads.activations(M, K, seed=5, outliers=10, ld=ld)
+    xd = bf16_dev(x)[:, :K]
+    assert xd.stride(0) == ld
+    c1, s1 = ck.rotate_quant(xd, 64, 8)
+    c2, s2 = ck.rotate_quant(bf16_dev(np.ascontiguousarray(x[:, :K])), 64, 8)
+    assert np.isfinite(host(s1)).all()
+    assert np.array_equal(host(c1), host(c2)) and np.array_equal(host(s1), host(s2))
+
+
+def test_rotate_quant_deterministic():
+    x = bf16_dev(workloads.activations(300, 2048, seed=1, outliers=20))
+    a = [ck.rotate_quant(x, 256, 8) for _ in range(2)]
+    assert torch.equal(a[0][0], a[1][0]) and torch.equal(a[0][1], a[1][1])
+
+
+# ------------------------------------------------------- integer accumulators
+
+
+def _rand_codes(M, K, qmax, seed):
+    return np.random.default_rng(seed).integers(-qmax, qmax + 1, size=(M, K), dtype=np.int8)
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 3840, 96), (5, 384, 272), (8, 3840, 160), (16, 1024, 64), (33, 3840, 48),
+    (64, 4096, 32), (65, 384, 528), (300, 1152, 272), (513, 128, 16),
+])
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_accumulators_bit_exact(M, K, N, qmax):
+    codes = _rand_codes(M, K, qmax, seed=M + K + N)
+    packed = workloads.packed_weights(N, K, seed=N)
+    acc = host(ck.accumulators_i32(i8_dev(codes), u8_dev(packed)))
+    ref = oracle.int_gemm(codes, oracle.unpack(packed))
+    assert np.array_equal(acc.astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("M", [3, 70])
+def test_accumulators_extremes(M):
+    """Largest magnitudes: every code +-127 against every weight -8 or +7, long K."""
+    K, N = 32768, 32
+    codes = np.full((M, K), 127, dtype=np.int8)
+    codes[1::2] = -127
+    packed = np.zeros((N, K // 2), dtype=np.uint8)   # all weights -8
+    packed[N // 2:] = 0xFF                            # all weights +7
+    acc = host(ck.accumulators_i32(i8_dev(codes), u8_dev(packed)))
+    ref = oracle.int_gemm(codes, oracle.unpack(packed))
+    assert np.array_equal(acc.astype(np.int64), ref)
+    assert np.abs(ref).max() == 127 * 8 * K
+
+
+# ------------------------------------------------------------ matmul outputs
+
+
+@pytest.mark.parametrize("per_group", [True, False])
+@pytest.mark.parametrize("M", [1, 4, 8, 13, 32, 64, 100, 257])
+def test_gemm_q_outputs(M, per_group):
+    K, N = 1280, 272
+    inp = workloads.linear_inputs(M, K, N, seed=M, outliers=13, scale="group" if per_group else "channel",
+                                  zero_rows=(M - 1,) if M > 2 else (), with_bias=(M % 2 == 0))
+    codes, scales = oracle.rotate_quant(inp["x"], 64, 8)
+    out = ck.gemm_q(i8_dev(codes), torch.from_numpy(scales).to(DEV), u8_dev(inp["packed"]),
+                    bf16_dev(inp["w_scales"]), per_group,
+                    bias=None if inp["bias"] is None else bf16_dev(inp["bias"]))
+    ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
+    assert_output_close(host(out), ref)
+
+
+@pytest.mark.parametrize("per_group", [True, False])
+def test_gemv_entry_matches_oracle(per_group):
+    K, N = 3840, 1024
+    for M in (1, 4, 8):
+        inp = workloads.linear_inputs(M, K, N, seed=11, outliers=8, scale="group" if per_group else "channel")
+        codes, scales = oracle.rotate_quant(inp["x"], 64, 8)
+        out = ck.gemv(i8_dev(codes), torch.from_numpy(scales).to(DEV), u8_dev(inp["packed"]),
+                      bf16_dev(inp["w_scales"]), per_group)
+        ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group)
+        assert_output_close(host(out), ref)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("per_group", [True, False])
+@pytest.mark.parametrize("G", [16, 64, 256])
+@pytest.mark.parametrize("M", [3, 40, 300])
+def test_linear_end_to_end(M, G, per_group, bits):
+    K, N = 1536, 144
+    inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=15, scale="group" if per_group else "channel",
+                                  zero_rows=(1,), with_bias=True)
+    xd = bf16_dev(inp["x"])
+    wd, sd, bd = u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+    out = host(ck.linear(xd, G, bits, wd, sd, per_group, bias=bd))
+    codes, scales = ck.rotate_quant(xd, G, bits)
+    codes, scales = host(codes), host(scales)
+    # codes against the oracle's own rotation (tolerance of the fp32 transform)
+    ref_codes, _ = oracle.rotate_quant(inp["x"], G, bits)
+    assert_codes_close(codes, ref_codes)
+    # output against the oracle epilogue on the GPU's own codes and scales
+    ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
+    assert_output_close(out, ref)
+    assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
+
+
+def test_linear_x_scale_power_of_two_is_exact():
+    inp = workloads.linear_inputs(20, 512, 64, seed=2, outliers=4, scale="channel")
+    xd, wd, sd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"])
+    a = host(ck.linear(xd, 64, 8, wd, sd, False))
+    b = host(ck.linear(xd, 64, 8, wd, sd, False, x_scale=4.0))
+    assert np.array_equal(b, 4.0 * a)
+
+
+def test_linear_int8_weight_tensor_and_strided_weights():
+    """Packed weights given as an int8 tensor, and as a strided view, give the same bytes."""
+    M, K, N = 10, 512, 48
+    inp = workloads.linear_inputs(M, K, N, seed=4, outliers=3, scale="group")
+    wide = workloads.packed_weights(N, K, seed=4, ld=K // 2 + 64)
+    assert np.array_equal(wide[:, :K // 2], inp["packed"])
+    xd, sd = bf16_dev(inp["x"]), bf16_dev(inp["w_scales"])
+    ref = host(ck.linear(xd, 64, 8, u8_dev(inp["packed"]), sd, True))
+    as_i8 = u8_dev(inp["packed"]).view(torch.int8)
+    strided = u8_dev(wide)[:, :K // 2]
+    assert np.array_equal(host(ck.linear(xd, 64, 8, as_i8, sd, True)), ref)
+    assert np.array_equal(host(ck.linear(xd, 64, 8, strided, sd, True)), ref)
+
+
+def test_empty_batch_is_noop():
+    inp = workloads.linear_inputs(1, 256, 32, seed=1, outliers=0, scale="channel")
+    x = bf16_dev(inp["x"])[:0]
+    out = ck.linear(x, 64, 8, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), False)
+    assert out.shape == (0, 32)
+
+
+def test_matmul_deterministic():
+    inp = workloads.linear_inputs(300, 1024, 528, seed=8, outliers=10, scale="group")
+    args = (bf16_dev(inp["x"]), 64, 4, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), True)
+    assert torch.equal(ck.linear(*args), ck.linear(*args))
+    inp = workloads.linear_inputs(8, 1024, 528, seed=8, outliers=10, scale="group")
+    args = (bf16_dev(inp["x"]), 64, 8, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), True)
+    assert torch.equal(ck.linear(*args), ck.linear(*args))
+
+
+def test_errors_raise():
+    x = bf16_dev(workloads.activations(4, 512, seed=0))
+    with pytest.raises(ck.CKError):
+        ck.rotate_quant(x, 32, 8)          # unsupported G
+    with pytest.raises(ck.CKError):
+        ck.rotate_quant(x[:, :96], 16, 8)  # K % 64: unsupported
+    with pytest.raises(ValueError):
+        ck.rotate_quant(x[:, :320], 256, 8)  # K % G: invalid
+
+
+# ----------------------------------------------------------------- AWQ W4A16
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 3072, 1024), (3, 1024, 272), (8, 4096, 64), (1, 64, 16)])
+def test_awq_gemv_matches_oracle(M, K, N):
+    d = workloads.awq_inputs(M, K, N, seed=K + N, with_bias=(M == 3))
+    out = ck.w4a16_gemv(bf16_dev(d["x"]), u8_dev(d["packed"]), bf16_dev(d["scales"]), bf16_dev(d["zeros"]),
+                        bias=None if d["bias"] is None else bf16_dev(d["bias"]))
+    ref = oracle.awq_gemv(d["x"], d["packed"], d["scales"], d["zeros"], bias=d["bias"])
+    assert_output_close(host(out), ref)
