@@ -1,18 +1,20 @@
 """Benchmark of the ConvRot packed-INT4 linear on one MI355X.
 
 Headline step: the W4A8 ConvRot decode linear at M = 1, K = 3840, N = 10240,
-G = 64, per-group (64) bf16 weight scales -- rotate-quant of the activation row
-followed by the weight-streaming GEMV, i.e. exactly the two launches
-ck_w4a8_linear makes (issued here through ck_rotate_quant and ck_w4_gemv so
-that HIP events can bracket the GEMV).  The metric is packed-weight bandwidth:
-N * K / 2 bytes per step over the step time.  Inputs are resident in HBM before
-timing starts; the step cycles through enough weight copies (> 512 MiB) that
-every step reads its weights from HBM, not from the 256 MiB Infinity Cache.
+G = 64, per-group (64) bf16 weight scales, through ck_w4a8_linear -- one
+launch in which the activation row is rotated and quantised while the packed
+weights stream in.  The metric is packed-weight bandwidth: N * K / 2 bytes per
+step over the step time.  Inputs are resident in HBM before timing starts; the
+steps cycle through enough weight copies (> 512 MiB) that every step reads its
+weights from HBM, not from the 256 MiB Infinity Cache.  The K timed steps are
+captured in one HIP graph and replayed between two synchronisations, so the
+figure is the GPU's and not the Python launch path's (reported separately as
+eager_us_per_step).
 
 After the timed region the other metric figures are measured the same way
 (ConvRot linear microseconds and int8 TOPS at M = 8192, the decode GEMV at
-M = 4 and 8, standalone rotate-quant, the AWQ W4A16 GEMV) and reported under
-"also"; the CPU oracle is timed on a bounded sample under "cpu_baseline".
+M = 4 and 8, M = 32, standalone rotate-quant, the AWQ W4A16 GEMV) and reported
+under "also"; the CPU oracle is timed on a bounded sample under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
 """
@@ -31,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_decode_gemv_m1_k3840_n10240_traffic.txt")
-GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_skinny.hip", "packed_int4_convrot_amd/csrc/ck_device.h"]
+GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv.hip", "packed_int4_convrot_amd/csrc/ck_device.h"]
 
 
 def log(msg):
@@ -105,56 +107,36 @@ def main():
     scales0 = bf16(inp["w_scales"])
     packs = [packed0] + [packed0.clone() for _ in range(args.copies - 1)]
     scls = [scales0] + [scales0.clone() for _ in range(args.copies - 1)]
-    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
-    rs = torch.empty((M,), dtype=torch.float32, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
-        ck.rotate_quant(x, G, 8, codes, rs)
-        if ev is not None:
-            ev[0].record(stream)
-        ck.gemv(codes, rs, packs[i % args.copies], scls[i % args.copies], True, out=out)
-        if ev is not None:
-            ev[1].record(stream)
+    def step(i):
+        ck.linear(x, G, 8, packs[i % args.copies], scls[i % args.copies], True, out=out, workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
+    g_warm = capture(torch, step, args.warmup)
+    g_steps = capture(torch, step, args.steps)
+    g_warm.replay()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
+    g_steps.replay()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_step = t_start.elapsed_time(t_end) / args.steps
     packed_bytes = N * K // 2
     value = packed_bytes / (ms_step * 1e-3) / 1e9
-
-    alg_bytes = packed_bytes + (K // 64) * N * 2 + M * K + M * 4 + M * N * 2
-    achieved = alg_bytes / (gemv_ms * 1e-3) / 1e9
+    # The step is one launch (rotate-quant fused into the GEMV), so the
+    # average launch duration is the timed region over the steps.
+    alg_bytes = packed_bytes + (K // 64) * N * 2 + M * K * 2 + M * N * 2
+    achieved = alg_bytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(alg_bytes)
-    log("bench: step %.2f us (wall %.2f us), GEMV %.2f us, %.0f GB/s packed" %
-        (ms_step * 1e3, wall / args.steps * 1e6, gemv_ms * 1e3, value))
-
-    # the same step through the single whole-linear entry point, for comparison
-    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(args.steps):
-        ck.linear(x, G, 8, packs[i % args.copies], scls[i % args.copies], True, out=out, workspace=ws)
-    b.record(stream)
-    torch.cuda.synchronize()
-    linear_us = a.elapsed_time(b) / args.steps * 1e3
+    eager_us = _time_eager(torch, step, stream, min(args.steps, 100)) * 1.0
+    log("bench: step %.3f us (wall %.2f us), %.0f GB/s packed, eager %.2f us/step" %
+        (ms_step * 1e3, wall / args.steps * 1e6, value, eager_us))
 
     result = {
         "metric": "ConvRot linear us + int8 TOPS (M=8192) and packed-weight GB/s (M=1 GEMV)",
@@ -163,7 +145,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -172,12 +154,13 @@ def main():
                 "uniform [0.002,0.02] bf16 group scales)",
         "config": {"workload": "w4a8_convrot_decode_linear", "M": M, "K": K, "N": N, "G": G,
                    "weight_scales": "per-group (64), bf16", "weight_copies_cycled": args.copies,
-                   "step": "ck_rotate_quant + ck_w4_gemv (the launches of ck_w4a8_linear)"},
-        "roofline": {"bound": "hbm", "kernel": "w4_skinny_kernel (decode GEMV)",
+                   "step": "ck_w4a8_linear (rotate-quant fused into the decode GEMV, one launch)",
+                   "timing": "K steps captured in one HIP graph, replayed between synchronisations"},
+        "roofline": {"bound": "hbm", "kernel": "w4_gemv_kernel (fused rotate-quant + decode GEMV)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(gemv_ms * 1e3, 3)},
-        "whole_linear_entry_us": round(linear_us, 3),
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(ms_step * 1e3, 3)},
+        "eager_us_per_step": round(eager_us, 3),
     }
 
     # ------------------------------------------------------------ extras
@@ -191,8 +174,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _time(fn, stream, iters, warmup=3):
-    import torch
+def capture(torch, fn, n):
+    """A HIP graph holding n calls fn(0..n-1) (the library allocates and syncs nothing)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    return g
+
+
+def _time_eager(torch, fn, stream, iters, warmup=3):
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -203,6 +200,21 @@ def _time(fn, stream, iters, warmup=3):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / iters * 1e3  # us
+
+
+def _time(fn, stream, iters, warmup=3):
+    """Microseconds per call, from a HIP graph of `iters` calls replayed once."""
+    import torch
+    g_w = capture(torch, fn, warmup)
+    g = capture(torch, fn, iters)
+    g_w.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters * 1e3
 
 
 def extras(ck, workloads, torch, dev, bf16, u8, stream):

@@ -184,7 +184,10 @@ int run_gemm(const char *fn, const int8_t *codes, int64_t ldq, const float *rs, 
 {
     const bool pg = w.kind == CK_WS_PER_GROUP;
     int e;
-    if (M <= 64 && ck::w4_skinny_supports(M, K))
+    if (ck::w4_gemv_supports(M, K))
+        e = ck::launch_w4_gemv(nullptr, 0, 0, 0, codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw,
+                               w.scales, pg, (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
+    else if (M <= 64 && ck::w4_skinny_supports(M, K))
         e = ck::launch_w4_skinny(codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
                                  (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
     else
@@ -200,7 +203,8 @@ int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, c
     CK_TRY(check_m(fn, M));
     CK_TRY(check_k(fn, K));
     CK_TRY(check_weights(fn, w, K, true));
-    if (gemv && (M > 8 || !ck::w4_skinny_supports(M < 1 ? 1 : M, K)))
+    const int64_t m1 = M < 1 ? 1 : M;
+    if (gemv && (M > 8 || !(ck::w4_gemv_supports(m1, K) || ck::w4_skinny_supports(m1, K))))
         return fail(CK_ERR_UNSUPPORTED, "%s: decode GEMV takes 1 <= M <= 8 and K <= 8192 (M=%lld, K=%lld)",
                     fn, (long long)M, (long long)K);
     if (M == 0)
@@ -253,9 +257,17 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
         overlap(rw, scales_span(w, K)) || overlap(rw, span(bias, 1, w.N, w.N, 2)))
         return fail(CK_ERR_WORKSPACE, "%s: workspace overlaps an input", fn);
 
+    const int qmax = bits == 8 ? 127 : 7;
+    if (ck::w4_gemv_fused_supports(M, K)) {
+        // Decode shapes: one launch that rotates, quantises and multiplies.
+        const int e = ck::launch_w4_gemv(x, ldx, G, qmax, nullptr, 0, nullptr, (int)M, (int)K, w.packed,
+                                         w.ldw, w.scales, w.kind == CK_WS_PER_GROUP, (int)w.N, bias,
+                                         x_scale, out, ldo, nullptr, 0, stream);
+        return hip_status(e, fn);
+    }
     int8_t *codes = static_cast<int8_t *>(ws);
     float *rs = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round_up((size_t)(M * K), kWsAlign));
-    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, bits == 8 ? 127 : 7, codes, K, rs,
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, qmax, codes, K, rs,
                                           nullptr, 0, stream);
     if (e != 0)
         return hip_status(e, fn);

@@ -11,6 +11,17 @@ int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
                         void *stream);
 
+// Decode GEMV for 1 <= M <= 4 (VALU dot4, 1 KiB coalesced weight rows).  With
+// G != 0 it rotates and quantises the bf16 rows x itself (fused linear); with
+// G == 0 it reads given codes and row_scales.  acc_out != nullptr (G == 0
+// only) selects the int32 test epilogue.
+int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
+                   const float *row_scales, int M, int K, const uint8_t *packed, int64_t ldw,
+                   const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias, float x_scale,
+                   uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
+bool w4_gemv_supports(int64_t M, int64_t K);
+bool w4_gemv_fused_supports(int64_t M, int64_t K);  // G != 0 form
+
 // Skinny path: M <= 64, weights streamed once, activations held in registers.
 // acc_out != nullptr selects the int32 test epilogue.
 int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,

@@ -50,28 +50,26 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     const int col = lane % 16;
     const int kb = lane / 16;
 
-    // Activation operands for this wave's groups, permuted to the decode order.
-    v4i a[GPW][MT];
+    // Issue the activation loads of this wave's groups and the first tile's
+    // weight loads before any of them is used, so that all of them are in
+    // flight together.  Addresses are clamped into the matrices; the values
+    // of out-of-range rows / groups are replaced by zero afterwards.
+    const int ntiles = N / 16;
+    int tile = blockIdx.x;
+    u32x4 raw[GPW][MT];
 #pragma unroll
     for (int j = 0; j < GPW; ++j)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + col;
-            if (j < cnt && m < M) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(codes + (int64_t)m * ldq +
-                                                                 64 * (g0 + j) + 16 * kb);
-                a[j][mt] = act_perm16(w.x, w.y, w.z, w.w);
-            } else {
-                a[j][mt] = v4i{0, 0, 0, 0};
-            }
+            const int m = min(mt * 16 + col, M - 1);
+            const int g = min(g0 + j, ng - 1);
+            raw[j][mt] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + 64 * g + 16 * kb);
         }
-
-    const int ntiles = N / 16;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int n = tile * 16 + col;
+    u32x2 bw[GPW];
+    uint16_t sw[GPW];
+    auto load_tile = [&](int t) {
+        const int n = t * 16 + col;
         const uint8_t *wrow = packed + (int64_t)n * ldw + 8 * kb + 32 * g0;
-        u32x2 bw[GPW];
-        uint16_t sw[GPW];
 #pragma unroll
         for (int j = 0; j < GPW; ++j)
             if (j < cnt) {
@@ -79,6 +77,22 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
                 if constexpr (PER_GROUP)
                     sw[j] = w_scales[(int64_t)(g0 + j) * N + n];
             }
+    };
+    if (tile < ntiles)
+        load_tile(tile);
+
+    // Activation operands, permuted to the decode order.
+    v4i a[GPW][MT];
+#pragma unroll
+    for (int j = 0; j < GPW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const bool live = j < cnt && mt * 16 + col < M;
+            const v4i p = act_perm16(raw[j][mt][0], raw[j][mt][1], raw[j][mt][2], raw[j][mt][3]);
+            a[j][mt] = live ? p : v4i{0, 0, 0, 0};
+        }
+
+    for (; tile < ntiles; tile += gridDim.x) {
 
         float y[MT][4];
         v4i acc[MT];
@@ -109,6 +123,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
                         acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, acc[mt], 0, 0, 0);
                 }
             }
+
+        if (tile + (int)gridDim.x < ntiles)
+            load_tile(tile + gridDim.x);  // next tile's weights fly during the reduction
 
         // Cross-wave reduction: red[w][mt][lane][i].
 #pragma unroll

@@ -61,33 +61,24 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
     const int cnt = max(0, min(gpw, ng - g0));
     const int col = lane % 16, kb = lane / 16;
 
-    // Activation operands (two 32-wide halves per group) and the group sums X.
-    v8bf a[kGpw][2];
-    v4f xs[kGpw];
-    const v8bf ones = as_v8bf(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+    // All activation loads and the first tile's weight loads are issued
+    // before any is used (clamped addresses; out-of-range values zeroed).
+    const int ntiles = N / 16;
+    int tile = blockIdx.x;
+    u32x4 raw[kGpw][2];
 #pragma unroll
-    for (int j = 0; j < kGpw; ++j) {
+    for (int j = 0; j < kGpw; ++j)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            if (j < cnt && col < M) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(
-                    x + (int64_t)col * ldx + 64 * (g0 + j) + 16 * kb + 8 * s);
-                a[j][s] = x_perm8(w);
-            } else {
-                a[j][s] = as_v8bf(0u, 0u, 0u, 0u);
-            }
+            const int m = min(col, M - 1);
+            const int g = min(g0 + j, ng - 1);
+            raw[j][s] = *reinterpret_cast<const u32x4 *>(x + (int64_t)m * ldx + 64 * g + 16 * kb + 8 * s);
         }
-        v4f z{0.f, 0.f, 0.f, 0.f};
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][0], ones, z, 0, 0, 0);
-        xs[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][1], ones, z, 0, 0, 0);
-    }
-
-    const int ntiles = N / 16;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int n = tile * 16 + col;
+    u32x2 bw[kGpw];
+    uint16_t sv[kGpw], zv[kGpw];
+    auto load_tile = [&](int t) {
+        const int n = t * 16 + col;
         const uint8_t *wrow = packed + (int64_t)n * ldw + 8 * kb + 32 * g0;
-        u32x2 bw[kGpw];
-        uint16_t sv[kGpw], zv[kGpw];
 #pragma unroll
         for (int j = 0; j < kGpw; ++j)
             if (j < cnt) {
@@ -95,6 +86,28 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
                 sv[j] = scales[(int64_t)(g0 + j) * N + n];
                 zv[j] = zeros[(int64_t)(g0 + j) * N + n];
             }
+    };
+    if (tile < ntiles)
+        load_tile(tile);
+
+    // Activation operands (two 32-wide halves per group) and the group sums X.
+    v8bf a[kGpw][2];
+    v4f xs[kGpw];
+    const v8bf ones = as_v8bf(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+#pragma unroll
+    for (int j = 0; j < kGpw; ++j) {
+        const bool live = j < cnt && col < M;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 w = make_uint4(raw[j][s][0], raw[j][s][1], raw[j][s][2], raw[j][s][3]);
+            a[j][s] = live ? x_perm8(w) : as_v8bf(0u, 0u, 0u, 0u);
+        }
+        v4f z{0.f, 0.f, 0.f, 0.f};
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][0], ones, z, 0, 0, 0);
+        xs[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][1], ones, z, 0, 0, 0);
+    }
+
+    for (; tile < ntiles; tile += gridDim.x) {
         float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kGpw; ++j)
@@ -108,6 +121,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
                 for (int i = 0; i < 4; ++i)
                     y[i] = __builtin_fmaf(s, p[i], __builtin_fmaf(c, xs[j][i], y[i]));
             }
+        if (tile + (int)gridDim.x < ntiles)
+            load_tile(tile + gridDim.x);
         *reinterpret_cast<float4 *>(red + (wave * kWave + lane) * 4) = make_float4(y[0], y[1], y[2], y[3]);
         __syncthreads();
         for (int e = threadIdx.x; e < kWave * 4; e += blockDim.x) {

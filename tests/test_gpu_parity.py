@@ -149,7 +149,7 @@ def test_gemv_entry_matches_oracle(per_group):
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("per_group", [True, False])
 @pytest.mark.parametrize("G", [16, 64, 256])
-@pytest.mark.parametrize("M", [3, 40, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 40, 300])
 def test_linear_end_to_end(M, G, per_group, bits):
     K, N = 1536, 144
     inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=15, scale="group" if per_group else "channel",
@@ -166,6 +166,49 @@ def test_linear_end_to_end(M, G, per_group, bits):
     ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
     assert_output_close(out, ref)
     assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("G", [16, 64, 256])
+def test_fused_decode_linear_equals_two_step_path(M, G):
+    """The one-launch decode linear (rotate-quant inside the GEMV) gives bit-identical
+    outputs to ck_rotate_quant followed by ck_w4_gemv."""
+    K, N = 3840, 1024
+    for per_group in (True, False):
+        inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=8, scale="group" if per_group else "channel",
+                                      with_bias=True)
+        xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+        fused = ck.linear(xd, G, 8, wd, sd, per_group, bias=bd)
+        codes, scales = ck.rotate_quant(xd, G, 8)
+        two = ck.gemv(codes, scales, wd, sd, per_group, bias=bd)
+        assert torch.equal(fused, two)
+
+
+@pytest.mark.parametrize("M", [1, 8, 300])
+def test_graph_replay_matches_eager(M):
+    """Captured into a HIP graph, the linear gives the eager result on every replay."""
+    K, N = 1024, 272
+    inp = workloads.linear_inputs(M, K, N, seed=M, outliers=5, scale="group", with_bias=True)
+    xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
+    eager = ck.linear(xd, 64, 8, wd, sd, True, bias=bd)
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ck.linear(xd, 64, 8, wd, sd, True, bias=bd, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ck.linear(xd, 64, 8, wd, sd, True, bias=bd, out=out, workspace=ws)
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        ck.rotate_quant(xd, 256, 4)  # unrelated eager work between replays
 
 
 def test_linear_x_scale_power_of_two_is_exact():
