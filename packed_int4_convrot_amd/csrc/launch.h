@@ -11,8 +11,8 @@ int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
                         void *stream);
 
-// Decode GEMV for 1 <= M <= 4 (VALU dot4, 1 KiB coalesced weight rows).  With
-// G != 0 it rotates and quantises the bf16 rows x itself (fused linear); with
+// Decode GEMV for 1 <= M <= 8 (VALU dot4, 1 KiB coalesced weight rows).  With
+// G != 0 (M = 1) it rotates and quantises the bf16 row x itself (fused linear); with
 // G == 0 it reads given codes and row_scales.  acc_out != nullptr (G == 0
 // only) selects the int32 test epilogue.
 int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,

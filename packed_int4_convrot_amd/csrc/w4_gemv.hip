@@ -1,5 +1,5 @@
-// Decode GEMV for 1 <= M <= 4 activation rows, optionally fused with the
-// rotate-quant of those rows.
+// Decode GEMV for 1 <= M <= 8 activation rows, optionally (M = 1) fused with
+// the rotate-quant of that row.
 //
 // Prior art: the W4A8 decode GEMV of "[PR #182] HIP port of #176: W4A8 decode
 // GEMV and fused GatedDeltaNet decode" (description): register-side int4
@@ -34,9 +34,15 @@ namespace ck {
 namespace {
 
 constexpr int kMaxWaves = 8;  // K <= 16384
-// The fused form keeps each lane's 32 rotated fp32 values per activation row
-// in registers across the block-wide absmax; beyond two rows they spill.
-constexpr int kMaxFusedRows = 2;
+#ifndef CK_GEMV_ROWS
+#define CK_GEMV_ROWS 8  // weight rows per block (8 or 16)
+#endif
+// The fused form pays the rotation once per block; measured on MI355X it is
+// faster than a separate rotate-quant launch only for a single activation row.
+constexpr int kMaxFusedRows = 1;
+#ifndef CK_GEMV_MAX_M
+#define CK_GEMV_MAX_M 8
+#endif
 
 template <int MASK>
 __device__ __forceinline__ uint32_t lane_xor_u(uint32_t v)
@@ -138,17 +144,36 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     const bool active = kbase < K;
     const int kc = active ? kbase : K - 32;  // clamped: every address stays inside the row
 
-    // 1. weights (and their scales) for the R rows: issued before anything else.
-    u32x4 wv[R];
+    // 1. Loads, in this order: the activations (small, usually L2-resident),
+    //    the weight scales, then the R weight rows.  Loads retire in issue
+    //    order, so the activation work below waits only for the activations,
+    //    and row r's dot products only for rows 0..r, while the remaining
+    //    weight rows are still streaming in.
+    u32x4 araw[M][FUSED ? 4 : 2];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        wv[r] = load_nt16(packed + (int64_t)(n0 + r) * ldw + kc / 2);
+    for (int m = 0; m < M; ++m) {
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                araw[m][c] = *reinterpret_cast<const u32x4 *>(x + (int64_t)m * ldx + kc + 8 * c);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                araw[m][c] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + kc + 16 * c);
+        }
+    }
     uint16_t sv[PER_GROUP ? R : 1];
     if constexpr (PER_GROUP) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
             sv[r] = w_scales[(int64_t)(kc / 64) * N + n0 + r];
     }
+    u32x4 wv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        wv[r] = load_nt16(packed + (int64_t)(n0 + r) * ldw + kc / 2);
+    // Keep the compiler from moving these loads below the activation work.
+    __builtin_amdgcn_sched_barrier(0);
 
     // 2. activation codes for this lane's 32 columns: even k in alo, odd k in ahi.
     uint32_t alo[M][4], ahi[M][4];
@@ -160,10 +185,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float(&v)[32] = vv[m];
-            const uint16_t *xs = x + (int64_t)m * ldx + kc;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(xs + 8 * c);
+                const u32x4 w = araw[m][c];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     v[8 * c + 2 * j] = active ? __uint_as_float(w[j] << 16) : 0.f;
@@ -219,9 +243,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     } else {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const int8_t *cs = codes + (int64_t)m * ldq + kc;
-            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(cs);
-            const u32x4 c1 = *reinterpret_cast<const u32x4 *>(cs + 16);
+            const u32x4 c0 = araw[m][0];
+            const u32x4 c1 = araw[m][1];
             const v4i p0 = act_perm16(c0[0], c0[1], c0[2], c0[3]);
             const v4i p1 = act_perm16(c1[0], c1[1], c1[2], c1[3]);
             const uint32_t q[8] = {(uint32_t)p0[0], (uint32_t)p0[1], (uint32_t)p0[2], (uint32_t)p0[3],
@@ -344,7 +367,7 @@ hipError_t launch_m(int G, bool pg, bool i32, const uint16_t *x, int64_t ldx, fl
 
 }  // namespace
 
-bool w4_gemv_supports(int64_t M, int64_t K) { return M >= 1 && M <= 4 && K <= 2048 * kMaxWaves; }
+bool w4_gemv_supports(int64_t M, int64_t K) { return M >= 1 && M <= CK_GEMV_MAX_M && K <= 2048 * kMaxWaves; }
 bool w4_gemv_fused_supports(int64_t M, int64_t K) { return w4_gemv_supports(M, K) && M <= kMaxFusedRows; }
 
 int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
@@ -357,13 +380,20 @@ int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool i32 = acc_out != nullptr;
     const float q = (float)qmax;
-    constexpr int R = 16;
+    constexpr int R = CK_GEMV_ROWS;
     hipError_t e;
     switch (M) {
     case 1: e = launch_m<1, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 2: e = launch_m<2, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 3: e = launch_m<3, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    default: e = launch_m<4, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+    case 4: e = launch_m<4, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+#if CK_GEMV_MAX_M > 4
+    case 5: e = launch_m<5, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+    case 6: e = launch_m<6, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+    case 7: e = launch_m<7, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+    case 8: e = launch_m<8, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+#endif
+    default: e = hipErrorInvalidValue; break;
     }
     return (int)e;
 }

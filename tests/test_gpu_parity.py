@@ -153,7 +153,7 @@ def test_gemv_entry_matches_oracle(per_group):
 def test_linear_end_to_end(M, G, per_group, bits):
     K, N = 1536, 144
     inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=15, scale="group" if per_group else "channel",
-                                  zero_rows=(1,), with_bias=True)
+                                  zero_rows=(1,) if M > 1 else (), with_bias=True)
     xd = bf16_dev(inp["x"])
     wd, sd, bd = u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
     out = host(ck.linear(xd, G, bits, wd, sd, per_group, bias=bd))
@@ -165,7 +165,8 @@ def test_linear_end_to_end(M, G, per_group, bits):
     # output against the oracle epilogue on the GPU's own codes and scales
     ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
     assert_output_close(out, ref)
-    assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
+    if M > 1:
+        assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
 
 
 @pytest.mark.parametrize("M", [1, 2])
