@@ -50,7 +50,8 @@
  *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales.
  *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
  *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
- *    ldw % 16 == 0; out 4-byte aligned with ldo % 2 == 0.
+ *    ldw % 16 == 0; outputs 16-byte aligned with 16-byte aligned rows
+ *    (bf16: ldo % 8 == 0; int32 test outputs: lda % 4 == 0).
  */
 #ifndef CK_H
 #define CK_H

@@ -154,16 +154,17 @@ Range scales_span(const Weights &w, int64_t K)
     return span(w.scales, 1, w.N, w.N, 2);
 }
 
+// Outputs are written with 16-byte stores: 16-byte aligned rows.
 int check_out(const char *fn, const void *out, int64_t N, int64_t ldo, size_t esize)
 {
     if (!out)
         return fail(CK_ERR_INVALID_ARG, "%s: output is NULL", fn);
-    if (ldo < N || ldo % 2 != 0)
-        return fail(CK_ERR_INVALID_ARG, "%s: output stride (%lld) must be >= N and even", fn,
-                    (long long)ldo);
-    if (!aligned(out, 4))
-        return fail(CK_ERR_INVALID_ARG, "%s: output must be 4-byte aligned", fn);
-    (void)esize;
+    const int64_t per16 = 16 / (int64_t)esize;
+    if (ldo < N || ldo % per16 != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: output stride (%lld) must be >= N and a multiple of %lld",
+                    fn, (long long)ldo, (long long)per16);
+    if (!aligned(out, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: output must be 16-byte aligned", fn);
     return CK_OK;
 }
 

@@ -38,6 +38,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
 // Byte permute of the 8 bytes {hi:lo}: selector byte values 0..3 pick bytes of
 // `lo`, 4..7 bytes of `hi`, 0x0c gives 0x00.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)

@@ -97,6 +97,8 @@ def gq(fn=None, codes=P, ldq=256, rs=P2, M=4, K=256, packed=P3, ldw=128, ws=P4, 
     (dict(ws=None), ck.CK_ERR_INVALID_ARG),
     (dict(out=None), ck.CK_ERR_INVALID_ARG),
     (dict(ldo=32), ck.CK_ERR_INVALID_ARG),
+    (dict(ldo=68), ck.CK_ERR_INVALID_ARG),       # rows not 16-byte aligned
+    (dict(out=P5 + 4), ck.CK_ERR_INVALID_ARG),   # output not 16-byte aligned
     (dict(out=P3), ck.CK_ERR_INVALID_ARG),       # overlaps the packed weights
     (dict(out=P + 128), ck.CK_ERR_INVALID_ARG),  # overlaps the codes
     (dict(rs=None), ck.CK_ERR_INVALID_ARG),
