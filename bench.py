@@ -17,6 +17,12 @@ M = 4 and 8, M = 32, standalone rotate-quant, the AWQ W4A16 GEMV) and reported
 under "also"; the CPU oracle is timed on a bounded sample under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+
+HBM traffic of the headline kernel comes from two rocprofv3 counter passes
+(FETCH_SIZE, then WRITE_SIZE) over this script, scaled by what the same
+counters read for a plain copy of known size (`--calibration-copy`);
+`--write-traffic` turns the four counter CSVs into the record that
+`roofline.traffic` is read from.
 """
 from __future__ import annotations
 
@@ -48,6 +54,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=32, help="weight copies cycled through (cold cache)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="only run a plain elementwise copy of CALIB_BYTES (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="write the traffic record from rocprofv3 counter_collection CSVs and exit")
     return ap.parse_args()
 
 
@@ -57,6 +67,76 @@ def sources_sha(paths):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+CALIB_BYTES = 256 << 20        # bytes read and bytes written by the calibration copy
+CALIB_KERNEL = "neg_kernel"    # torch's elementwise negation: one read and one write per element
+HEADLINE_KERNEL = "w4_gemv_kernel<1,"
+
+
+def calibration_copy():
+    """A plain elementwise copy of known size (int32 negation, CALIB_BYTES in and out),
+    run a few times, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.neg(src, out=dst)
+        torch.neg(dst, out=src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_each_way": CALIB_BYTES, "dispatches": 8}), flush=True)
+
+
+def _counter_per_dispatch(path, kernel_substring, counter):
+    """Mean over dispatches of a kernel of one counter (summed over its instances) in a
+    rocprofv3 counter_collection CSV, with the dispatch count."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if kernel_substring in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                per[row["Dispatch_Id"]] = per.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s dispatches of %r in %s" % (counter, kernel_substring, path))
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, alg_bytes):
+    fetch_kib, nf = _counter_per_dispatch(fetch_csv, HEADLINE_KERNEL, "FETCH_SIZE")
+    write_kib, nw = _counter_per_dispatch(write_csv, HEADLINE_KERNEL, "WRITE_SIZE")
+    cal_fetch_kib, ncf = _counter_per_dispatch(cal_fetch_csv, CALIB_KERNEL, "FETCH_SIZE")
+    cal_write_kib, ncw = _counter_per_dispatch(cal_write_csv, CALIB_KERNEL, "WRITE_SIZE")
+    f_scale = CALIB_BYTES / (cal_fetch_kib * 1024.0)
+    w_scale = CALIB_BYTES / (cal_write_kib * 1024.0)
+    hbm = fetch_kib * 1024.0 * f_scale + write_kib * 1024.0 * w_scale
+    rec = {"kernel": HEADLINE_KERNEL, "sources_sha": sources_sha(GEMV_SOURCES),
+           "fetch_kib_per_dispatch": round(fetch_kib, 1), "write_kib_per_dispatch": round(write_kib, 1),
+           "dispatches": [nf, nw], "calibration_fetch_kib": round(cal_fetch_kib, 1),
+           "calibration_write_kib": round(cal_write_kib, 1), "calibration_dispatches": [ncf, ncw],
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes_per_launch": alg_bytes,
+           "traffic_over_algorithmic": round(hbm / alg_bytes, 4)}
+    text = ("HBM traffic of the fused W4A8 decode linear kernel (M=1, K=3840, N=10240, G=64, per-group scales)\n"
+            "from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the same counter\n"
+            "on a plain copy of %d bytes each way (torch int32 negation).\n\n"
+            "Commands (repository root, TMPDIR=/tmp):\n"
+            "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 20 --warmup 2 --no-extras --no-cpu-baseline\n"
+            "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 20 --warmup 2 --no-extras --no-cpu-baseline\n"
+            "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_cal_fetch -o run -- python3 bench.py --calibration-copy\n"
+            "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_cal_write -o run -- python3 bench.py --calibration-copy\n"
+            "  python3 bench.py --write-traffic <the four run_counter_collection.csv files>\n\n"
+            "JSON: %s\n" % (CALIB_BYTES, json.dumps(rec)))
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def headline_alg_bytes(M, K, N):
+    """Bytes the fused M = 1 step must move: packed weights, group scales, the bf16
+    activation row and the bf16 output row."""
+    return N * K // 2 + (K // 64) * N * 2 + M * K * 2 + M * N * 2
 
 
 def measured_traffic(bytes_per_launch_alg):
@@ -74,12 +154,19 @@ def measured_traffic(bytes_per_launch_alg):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, alg_bytes=headline_alg_bytes(1, 3840, 10240))
+        return
     if args.gpus != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path, run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
+
+    if args.calibration_copy:
+        calibration_copy()
+        return
 
     import packed_int4_convrot_amd as ck
     import workloads
@@ -131,7 +218,7 @@ def main():
     value = packed_bytes / (ms_step * 1e-3) / 1e9
     # The step is one launch (rotate-quant fused into the GEMV), so the
     # average launch duration is the timed region over the steps.
-    alg_bytes = packed_bytes + (K // 64) * N * 2 + M * K * 2 + M * N * 2
+    alg_bytes = headline_alg_bytes(M, K, N)
     achieved = alg_bytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(alg_bytes)
     eager_us = _time_eager(torch, step, stream, min(args.steps, 100)) * 1.0
