@@ -178,10 +178,11 @@ int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
  * AWQ W4A16 product with fp activations (no activation quantisation):
  *   W[n,k]   = (q[n,k] - 8) * scales[k/Gw, n] + zeros[k/Gw, n]
  *   out[m,n] = sum_k x[m,k] * W[n,k]  (+ bias[n]), fp32 arithmetic, bf16 out.
- *   x       bf16 [M, ldx], 1 <= M <= 8 and K <= 4096 (CK_ERR_UNSUPPORTED
+ *   x       bf16 [M, ldx], 1 <= M <= 8 and K <= 16384 (CK_ERR_UNSUPPORTED
  *           otherwise)
  *   packed  uint8 [N, ldw] as in ck_w4_gemm_q
- *   scales, zeros  bf16 [K/Gw, N], Gw = 64
+ *   scales, zeros  bf16 [K/Gw, N], Gw = 64, each 16-byte aligned
+ *           (CK_ERR_INVALID_ARG otherwise)
  *   bias    bf16 [N] or NULL;  out bf16 [M, ldo]
  * The weight is never materialised; it is decoded in registers.
  */

@@ -389,10 +389,10 @@ int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const ui
     CK_TRY(check_k(fn, K));
     const Weights w{packed, ldw, scales, CK_WS_PER_GROUP, Gw, N};
     CK_TRY(check_weights(fn, w, K, true));
-    if (!zeros || !aligned(zeros, 2))
-        return fail(CK_ERR_INVALID_ARG, "%s: zeros must be a non-NULL 2-byte aligned pointer", fn);
+    if (!aligned(scales, 16) || !zeros || !aligned(zeros, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: scales and zeros must be non-NULL 16-byte aligned pointers", fn);
     if (M > 8 || !ck::w4a16_supports(K))
-        return fail(CK_ERR_UNSUPPORTED, "%s: takes 1 <= M <= 8 and K <= 4096 (M=%lld, K=%lld)", fn,
+        return fail(CK_ERR_UNSUPPORTED, "%s: takes 1 <= M <= 8 and K <= 16384 (M=%lld, K=%lld)", fn,
                     (long long)M, (long long)K);
     if (M == 0)
         return ok();

@@ -25,6 +25,18 @@ __device__ __forceinline__ u32x2 load_nt8(const void *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by
+// index.  This renumbering gives every XCD a contiguous run of logical
+// blocks, so neighbouring blocks that share cache lines (weight-scale rows,
+// activation tiles) hit in the same L2.  A bijection on [0, nblocks).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int b, int nblocks)
+{
+    const int xcd = b % kXcds, local = b / kXcds;
+    const int per = nblocks / kXcds, rem = nblocks % kXcds;
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 

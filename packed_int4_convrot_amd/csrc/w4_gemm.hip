@@ -38,7 +38,6 @@
 namespace ck {
 namespace {
 
-constexpr int kXcds = 8;
 constexpr int kStages = 4;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -83,10 +82,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
-    const int b = blockIdx.x;
-    const int xcd = b % kXcds, local = b / kXcds;
-    const int per = tiles / kXcds, rem = tiles % kXcds;
-    const int tile = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    const int tile = xcd_block(blockIdx.x, tiles);
     const int m0 = (tile / tiles_n) * BM;
     const int n0 = (tile % tiles_n) * BN;
 
@@ -236,40 +232,42 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                         }
             }
         } else {
-            // Column factors (weight scale / 16) and bias for this lane's 4 x 4 x WN columns.
-            float cs[WN][4][4], bc[WN][4][4];
+            // Stage the wave's 32 WM x 32 WN bf16 tile in LDS (rows padded to
+            // 16 bytes past the tile width) and write it back with 16-byte
+            // row-contiguous stores.  Column factors (weight scale / 16) and
+            // bias are loaded one 32-column tile at a time to bound registers.
+            constexpr int TW = WN * 32;          // tile width (columns)
+            constexpr int PITCH = TW * 2 + 16;   // bytes per staged row
+            float rsc[WM];
 #pragma unroll
-            for (int j = 0; j < WN; ++j)
+            for (int i = 0; i < WM; ++i)
+                rsc[i] = row_scales[min(m0w + i * 32 + l32, M - 1)] * x_scale;
+            __builtin_amdgcn_s_barrier();        // every wave is done with the operand stages
+            lds_u8 *wt = smem + wave * (WM * 32 * PITCH);
+#pragma unroll
+            for (int j = 0; j < WN; ++j) {
+                float cs[4][4], bc[4][4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int n = min(n0w + j * 32 + 8 * q + 4 * h + t, N - 1);
-                        cs[j][q][t] = 0.0625f * bf16_to_f32(w_scales[n]);
-                        bc[j][q][t] = bias ? bf16_to_f32(bias[n]) : 0.f;
+                        cs[q][t] = 0.0625f * bf16_to_f32(w_scales[n]);
+                        bc[q][t] = bias ? bf16_to_f32(bias[n]) : 0.f;
                     }
-            // Stage the wave's 32 WM x 32 WN bf16 tile in LDS (rows padded to
-            // 16 bytes past the tile width) and write it back with 16-byte
-            // row-contiguous stores.
-            constexpr int TW = WN * 32;          // tile width (columns)
-            constexpr int PITCH = TW * 2 + 16;   // bytes per staged row
-            __builtin_amdgcn_s_barrier();        // every wave is done with the operand stages
-            lds_u8 *wt = smem + wave * (WM * 32 * PITCH);
 #pragma unroll
-            for (int i = 0; i < WM; ++i) {
-                const int ml = i * 32 + l32;
-                const float rsc = row_scales[min(m0w + ml, M - 1)] * x_scale;
-#pragma unroll
-                for (int j = 0; j < WN; ++j)
+                for (int i = 0; i < WM; ++i) {
+                    const int ml = i * 32 + l32;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float v[4];
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            v[t] = __builtin_fmaf((float)acc[i][j][4 * q + t], cs[j][q][t] * rsc, bc[j][q][t]);
+                            v[t] = __builtin_fmaf((float)acc[i][j][4 * q + t], cs[q][t] * rsc[i], bc[q][t]);
                         const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                         *(__attribute__((address_space(3))) u32x2 *)(wt + ml * PITCH + (j * 32 + 8 * q + 4 * h) * 2) = pk;
                     }
+                }
             }
             constexpr int CHUNKS = TW * 2 / 16;      // 16-byte chunks per row
             constexpr int ROWS = kWave / CHUNKS;     // rows per store instruction

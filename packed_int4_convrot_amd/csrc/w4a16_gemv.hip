@@ -2,149 +2,189 @@
 // scales and zero points, W[n,k] = (q - 8) * s[k/64, n] + z[k/64, n]
 // ("comfy_kitchen/tensor/awq_w4a16.py", module docstring and dequantize()).
 // The page's eager path materialises W in bf16 and calls a matmul; here W is
-// never built.  Per 64-wide group g and output column n:
-//   y += s[g,n] * sum_k x_k (q_k - 8) + z[g,n] * X_g,   X_g = sum_k x_k
-//      = s[g,n] * P_g + (z[g,n] - 136 s[g,n]) * X_g,     P_g = sum_k x_k (128 + q_k)
-// P_g runs on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate): the
-// weight operand is bf16(128 + q), which is the exact bit pattern 0x4300 | q,
-// built from the packed bytes with one byte permute per two weights.  X_g is
-// computed once per group by the same instruction with an all-ones operand.
+// never built.  For a 64-wide group g and output column n,
+//   sum_k x_k W[n,k] = s[g,n] * P + (z[g,n] - 136 s[g,n]) * X,
+//   P = sum_k x_k (128 + q_k),   X = sum_k x_k,
+// and both sums split over any partition of the group's columns.
 //
-// Operand layouts (16 x 32 x 16): A lane l holds 8 bf16 of row m = l % 16,
-// k-block l / 16; B lane l holds 8 bf16 of column n = l % 16, k-block l / 16;
-// D lane l holds D[4*(l/16) + i][l % 16].  The weight decode yields k order
-// [0,2,4,6,1,3,5,7] inside each 8-wide block; the activations are permuted to
-// match when they are loaded (once per wave).
+// The product streams the weights once, so the kernel is laid out for HBM:
+//   * wave w of a block owns columns k in [2048 w, 2048 w + 2048); lane l owns
+//     the 32 columns from 2048 w + 32 l (half a group), i.e. 16 packed bytes of
+//     every weight row, so each load instruction reads 1 KiB of one row;
+//   * a block owns 8 consecutive weight rows n0 .. n0 + 7; a lane loads its
+//     activations, then the 8 scales and 8 zero points of its group for those
+//     rows (one 16-byte load each, N contiguous), then the 8 weight rows.
+//     Loads retire in issue order, so the activation work waits only for the
+//     activations while the weights stream in;
+//   * bf16(128 + q) is the bit pattern 0x4300 | q, so one byte permute against
+//     a 0x43 constant turns two nibbles into a bf16 pair; v_dot2_f32_bf16
+//     multiplies it with the matching activation pair and accumulates in fp32
+//     (the products are exact: 8-bit by 8-bit significands).  Low nibbles are
+//     even k and high nibbles odd k, so the activations are paired to match
+//     ((x0,x2), (x4,x6), (x1,x3), (x5,x7) per 8 columns) once per lane;
+//   * the per-lane partials s P + (z - 136 s) X of the 8 rows are summed by
+//     the transposed lane reduction, then across waves through LDS in a fixed
+//     order, and the bias is added once.
 #include "ck_device.h"
+#include "gemv_reduce.h"
 #include "launch.h"
 
 namespace ck {
 namespace {
 
-constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
-constexpr int kGpw = 8;  // K-groups per wave held in registers
+constexpr int kMaxWaves = 8;  // K <= 16384
+constexpr int kRows = 8;      // weight rows per block
 
-__device__ __forceinline__ v8bf as_v8bf(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
-    v4i v{(int)a, (int)b, (int)c, (int)d};
-    return __builtin_bit_cast(v8bf, v);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
 }
 
-// 8 bf16 (four dwords, natural k order) -> k order [0,2,4,6,1,3,5,7].
-__device__ __forceinline__ v8bf x_perm8(uint4 w)
-{
-    return as_v8bf(perm(w.y, w.x, 0x05040100u), perm(w.w, w.z, 0x05040100u),
-                   perm(w.y, w.x, 0x07060302u), perm(w.w, w.z, 0x07060302u));
-}
-
-// One packed dword (k = 0..7) -> bf16(128 + q) in k order [0,2,4,6,1,3,5,7].
-__device__ __forceinline__ v8bf w_bf16_plus128(uint32_t d)
-{
-    const uint32_t e = d & 0x0f0f0f0fu;
-    const uint32_t o = (d >> 4) & 0x0f0f0f0fu;
-    const uint32_t m = 0x43434343u;
-    return as_v8bf(perm(m, e, 0x04010400u), perm(m, e, 0x04030402u), perm(m, o, 0x04010400u),
-                   perm(m, o, 0x04030402u));
-}
-
+template <int M>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
-    const uint16_t *__restrict__ x, int64_t ldx, int M, int K, const uint8_t *__restrict__ packed,
-    int64_t ldw, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros, int N,
-    const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int64_t ldo, int gpw)
+    const uint16_t *__restrict__ x, int64_t ldx, int K, const uint8_t *__restrict__ packed, int64_t ldw,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros, int N,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int64_t ldo)
 {
-    extern __shared__ float red[];  // [KS][64][4]
-    const int ks = blockDim.x / kWave;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int ng = K / 64;
-    const int g0 = wave * gpw;
-    const int cnt = max(0, min(gpw, ng - g0));
-    const int col = lane % 16, kb = lane / 16;
+    constexpr int R = kRows;
+    __shared__ uint32_t s_red[kMaxWaves][R][M];
 
-    // All activation loads and the first tile's weight loads are issued
-    // before any is used (clamped addresses; out-of-range values zeroed).
-    const int ntiles = N / 16;
-    int tile = blockIdx.x;
-    u32x4 raw[kGpw][2];
+    const int nw = blockDim.x / kWave;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int n0 = xcd_block(blockIdx.x, gridDim.x) * R;
+    const int kbase = 2048 * wave + 32 * lane;
+    const bool active = kbase < K;
+    const int kc = active ? kbase : K - 32;  // clamped: every address stays inside the row
+    const int64_t g = kc / 64;
+
+    // Activation rows are handled in passes of up to 4 against the weight
+    // registers, which bounds the registers held for activation pairs.
+    constexpr int MC = M < 4 ? M : 4;
+    constexpr int NPASS = (M + MC - 1) / MC;
+
+    // 1. Loads: the first pass's activations, then the group's scales and zero
+    //    points, then the weights.
+    u32x4 xr[MC][4];
+    auto load_x = [&](int mb) {
 #pragma unroll
-    for (int j = 0; j < kGpw; ++j)
+        for (int m = 0; m < MC; ++m)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int m = min(col, M - 1);
-            const int g = min(g0 + j, ng - 1);
-            raw[j][s] = *reinterpret_cast<const u32x4 *>(x + (int64_t)m * ldx + 64 * g + 16 * kb + 8 * s);
-        }
-    u32x2 bw[kGpw];
-    uint16_t sv[kGpw], zv[kGpw];
-    auto load_tile = [&](int t) {
-        const int n = t * 16 + col;
-        const uint8_t *wrow = packed + (int64_t)n * ldw + 8 * kb + 32 * g0;
-#pragma unroll
-        for (int j = 0; j < kGpw; ++j)
-            if (j < cnt) {
-                bw[j] = load_nt8(wrow + 32 * j);
-                sv[j] = scales[(int64_t)(g0 + j) * N + n];
-                zv[j] = zeros[(int64_t)(g0 + j) * N + n];
-            }
+            for (int c = 0; c < 4; ++c)
+                xr[m][c] = mb + m < M ? *reinterpret_cast<const u32x4 *>(x + (int64_t)(mb + m) * ldx + kc + 8 * c)
+                                      : u32x4{0u, 0u, 0u, 0u};
     };
-    if (tile < ntiles)
-        load_tile(tile);
+    load_x(0);
+    const u32x4 sv = *reinterpret_cast<const u32x4 *>(scales + g * N + n0);
+    const u32x4 zv = *reinterpret_cast<const u32x4 *>(zeros + g * N + n0);
+    u32x4 wv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        wv[r] = load_nt16(packed + (int64_t)(n0 + r) * ldw + kc / 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads in this order
 
-    // Activation operands (two 32-wide halves per group) and the group sums X.
-    v8bf a[kGpw][2];
-    v4f xs[kGpw];
-    const v8bf ones = as_v8bf(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+    uint32_t part[M][R];
 #pragma unroll
-    for (int j = 0; j < kGpw; ++j) {
-        const bool live = j < cnt && col < M;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint4 w = make_uint4(raw[j][s][0], raw[j][s][1], raw[j][s][2], raw[j][s][3]);
-            a[j][s] = live ? x_perm8(w) : as_v8bf(0u, 0u, 0u, 0u);
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int mb = pass * MC;
+        if (pass > 0) {
+            __builtin_amdgcn_sched_barrier(0);  // passes run one after another
+            load_x(mb);
         }
-        v4f z{0.f, 0.f, 0.f, 0.f};
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][0], ones, z, 0, 0, 0);
-        xs[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][1], ones, z, 0, 0, 0);
+        // 2. Activation pairs in the nibble order, and the lane's activation sums.
+        uint32_t xp[MC][16];
+        float xs[MC];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 w = xr[m][i];  // bf16 of columns kc + 8 i .. + 7
+                xp[m][4 * i + 0] = active ? perm(w[1], w[0], 0x05040100u) : 0u;  // (x0, x2)
+                xp[m][4 * i + 1] = active ? perm(w[3], w[2], 0x05040100u) : 0u;  // (x4, x6)
+                xp[m][4 * i + 2] = active ? perm(w[1], w[0], 0x07060302u) : 0u;  // (x1, x3)
+                xp[m][4 * i + 3] = active ? perm(w[3], w[2], 0x07060302u) : 0u;  // (x5, x7)
+            }
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                t = dot2(xp[m][j], 0x3F803F80u, t);  // bf16 (1, 1)
+            xs[m] = t;
+        }
+
+        // 3. Per weight row: P over the lane's 32 columns, then the group terms.
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float acc[MC];
+#pragma unroll
+            for (int m = 0; m < MC; ++m)
+                acc[m] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = wv[r][i] & 0x0f0f0f0fu;         // q of k = 0, 2, 4, 6
+                const uint32_t hi = (wv[r][i] >> 4) & 0x0f0f0f0fu;  // q of k = 1, 3, 5, 7
+                const uint32_t w0 = perm(0x43434343u, lo, 0x04010400u);  // bf16(128+q) of (k0, k2)
+                const uint32_t w1 = perm(0x43434343u, lo, 0x04030402u);  // (k4, k6)
+                const uint32_t w2 = perm(0x43434343u, hi, 0x04010400u);  // (k1, k3)
+                const uint32_t w3 = perm(0x43434343u, hi, 0x04030402u);  // (k5, k7)
+#pragma unroll
+                for (int m = 0; m < MC; ++m) {
+                    acc[m] = dot2(w0, xp[m][4 * i + 0], acc[m]);
+                    acc[m] = dot2(w1, xp[m][4 * i + 1], acc[m]);
+                    acc[m] = dot2(w2, xp[m][4 * i + 2], acc[m]);
+                    acc[m] = dot2(w3, xp[m][4 * i + 3], acc[m]);
+                }
+            }
+            const uint32_t sw = sv[r / 2], zw = zv[r / 2];
+            const float s = __uint_as_float((r & 1) ? (sw & 0xffff0000u) : (sw << 16));
+            const float z = __uint_as_float((r & 1) ? (zw & 0xffff0000u) : (zw << 16));
+            const float zc = __builtin_fmaf(-136.f, s, z);
+#pragma unroll
+            for (int m = 0; m < MC; ++m)
+                if (mb + m < M)
+                    part[mb + m][r] = __float_as_uint(__builtin_fmaf(s, acc[m], zc * xs[m]));
+            if constexpr (M > 1)
+                __builtin_amdgcn_sched_barrier(0);  // one row's decode live at a time
+        }
     }
 
-    for (; tile < ntiles; tile += gridDim.x) {
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
+    // 4. Sum over the lanes of the wave, then over the waves (fixed order).
+    const int row = lane >> 3;
+    const bool owner = (lane & 7) == 0;
 #pragma unroll
-        for (int j = 0; j < kGpw; ++j)
-            if (j < cnt) {
-                v4f p{0.f, 0.f, 0.f, 0.f};
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][0], w_bf16_plus128(bw[j][0]), p, 0, 0, 0);
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][1], w_bf16_plus128(bw[j][1]), p, 0, 0, 0);
-                const float s = bf16_to_f32(sv[j]);
-                const float c = __builtin_fmaf(-136.f, s, bf16_to_f32(zv[j]));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    y[i] = __builtin_fmaf(s, p[i], __builtin_fmaf(c, xs[j][i], y[i]));
-            }
-        if (tile + (int)gridDim.x < ntiles)
-            load_tile(tile + gridDim.x);
-        *reinterpret_cast<float4 *>(red + (wave * kWave + lane) * 4) = make_float4(y[0], y[1], y[2], y[3]);
-        __syncthreads();
-        for (int e = threadIdx.x; e < kWave * 4; e += blockDim.x) {
-            const int l = e / 4, i = e % 4;
-            const int m = 4 * (l / 16) + i;
-            const int nn = tile * 16 + l % 16;
-            if (m < M) {
-                float v = 0.f;
-                for (int w = 0; w < ks; ++w)
-                    v += red[w * kWave * 4 + e];
-                if (bias)
-                    v += bf16_to_f32(bias[nn]);
-                out[(int64_t)m * ldo + nn] = f32_to_bf16(v);
-            }
-        }
-        __syncthreads();
+    for (int m = 0; m < M; ++m) {
+        const uint32_t t = transposed_row_sum<R, true>(part[m], lane);
+        if (owner)
+            s_red[wave][row][m] = t;
     }
+    __syncthreads();
+    if (threadIdx.x < R * M) {
+        const int r = threadIdx.x / M, m = threadIdx.x % M;
+        const int n = n0 + r;
+        float y = __uint_as_float(s_red[0][r][m]);
+        for (int w = 1; w < nw; ++w)
+            y += __uint_as_float(s_red[w][r][m]);
+        if (bias)
+            y += bf16_to_f32(bias[n]);
+        out[(int64_t)m * ldo + n] = f32_to_bf16(y);
+    }
+}
+
+template <int M>
+hipError_t launch_m(const uint16_t *x, int64_t ldx, int K, const uint8_t *packed, int64_t ldw,
+                    const uint16_t *scales, const uint16_t *zeros, int N, const uint16_t *bias,
+                    uint16_t *out, int64_t ldo, hipStream_t s)
+{
+    const dim3 grid((unsigned)(N / kRows));
+    const dim3 block((unsigned)(kWave * ((K + 2047) / 2048)));
+    hipLaunchKernelGGL((w4a16_gemv_kernel<M>), grid, block, 0, s, x, ldx, K, packed, ldw, scales, zeros,
+                       N, bias, out, ldo);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-bool w4a16_supports(int64_t K) { return (K / 64 + kGpw - 1) / kGpw <= kMaxWaves; }
+bool w4a16_supports(int64_t K) { return K >= 64 && K <= 2048 * kMaxWaves; }
 
 int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed,
                       int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int N,
@@ -152,16 +192,22 @@ int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_
 {
     if (M <= 0)
         return 0;
-    const int ng = K / 64;
-    int ks = (ng + kGpw - 1) / kGpw;
-    if (ks < 4)
-        ks = ng < 4 ? ng : 4;
-    const int gpw = (ng + ks - 1) / ks;
+    if (!w4a16_supports(K) || K % 64 != 0 || N % kRows != 0)
+        return (int)hipErrorInvalidValue;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const size_t smem = (size_t)ks * kWave * 4 * sizeof(float);
-    hipLaunchKernelGGL(w4a16_gemv_kernel, dim3(N / 16), dim3(ks * kWave), smem, s, x, ldx, M, K,
-                       packed, ldw, scales, zeros, N, bias, out, ldo, gpw);
-    return (int)hipGetLastError();
+    hipError_t e;
+    switch (M) {
+    case 1: e = launch_m<1>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 2: e = launch_m<2>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 3: e = launch_m<3>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 4: e = launch_m<4>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 5: e = launch_m<5>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 6: e = launch_m<6>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 7: e = launch_m<7>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    case 8: e = launch_m<8>(x, ldx, K, packed, ldw, scales, zeros, N, bias, out, ldo, s); break;
+    default: e = hipErrorInvalidValue; break;
+    }
+    return (int)e;
 }
 
 }  // namespace ck

@@ -138,7 +138,9 @@ def test_awq_rejects():
     assert f(P, 9, 256, 256, P3, 128, P4, P2, 64, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
     assert f(P, 1, 256, 256, P3, 128, P4, None, 64, 64, None, P5, 64, None) == ck.CK_ERR_INVALID_ARG
     assert f(P, 1, 256, 256, P3, 128, P4, P2, 32, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
-    assert f(P, 1, 8192, 8192, P3, 4096, P4, P2, 64, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
+    assert f(P, 1, 32768, 32768, P3, 16384, P4, P2, 64, 64, None, P5, 64, None) == ck.CK_ERR_UNSUPPORTED
+    assert f(P, 1, 256, 256, P3, 128, P4 + 2, P2, 64, 64, None, P5, 64, None) == ck.CK_ERR_INVALID_ARG
+    assert f(P, 1, 256, 256, P3, 128, P4, P2 + 8, 64, 64, None, P5, 64, None) == ck.CK_ERR_INVALID_ARG
 
 
 def test_test_hooks_reject():

@@ -263,7 +263,8 @@ def test_errors_raise():
 # ----------------------------------------------------------------- AWQ W4A16
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 3072, 1024), (3, 1024, 272), (8, 4096, 64), (1, 64, 16)])
+@pytest.mark.parametrize("M,K,N", [(1, 3072, 1024), (3, 1024, 272), (8, 4096, 64), (1, 64, 16),
+                                   (2, 10240, 48), (5, 3072, 32), (7, 16384, 16), (4, 2112, 80)])
 def test_awq_gemv_matches_oracle(M, K, N):
     d = workloads.awq_inputs(M, K, N, seed=K + N, with_bias=(M == 3))
     out = ck.w4a16_gemv(bf16_dev(d["x"]), u8_dev(d["packed"]), bf16_dev(d["scales"]), bf16_dev(d["zeros"]),
