@@ -17,12 +17,19 @@
 // the nibble decode produces on B is matched by permuting A once (act_perm16).
 //
 // Work split:
-//   * a workgroup has KS waves; wave w owns a contiguous range of at most GPW
-//     K-groups and keeps the activation operands of that range in VGPRs for
-//     the whole kernel (loaded and permuted once);
-//   * the workgroup walks 16-column tiles of the output; for each tile every
-//     wave issues all its weight loads (8 bytes per lane per group, i.e. 32
-//     contiguous bytes per weight row per group) before the first MFMA;
+//   * a workgroup computes 16 output columns (weight rows n0 .. n0 + 15) for
+//     all M activation rows; it has KS waves, and wave w owns a contiguous
+//     range of GPW K-groups;
+//   * each wave first loads the activation operands of its groups into VGPRs
+//     (permuted once), then streams its slice of the 16 weight rows
+//     (GPW * 32 bytes per row) into its own LDS region with
+//     global_load_lds_dwordx4: every 1 KiB instruction covers whole 16-byte
+//     chunks of at most 8 rows, at least 128 contiguous bytes of each, which
+//     HBM serves at full rate (8-byte fragment loads straight from global
+//     memory would touch 16 rows x 32 bytes per instruction);
+//   * chunk slots inside an LDS row are XOR-swizzled by row, so the 8-byte
+//     fragment reads of 16 rows hit 16 different bank groups; a wave reads
+//     only its own region, so its own vmcnt wait is the only synchronisation;
 //   * per-wave partial results are summed across waves through LDS in a fixed
 //     order (deterministic), then scaled, biased and stored as bf16.
 #include "ck_device.h"
@@ -33,29 +40,44 @@ namespace {
 
 constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// s_waitcnt vmcnt(0), other counters untouched.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int MT, int GPW, bool PER_GROUP, bool OUT_I32>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int M,
     int K, const uint8_t *__restrict__ packed, int64_t ldw, const uint16_t *__restrict__ w_scales,
     int N, const uint16_t *__restrict__ bias, float x_scale, uint16_t *__restrict__ out,
-    int64_t ldo, int32_t *__restrict__ acc_out, int64_t lda, int gpw)
+    int64_t ldo, int32_t *__restrict__ acc_out, int64_t lda)
 {
-    extern __shared__ int red_smem[];  // [KS][MT][64][4] partials
+    constexpr int P = 32 * GPW;        // bytes of one weight row in a wave's slice
+    constexpr int CPR = P / 16;        // 16-byte chunks per slice row
+    constexpr int SLICE = 16 * P;      // bytes of a wave's slice (16 rows)
+    constexpr int NLD = SLICE / 1024;  // DMA instructions per wave
+    // Slot swizzle: chunk c of row r sits in slot c ^ (r >> SH), which spreads
+    // a column of 16 rows over the 16 bank groups of 16 bytes.
+    constexpr int SH = CPR >= 16 ? 0 : CPR == 8 ? 1 : 2;
+    static_assert(CPR >= 4 && NLD * 1024 == SLICE, "slice shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
+    lds_u8 *smem = (lds_u8 *)smem_generic;
+
     const int ks = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int ng = K / 64;
-    const int g0 = wave * gpw;
-    const int cnt = max(0, min(gpw, ng - g0));
+    const int g0 = wave * GPW;
+    const int cnt = max(0, min(GPW, ng - g0));
     const int col = lane % 16;
     const int kb = lane / 16;
+    const int n0 = xcd_block(blockIdx.x, gridDim.x) * 16;
+    lds_u8 *slice = smem + wave * SLICE;
+    int *red_smem = reinterpret_cast<int *>(smem_generic + ks * SLICE);  // [KS][MT][64][4]
 
-    // Issue the activation loads of this wave's groups and the first tile's
-    // weight loads before any of them is used, so that all of them are in
-    // flight together.  Addresses are clamped into the matrices; the values
-    // of out-of-range rows / groups are replaced by zero afterwards.
-    const int ntiles = N / 16;
-    int tile = blockIdx.x;
+    // 1. Loads, in this order: the activations of this wave's groups (clamped
+    //    addresses; out-of-range values are replaced by zero below), the
+    //    weight scales, then the weight slice into LDS.
     u32x4 raw[GPW][MT];
 #pragma unroll
     for (int j = 0; j < GPW; ++j)
@@ -65,23 +87,23 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
             const int g = min(g0 + j, ng - 1);
             raw[j][mt] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + 64 * g + 16 * kb);
         }
-    u32x2 bw[GPW];
     uint16_t sw[GPW];
-    auto load_tile = [&](int t) {
-        const int n = t * 16 + col;
-        const uint8_t *wrow = packed + (int64_t)n * ldw + 8 * kb + 32 * g0;
+    if constexpr (PER_GROUP) {
 #pragma unroll
         for (int j = 0; j < GPW; ++j)
-            if (j < cnt) {
-                bw[j] = load_nt8(wrow + 32 * j);
-                if constexpr (PER_GROUP)
-                    sw[j] = w_scales[(int64_t)(g0 + j) * N + n];
-            }
-    };
-    if (tile < ntiles)
-        load_tile(tile);
+            sw[j] = w_scales[(int64_t)min(g0 + j, ng - 1) * N + n0 + col];
+    }
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+        const int s = 64 * j + lane;  // slot in the slice
+        const int r = s / CPR;
+        const int c = (s % CPR) ^ (r >> SH);  // chunk of row r stored in that slot
+        if (c < 2 * cnt)
+            __builtin_amdgcn_global_load_lds(packed + (int64_t)(n0 + r) * ldw + 32 * g0 + 16 * c,
+                                             slice + 1024 * j, 16, 0, 0);
+    }
 
-    // Activation operands, permuted to the decode order.
+    // 2. Activation operands, permuted to the decode order (overlaps the DMA).
     v4i a[GPW][MT];
 #pragma unroll
     for (int j = 0; j < GPW; ++j)
@@ -92,84 +114,83 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
             a[j][mt] = live ? p : v4i{0, 0, 0, 0};
         }
 
-    for (; tile < ntiles; tile += gridDim.x) {
+    // 3. This wave's slice has landed once its own loads have retired.
+    wait_vmcnt0();
 
-        float y[MT][4];
-        v4i acc[MT];
+    float y[MT][4];
+    v4i acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = v4i{0, 0, 0, 0};
+    for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                y[mt][i] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i)
+            y[mt][i] = 0.f;
+    }
 #pragma unroll
-        for (int j = 0; j < GPW; ++j)
-            if (j < cnt) {
-                const v4i b = w4_operand_x16(bw[j][0], bw[j][1]);
-                if constexpr (PER_GROUP) {
-                    const float s = bf16_to_f32(sw[j]);
+    for (int j = 0; j < GPW; ++j)
+        if (j < cnt) {
+            // Lane (col, kb) holds k = 64 g + 16 kb .. + 15: bytes 32 j + 8 kb of row col.
+            const int c = 2 * j + (kb >> 1);
+            const u32x2 wq = *(const __attribute__((address_space(3))) u32x2 *)(
+                slice + col * P + 16 * (c ^ (col >> SH)) + 8 * (kb & 1));
+            const v4i b = w4_operand_x16(wq[0], wq[1]);
+            if constexpr (PER_GROUP) {
+                const float sc = bf16_to_f32(sw[j]);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b,
-                                                                           v4i{0, 0, 0, 0}, 0, 0, 0);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            y[mt][i] = __builtin_fmaf(s, (float)d[i], y[mt][i]);
-                    }
-                } else {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, acc[mt], 0, 0, 0);
+                    for (int i = 0; i < 4; ++i)
+                        y[mt][i] = __builtin_fmaf(sc, (float)d[i], y[mt][i]);
                 }
-            }
-
-        if (tile + (int)gridDim.x < ntiles)
-            load_tile(tile + gridDim.x);  // next tile's weights fly during the reduction
-
-        // Cross-wave reduction: red[w][mt][lane][i].
+            } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            int *dst = red_smem + ((wave * MT + mt) * kWave + lane) * 4;
-            if constexpr (PER_GROUP)
-                *reinterpret_cast<float4 *>(dst) = make_float4(y[mt][0], y[mt][1], y[mt][2], y[mt][3]);
-            else
-                *reinterpret_cast<int4 *>(dst) = make_int4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, acc[mt], 0, 0, 0);
+            }
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < MT * kWave * 4; e += blockDim.x) {
-            const int mt = e / (kWave * 4);
-            const int l = (e / 4) % kWave;
-            const int i = e % 4;
-            const int m = mt * 16 + 4 * (l / 16) + i;
-            const int nn = tile * 16 + l % 16;
-            if (m < M) {
-                if constexpr (OUT_I32) {
+
+    // 4. Cross-wave reduction: red[w][mt][lane][i], summed in wave order.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        int *dst = red_smem + ((wave * MT + mt) * kWave + lane) * 4;
+        if constexpr (PER_GROUP)
+            *reinterpret_cast<float4 *>(dst) = make_float4(y[mt][0], y[mt][1], y[mt][2], y[mt][3]);
+        else
+            *reinterpret_cast<int4 *>(dst) = make_int4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < MT * kWave * 4; e += blockDim.x) {
+        const int mt = e / (kWave * 4);
+        const int l = (e / 4) % kWave;
+        const int i = e % 4;
+        const int m = mt * 16 + 4 * (l / 16) + i;
+        const int nn = n0 + l % 16;
+        if (m < M) {
+            if constexpr (OUT_I32) {
+                int s = 0;
+                for (int w = 0; w < ks; ++w)
+                    s += red_smem[w * MT * kWave * 4 + e];
+                acc_out[(int64_t)m * lda + nn] = s >> 4;  // exact: s = 16 * sum
+            } else {
+                float yv;
+                if constexpr (PER_GROUP) {
+                    float s = 0.f;
+                    for (int w = 0; w < ks; ++w)
+                        s += __int_as_float(red_smem[w * MT * kWave * 4 + e]);
+                    yv = s * 0.0625f;
+                } else {
                     int s = 0;
                     for (int w = 0; w < ks; ++w)
                         s += red_smem[w * MT * kWave * 4 + e];
-                    acc_out[(int64_t)m * lda + nn] = s >> 4;  // exact: s = 16 * sum
-                } else {
-                    float yv;
-                    if constexpr (PER_GROUP) {
-                        float s = 0.f;
-                        for (int w = 0; w < ks; ++w)
-                            s += __int_as_float(red_smem[w * MT * kWave * 4 + e]);
-                        yv = s * 0.0625f;
-                    } else {
-                        int s = 0;
-                        for (int w = 0; w < ks; ++w)
-                            s += red_smem[w * MT * kWave * 4 + e];
-                        yv = bf16_to_f32(w_scales[nn]) * ((float)s * 0.0625f);
-                    }
-                    yv *= row_scales[m] * x_scale;
-                    if (bias)
-                        yv += bf16_to_f32(bias[nn]);
-                    out[(int64_t)m * ldo + nn] = f32_to_bf16(yv);
+                    yv = bf16_to_f32(w_scales[nn]) * ((float)s * 0.0625f);
                 }
+                yv *= row_scales[m] * x_scale;
+                if (bias)
+                    yv += bf16_to_f32(bias[nn]);
+                out[(int64_t)m * ldo + nn] = f32_to_bf16(yv);
             }
         }
-        __syncthreads();
     }
 }
 
@@ -177,22 +198,18 @@ struct SkinnyShape {
     int mt, ks, gpw;
 };
 
-// MT = ceil(M / 16) m-tiles; GPW groups per wave (capped so that the register
-// copy of the activations stays <= 64 VGPRs per m-tile); KS waves.
+// MT = ceil(M / 16) m-tiles; GPW groups per wave, chosen so that the
+// register copy of the activations (GPW * MT * 4 VGPRs) stays at most 128;
+// KS = ceil(K / 64 / GPW) <= 8 waves.
 bool skinny_shape(int64_t M, int64_t K, SkinnyShape &s)
 {
     if (M < 1 || M > 64)
         return false;
     const int ng = (int)(K / 64);
     s.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    const int gmax = s.mt == 1 ? 16 : s.mt == 2 ? 8 : 4;
-    s.ks = (ng + gmax - 1) / gmax;
-    if (s.ks < 4)
-        s.ks = ng < 4 ? ng : 4;
-    if (s.ks > kMaxWaves)
-        return false;
-    s.gpw = (ng + s.ks - 1) / s.ks;
-    return true;
+    s.gpw = s.mt == 1 ? 16 : s.mt == 2 ? (ng <= 8 * kMaxWaves ? 8 : 16) : 8;
+    s.ks = (ng + s.gpw - 1) / s.gpw;
+    return s.ks >= 1 && s.ks <= kMaxWaves;
 }
 
 template <int MT, int GPW, bool PG, bool I32>
@@ -202,11 +219,16 @@ hipError_t launch_t(const SkinnyShape &sh, const int8_t *codes, int64_t ldq, con
                     int64_t lda, hipStream_t s)
 {
     const int ntiles = N / 16;
-    const size_t smem = (size_t)sh.ks * MT * kWave * 4 * sizeof(int);
+    const size_t smem = (size_t)sh.ks * (16 * 32 * GPW + MT * kWave * 4 * sizeof(int));
+    auto kern = w4_skinny_kernel<MT, GPW, PG, I32>;
+    constexpr size_t smem_max = (size_t)kMaxWaves * (16 * 32 * GPW + MT * kWave * 4 * sizeof(int));
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_max);
+    if (attr != hipSuccess)
+        return attr;
     const dim3 grid((unsigned)ntiles);
-    hipLaunchKernelGGL((w4_skinny_kernel<MT, GPW, PG, I32>), grid, dim3(sh.ks * kWave), smem, s,
-                       codes, ldq, rs, M, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda,
-                       sh.gpw);
+    hipLaunchKernelGGL(kern, grid, dim3(sh.ks * kWave), smem, s,
+                       codes, ldq, rs, M, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda);
     return hipGetLastError();
 }
 
@@ -245,18 +267,25 @@ int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool i32 = acc_out != nullptr;
     hipError_t e;
-    switch (sh.mt) {
-    case 1:
+    switch (sh.mt * 100 + sh.gpw) {
+    case 116:
         e = launch_mt<1, 16>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
                              w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
         break;
-    case 2:
+    case 208:
         e = launch_mt<2, 8>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
                             w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
         break;
-    default:
-        e = launch_mt<4, 4>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
+    case 216:
+        e = launch_mt<2, 16>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
+                             w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
+        break;
+    case 408:
+        e = launch_mt<4, 8>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
                             w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
+        break;
+    default:
+        e = hipErrorInvalidValue;
         break;
     }
     return (int)e;

@@ -93,6 +93,10 @@ def _rand_codes(M, K, qmax, seed):
 @pytest.mark.parametrize("M,K,N", [
     (1, 3840, 96), (5, 384, 272), (8, 3840, 160), (16, 1024, 64), (33, 3840, 48),
     (64, 4096, 32), (65, 384, 528), (300, 1152, 272), (513, 128, 16),
+    # few-row kernel: every m-tile count, a partial last wave, a single wave
+    # with masked weight-slice lanes, and the widest (8-wave) slice set
+    (40, 2048, 48), (20, 3840, 64), (12, 8192, 32), (9, 192, 16), (17, 4096, 16),
+    (20, 6144, 32), (50, 1024, 64), (64, 3840, 16),
 ])
 @pytest.mark.parametrize("qmax", [127, 7])
 def test_accumulators_bit_exact(M, K, N, qmax):
