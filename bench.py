@@ -253,6 +253,7 @@ def main():
     # ------------------------------------------------------------ extras
     if not args.no_extras:
         result["also"] = extras(ck, workloads, torch, dev, bf16, u8, stream)
+        result["also"]["same_bytes_plain_copy"] = same_bytes_copy(torch, dev, stream, alg_bytes, args.copies)
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
@@ -302,6 +303,18 @@ def _time(fn, stream, iters, warmup=3):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / iters * 1e3
+
+
+def same_bytes_copy(torch, dev, stream, nbytes, copies):
+    """A plain elementwise copy (torch int32 negation: one read and one write per
+    element) moving the same HBM bytes as one headline step, from cold sources,
+    timed like the headline: what one launch of this size can reach."""
+    n = nbytes // 8
+    srcs = [torch.ones(n, dtype=torch.int32, device=dev) for _ in range(copies)]
+    dst = torch.empty(n, dtype=torch.int32, device=dev)
+    us = _time(lambda i: torch.neg(srcs[i % copies], out=dst), stream, 100)
+    return {"bytes": n * 8, "us": round(us, 3), "GBps": round(n * 8 / us / 1e3, 1),
+            "frac_hbm": round(n * 8 / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def extras(ck, workloads, torch, dev, bf16, u8, stream):

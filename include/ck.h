@@ -50,8 +50,9 @@
  *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales.
  *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
  *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
- *    ldw % 16 == 0; outputs 16-byte aligned with 16-byte aligned rows
- *    (bf16: ldo % 8 == 0; int32 test outputs: lda % 4 == 0).
+ *    ldw % 16 == 0; AWQ scales and zero points 16-byte aligned; outputs
+ *    16-byte aligned with 16-byte aligned rows (bf16: ldo % 8 == 0; int32
+ *    test outputs: lda % 4 == 0).
  */
 #ifndef CK_H
 #define CK_H
@@ -131,9 +132,10 @@ int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int6
 
 /*
  * ck_w4_gemv  [GEMV]
- * Decode form of ck_w4_gemm_q for 1 <= M <= 8 and K <= 8192
- * (CK_ERR_UNSUPPORTED otherwise): the same arithmetic, run by the kernel that
- * streams the packed weights once.
+ * Decode form of ck_w4_gemm_q for 1 <= M <= 8 and K <= 16384
+ * (CK_ERR_UNSUPPORTED otherwise): the same arithmetic, run by a kernel that
+ * streams the packed weights once (VALU dot products for M <= 5, MFMA for
+ * 6 <= M <= 8 when K fits its range).
  */
 int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
                int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
