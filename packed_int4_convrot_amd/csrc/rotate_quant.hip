@@ -13,7 +13,8 @@
 //     wave (groups never straddle a wave or a chunk round);
 //   * the first three butterfly stages (strides 1, 2, 4) run inside the
 //     thread's 8 registers, the remaining log2(G/8) stages across lanes
-//     (DPP quad permutes for lane distance 1 and 2, ds_swizzle for 4..16);
+//     (DPP quad permutes for lane distance 1 and 2, ds_swizzle for 4..16, and
+//     ds_swizzle for every distance at G = 256, where the VALU is the limit);
 //   * the fp32 values stay in registers until the row absmax is known
 //     (wave reduction, then LDS across waves); then every thread quantises and
 //     stores its own 8 codes with one 8-byte store.
@@ -27,12 +28,17 @@
 namespace ck {
 namespace {
 
-// Value held by the lane whose index differs in bit log2(MASK).
-template <int MASK>
+// Value held by the lane whose index differs in bit log2(MASK).  DPP moves
+// are VALU instructions, ds_swizzle runs on the LDS pipe; SWZ selects the
+// swizzle for every distance, which moves VALU work off the butterflies when
+// they are the bottleneck (G = 256).
+template <int MASK, bool SWZ = false>
 __device__ __forceinline__ float lane_xor(float v)
 {
     int i = __float_as_int(v);
-    if constexpr (MASK == 1)
+    if constexpr (SWZ)
+        i = __builtin_amdgcn_ds_swizzle(i, 0x1F | (MASK << 10));      // bitmask mode: lane ^ MASK
+    else if constexpr (MASK == 1)
         i = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
     else if constexpr (MASK == 2)
         i = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
@@ -43,14 +49,14 @@ __device__ __forceinline__ float lane_xor(float v)
 
 // One cross-lane butterfly stage: the lower lane of each pair keeps u + v,
 // the upper lane v' = u - v (written as fma(v, -1, u), same rounding).
-template <int MASK, int CPT>
+template <int MASK, int CPT, bool SWZ>
 __device__ __forceinline__ void lane_stage(float (&v)[CPT][8], float sgn)
 {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float p = lane_xor<MASK>(v[i][r]);
+            const float p = lane_xor<MASK, SWZ>(v[i][r]);
             v[i][r] = __builtin_fmaf(v[i][r], sgn, p);
         }
 }
@@ -70,11 +76,15 @@ __device__ __forceinline__ void fht(float (&v)[CPT][8], int lane)
                     v[i][r + h] = a - b;
                 }
     }
-    if constexpr (G >= 16) lane_stage<1, CPT>(v, (lane & 1) ? -1.f : 1.f);
-    if constexpr (G >= 32) lane_stage<2, CPT>(v, (lane & 2) ? -1.f : 1.f);
-    if constexpr (G >= 64) lane_stage<4, CPT>(v, (lane & 4) ? -1.f : 1.f);
-    if constexpr (G >= 128) lane_stage<8, CPT>(v, (lane & 8) ? -1.f : 1.f);
-    if constexpr (G >= 256) lane_stage<16, CPT>(v, (lane & 16) ? -1.f : 1.f);
+    // At G = 256 the five cross-lane stages make the kernel VALU-bound
+    // (about 17 VALU instructions per element); exchanging through the LDS
+    // pipe instead of DPP measured 6-8% faster there, and slower at G <= 64.
+    constexpr bool SWZ = G >= 256;
+    if constexpr (G >= 16) lane_stage<1, CPT, SWZ>(v, (lane & 1) ? -1.f : 1.f);
+    if constexpr (G >= 32) lane_stage<2, CPT, SWZ>(v, (lane & 2) ? -1.f : 1.f);
+    if constexpr (G >= 64) lane_stage<4, CPT, SWZ>(v, (lane & 4) ? -1.f : 1.f);
+    if constexpr (G >= 128) lane_stage<8, CPT, SWZ>(v, (lane & 8) ? -1.f : 1.f);
+    if constexpr (G >= 256) lane_stage<16, CPT, SWZ>(v, (lane & 16) ? -1.f : 1.f);
 }
 
 __device__ __forceinline__ float wave_max(float v)
