@@ -42,7 +42,11 @@ constexpr int kStages = 4;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Slot swizzles, chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950 for the
+// fragment read patterns: (r >> 2) & 3 for the 64-byte activation rows and
+// ((n >> 2) ^ (n >> 3)) & 1 for the 32-byte weight rows read without conflicts
+// (e.g. ((r >> 1) ^ (r >> 3)) & 3 gave 2-way conflicts).
+__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_b(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
