@@ -192,8 +192,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                 for (int j = 0; j < WN; ++j) {
                     if constexpr (TRANS)  // D^T[n][m]: lane = row m, registers = columns n
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af, acc[i][j], 0, 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf[j], acc[i][j], 0, 0, 0);
+                    else  // per group: the step's first product starts from zero
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            af, bf[j], s == 0 ? v16i{} : acc[i][j], 0, 0, 0);
                 }
             }
         }
@@ -204,10 +205,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
 #pragma unroll
                 for (int i = 0; i < WM; ++i)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
+                    for (int r = 0; r < 16; ++r)
                         y[i][j][r] = __builtin_fmaf(scf, (float)acc[i][j][r], y[i][j][r]);
-                        acc[i][j][r] = 0;
-                    }
             }
         }
     }
@@ -342,7 +341,7 @@ int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, in
         e = launch_t<2, 4, 4, 2, false, true>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
                                         bias, x_scale, out, ldo, acc_out, lda, s);
     else if (per_group)
-        e = launch_t<2, 2, 2, 2, true, false>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
+        e = launch_t<2, 4, 2, 2, true, false>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
                                         bias, x_scale, out, ldo, acc_out, lda, s);
     else
         e = launch_t<2, 4, 4, 2, false, false>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
