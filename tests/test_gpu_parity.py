@@ -153,7 +153,7 @@ def test_gemv_entry_matches_oracle(per_group):
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("per_group", [True, False])
 @pytest.mark.parametrize("G", [16, 64, 256])
-@pytest.mark.parametrize("M", [1, 2, 3, 40, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 40, 64, 300])
 def test_linear_end_to_end(M, G, per_group, bits):
     K, N = 1536, 144
     inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=15, scale="group" if per_group else "channel",
@@ -173,12 +173,13 @@ def test_linear_end_to_end(M, G, per_group, bits):
         assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M,K", [(1, 3840), (2, 3840), (1, 256), (1, 2304), (1, 8192)])
 @pytest.mark.parametrize("G", [16, 64, 256])
-def test_fused_decode_linear_equals_two_step_path(M, G):
+def test_fused_decode_linear_equals_two_step_path(M, K, G):
     """The one-launch decode linear (rotate-quant inside the GEMV) gives bit-identical
-    outputs to ck_rotate_quant followed by ck_w4_gemv."""
-    K, N = 3840, 1024
+    outputs to ck_rotate_quant followed by ck_w4_gemv: one wave with 8 active lanes,
+    a partial second wave, and four waves."""
+    N = 1024
     for per_group in (True, False):
         inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=8, scale="group" if per_group else "channel",
                                       with_bias=True)
@@ -187,6 +188,21 @@ def test_fused_decode_linear_equals_two_step_path(M, G):
         codes, scales = ck.rotate_quant(xd, G, 8)
         two = ck.gemv(codes, scales, wd, sd, per_group, bias=bd)
         assert torch.equal(fused, two)
+
+
+def test_fused_decode_linear_strided_input_ignores_padding():
+    """Row stride > K: the fused kernel reads only the K columns (the padding is NaN)."""
+    K, N, ld = 3840, 512, 4096
+    inp = workloads.linear_inputs(1, K, N, seed=9, outliers=8, scale="group", with_bias=False)
+    padded = workloads.activations(1, K, seed=9, outliers=8, ld=ld)
+    assert np.array_equal(padded[:, :K], inp["x"])
+    wd, sd = u8_dev(inp["packed"]), bf16_dev(inp["w_scales"])
+    xs = bf16_dev(padded)[:, :K]
+    assert xs.stride(0) == ld
+    out = ck.linear(xs, 64, 8, wd, sd, True)
+    ref = ck.linear(bf16_dev(inp["x"]), 64, 8, wd, sd, True)
+    assert not torch.isnan(out).any()
+    assert torch.equal(out, ref)
 
 
 @pytest.mark.parametrize("M", [1, 8, 300])
