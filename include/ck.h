@@ -47,7 +47,9 @@
  *  - Shape limits (CK_ERR_UNSUPPORTED otherwise): G in {16, 64, 256};
  *    bits in {8, 4}; K % 64 == 0 and 64 <= K <= 32768 (K % G != 0 is
  *    CK_ERR_INVALID_ARG: a row must split into whole groups);
- *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales.
+ *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales;
+ *    M, N <= 2^22 (one launch's grid), and for shapes that run the tiled
+ *    GEMM ceil(M / 128) * ceil(N / 256) < 2^23.
  *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
  *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
  *    ldw % 16 == 0; AWQ scales and zero points 16-byte aligned; outputs

@@ -59,7 +59,12 @@ Range span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t esize)
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 constexpr int64_t kMaxK = 32768;
-constexpr int64_t kMaxRows = 2147483647;
+// A launch covers at most 2^32 - 1 work-items per grid dimension; one
+// workgroup of up to 1024 threads per activation row bounds the rows to 2^22.
+constexpr int64_t kMaxRows = int64_t(1) << 22;
+// The tiled GEMM launches one 512-thread workgroup per 256 x 256 (or
+// 128 x 256) output tile.
+constexpr int64_t kMaxGemmTiles = (int64_t(1) << 32) / 512 - 1;
 
 int check_k(const char *fn, int64_t K)
 {
@@ -128,7 +133,8 @@ int check_weights(const char *fn, const Weights &w, int64_t K, bool need_scales)
     if (w.N <= 0)
         return fail(CK_ERR_INVALID_ARG, "%s: N must be positive (got %lld)", fn, (long long)w.N);
     if (w.N % 16 != 0 || w.N > kMaxRows)
-        return fail(CK_ERR_UNSUPPORTED, "%s: N must be a multiple of 16 (got %lld)", fn, (long long)w.N);
+        return fail(CK_ERR_UNSUPPORTED, "%s: N must be a multiple of 16 and at most %lld (got %lld)", fn,
+                    (long long)kMaxRows, (long long)w.N);
     if (w.ldw < K / 2 || w.ldw % 16 != 0)
         return fail(CK_ERR_INVALID_ARG, "%s: ldw (%lld) must be >= K/2 and a multiple of 16", fn,
                     (long long)w.ldw);
@@ -189,6 +195,9 @@ int run_gemm(const char *fn, const int8_t *codes, int64_t ldq, const float *rs, 
     const bool pg = w.kind == CK_WS_PER_GROUP;
     const bool gemv = ck::w4_gemv_supports(M, K);
     const bool skinny = M <= 64 && ck::w4_skinny_supports(M, K);
+    if (!gemv && !skinny && ((M + 127) / 128) * ((w.N + 255) / 256) > kMaxGemmTiles)
+        return fail(CK_ERR_UNSUPPORTED, "%s: M * N too large for one launch (M=%lld, N=%lld)", fn,
+                    (long long)M, (long long)w.N);
     int e;
     if (gemv && (M <= kGemvMaxRows || !skinny))
         e = ck::launch_w4_gemv(nullptr, 0, 0, 0, codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw,

@@ -107,6 +107,14 @@ def test_gemm_q_rejects(kw, status):
     assert gq(**kw) == status
 
 
+def test_launch_size_limits():
+    # rows beyond one launch's grid, and a tiled GEMM whose tile grid would overflow
+    assert rq(M=(1 << 22) + 1) == ck.CK_ERR_UNSUPPORTED
+    assert gq(M=(1 << 22), N=(1 << 22), ldo=(1 << 22)) == ck.CK_ERR_UNSUPPORTED
+    assert b"too large" in lib.ck_last_error_msg()
+    assert gq(N=(1 << 22) + 16) == ck.CK_ERR_UNSUPPORTED
+
+
 def test_gemv_rejects_large_m():
     assert gq(fn=lib.ck_w4_gemv, M=9) == ck.CK_ERR_UNSUPPORTED
     assert gq(fn=lib.ck_w4_gemv, M=0) == ck.CK_OK
