@@ -115,13 +115,38 @@ def _ld(t):
     return max(t.stride(0), t.shape[1])
 
 
+def _same_device(ref, *named):
+    for name, t in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, ref.device))
+
+
+def _dense(t, name, dtype, shape):
+    """A contiguous tensor of exactly this shape and dtype on the GPU (the kernels index
+    it as a packed array)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be a %s tensor of shape %s" % (name, dtype, tuple(shape)))
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous GPU tensor" % name)
+    return t
+
+
+def _out(t, name, dtype, M, N):
+    """An output matrix of M rows of N elements (row stride may exceed N)."""
+    _matrix(t, name, (dtype,))
+    if tuple(t.shape) != (M, N):
+        raise ValueError("%s has shape %s, expected (%d, %d)" % (name, tuple(t.shape), M, N))
+    return t
+
+
 def _weights(packed, w_scales, per_group, K):
     _matrix(packed, "packed", (torch.uint8, torch.int8))
     if packed.shape[1] != K // 2:
         raise ValueError("packed has %d bytes per row, expected K/2 = %d" % (packed.shape[1], K // 2))
-    if w_scales is not None and w_scales.dtype != torch.bfloat16:
-        raise ValueError("weight scales must be bf16")
-    return packed.shape[0]
+    N = packed.shape[0]
+    if w_scales is not None:
+        _dense(w_scales, "weight scales", torch.bfloat16, (K // 64, N) if per_group else (N,))
+    return N
 
 
 def workspace_bytes(M: int, K: int) -> int:
@@ -136,6 +161,9 @@ def rotate_quant(x, G: int, bits: int, codes=None, row_scales=None):
         codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if row_scales is None:
         row_scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _out(codes, "codes", torch.int8, M, K)
+    _dense(row_scales, "row_scales", torch.float32, (M,))
+    _same_device(x, ("codes", codes), ("row_scales", row_scales))
     _check(lib.ck_rotate_quant(_ptr(x), M, K, _ld(x), G, bits, _ptr(codes), _ld(codes),
                                _ptr(row_scales), _stream(x)))
     return codes, row_scales
@@ -158,6 +186,12 @@ def gemm_q(codes, row_scales, packed, w_scales, per_group: bool, bias=None, out=
     N = _weights(packed, w_scales, per_group, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=codes.device)
+    _dense(row_scales, "row_scales", torch.float32, (M,))
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    _out(out, "out", torch.bfloat16, M, N)
+    _same_device(codes, ("row_scales", row_scales), ("packed", packed), ("w_scales", w_scales),
+                 ("bias", bias), ("out", out))
     fn = lib.ck_w4_gemv if gemv else lib.ck_w4_gemm_q
     _check(fn(_ptr(codes), _ld(codes), _ptr(row_scales), M, K, _ptr(packed), _ld(packed),
               _ptr(w_scales), CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N,
@@ -176,14 +210,21 @@ def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
     _matrix(x, "x", (torch.bfloat16,))
     M, K = x.shape
     N = _weights(packed, w_scales, per_group, K)
+    if bits not in (8, 4):
+        raise ValueError("bits must be 8 or 4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     need = workspace_bytes(M, K)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    _out(out, "out", torch.bfloat16, M, N)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    _same_device(x, ("packed", packed), ("w_scales", w_scales), ("bias", bias), ("out", out),
+                 ("workspace", workspace))
     fn = lib.ck_w4a8_linear if bits == 8 else lib.ck_w4a4_linear
-    if bits not in (8, 4):
-        raise ValueError("bits must be 8 or 4")
     _check(fn(_ptr(x), M, K, _ld(x), G, _ptr(packed), _ld(packed), _ptr(w_scales),
               CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N, _ptr(bias), x_scale,
               _ptr(out), _ld(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -204,8 +245,14 @@ def w4a16_gemv(x, packed, scales, zeros, bias=None, out=None):
     _matrix(x, "x", (torch.bfloat16,))
     M, K = x.shape
     N = _weights(packed, scales, True, K)
+    _dense(zeros, "zeros", torch.bfloat16, (K // 64, N))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    _out(out, "out", torch.bfloat16, M, N)
+    _same_device(x, ("packed", packed), ("scales", scales), ("zeros", zeros), ("bias", bias),
+                 ("out", out))
     _check(lib.ck_w4a16_gemv(_ptr(x), M, K, _ld(x), _ptr(packed), _ld(packed), _ptr(scales),
                              _ptr(zeros), 64, N, _ptr(bias), _ptr(out), _ld(out), _stream(x)))
     return out

@@ -280,6 +280,30 @@ def test_errors_raise():
         ck.rotate_quant(x[:, :320], 256, 8)  # K % G: invalid
 
 
+def test_binding_rejects_mis_sized_tensors():
+    """Outputs and auxiliary operands are checked against M, N and K before any launch."""
+    M, K, N = 4, 512, 64
+    inp = workloads.linear_inputs(M, K, N, seed=3, outliers=0, scale="group", with_bias=True)
+    x, wd, sd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"])
+    codes, rs = ck.rotate_quant(x, 64, 8)
+    with pytest.raises(ValueError):   # output one row short
+        ck.linear(x, 64, 8, wd, sd, True, out=torch.empty((M - 1, N), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):   # row scales of the wrong length
+        ck.gemm_q(codes, rs[:-1], wd, sd, True)
+    with pytest.raises(ValueError):   # per-group scales given as a transposed view
+        ck.gemm_q(codes, rs, wd, sd.t().contiguous().t(), True)
+    with pytest.raises(ValueError):   # per-channel scales of the per-group shape
+        ck.gemm_q(codes, rs, wd, sd, False)
+    with pytest.raises(ValueError):   # bias of the wrong length
+        ck.linear(x, 64, 8, wd, sd, True, bias=bf16_dev(inp["bias"])[:-16])
+    with pytest.raises(ValueError):   # workspace of the wrong dtype
+        ck.linear(x, 64, 8, wd, sd, True, workspace=torch.empty((1 << 16,), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):   # codes output too short for K
+        ck.rotate_quant(x, 64, 8, codes=torch.empty((M, K - 64), dtype=torch.int8, device=DEV))
+    with pytest.raises(ValueError):   # AWQ zero points with one group missing
+        ck.w4a16_gemv(x, wd, sd, sd[:-1].contiguous())
+
+
 # ----------------------------------------------------------------- AWQ W4A16
 
 
