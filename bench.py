@@ -254,6 +254,7 @@ def main():
     if not args.no_extras:
         result["also"] = extras(ck, workloads, torch, dev, bf16, u8, stream)
         result["also"]["same_bytes_plain_copy"] = same_bytes_copy(torch, dev, stream, alg_bytes, args.copies)
+        result["also"]["launch_floor"] = launch_floor(torch, dev, stream)
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
@@ -315,6 +316,15 @@ def same_bytes_copy(torch, dev, stream, nbytes, copies):
     us = _time(lambda i: torch.neg(srcs[i % copies], out=dst), stream, 100)
     return {"bytes": n * 8, "us": round(us, 3), "GBps": round(n * 8 / us / 1e3, 1),
             "frac_hbm": round(n * 8 / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def launch_floor(torch, dev, stream):
+    """Per-launch cost of a trivial kernel (256 elements), timed like the headline:
+    the floor under every small-M figure."""
+    a = torch.ones(256, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    return {"us": round(_time(lambda i: torch.neg(a, out=b), stream, 100), 3),
+            "kernel": "torch elementwise negation of 256 int32"}
 
 
 def extras(ck, workloads, torch, dev, bf16, u8, stream):
