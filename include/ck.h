@@ -169,7 +169,11 @@ int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
 
 /*
  * ck_w4a4_linear  [W4A4] [SD]
- * As ck_w4a8_linear with int4 activations (qmax 7, symmetric).
+ * As ck_w4a8_linear with int4 activations (qmax 7, symmetric).  When the
+ * tiled GEMM serves M (more rows than the few-row kernels take), the codes are
+ * held in the workspace two per byte (4-bit two's complement, column 2j in
+ * the low nibble), as ck_test_rotate_quant4_packed writes them; the result is
+ * the same as with one code per byte.
  */
 int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
@@ -209,6 +213,22 @@ int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int
 int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,
                      const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,
                      int64_t lda, void *stream);
+
+/* The W4A4 codes of ck_rotate_quant(bits = 4) packed two per byte:
+ * codes4 uint8 [M, ldq], ldq >= K/2 bytes and a multiple of 16, 16-byte
+ * aligned; byte j of a row holds column 2j in bits 0..3 and column 2j + 1 in
+ * bits 4..7, each code in [-7, 7] as 4-bit two's complement.  row_scales as
+ * in ck_rotate_quant.  The workspace layout of ck_w4a4_linear's tiled path. */
+int ck_test_rotate_quant4_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                 int32_t G, uint8_t *codes4, int64_t ldq, float *row_scales,
+                                 void *stream);
+
+/* The integer accumulators of the tiled GEMM on packed W4A4 codes (codes4 as
+ * written by ck_test_rotate_quant4_packed), for any M >= 1:
+ * acc[m,n] = sum_k code[m,k] * (q[n,k] - 8), acc int32 [M, lda]. */
+int ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
+                        const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,
+                        int64_t lda, void *stream);
 
 #ifdef __cplusplus
 }

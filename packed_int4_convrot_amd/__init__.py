@@ -45,6 +45,8 @@ SIGNATURES = {
                       ctypes.c_int),
     "ck_test_rotate_f32": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p], ctypes.c_int),
     "ck_test_gemm_i32": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "ck_test_rotate_quant4_packed": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _p], ctypes.c_int),
+    "ck_test_gemm_i32_a4": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
 
 
@@ -256,6 +258,32 @@ def w4a16_gemv(x, packed, scales, zeros, bias=None, out=None):
     _check(lib.ck_w4a16_gemv(_ptr(x), M, K, _ld(x), _ptr(packed), _ld(packed), _ptr(scales),
                              _ptr(zeros), 64, N, _ptr(bias), _ptr(out), _ld(out), _stream(x)))
     return out
+
+
+def rotate_quant4_packed(x, G: int):
+    """W4A4 codes packed two per byte, uint8 [M, K/2] (column 2j in the low
+    nibble, 4-bit two's complement), and fp32 row scales [M]."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    codes4 = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    row_scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib.ck_test_rotate_quant4_packed(_ptr(x), M, K, _ld(x), G, _ptr(codes4), _ld(codes4),
+                                            _ptr(row_scales), _stream(x)))
+    return codes4, row_scales
+
+
+def accumulators_i32_a4(codes4, K: int, packed):
+    """int32 [M, N] accumulators of the tiled GEMM on packed W4A4 codes uint8 [M, K/2]."""
+    _matrix(codes4, "codes4", (torch.uint8,))
+    M = codes4.shape[0]
+    if codes4.shape[1] != K // 2:
+        raise ValueError("codes4 must have K/2 = %d columns (got %d)" % (K // 2, codes4.shape[1]))
+    N = _weights(packed, None, False, K)
+    acc = torch.empty((M, N), dtype=torch.int32, device=codes4.device)
+    _same_device(codes4, ("packed", packed))
+    _check(lib.ck_test_gemm_i32_a4(_ptr(codes4), _ld(codes4), M, K, _ptr(packed), _ld(packed), N,
+                                   _ptr(acc), _ld(acc), _stream(codes4)))
+    return acc
 
 
 def accumulators_i32(codes, packed):

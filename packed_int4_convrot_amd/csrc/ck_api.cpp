@@ -185,29 +185,50 @@ constexpr size_t kWsAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Dispatch of the integer matmul + epilogue by M.
-int run_gemm(const char *fn, const int8_t *codes, int64_t ldq, const float *rs, int64_t M, int64_t K,
-             const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
-             int32_t *acc, int64_t lda, void *stream)
+enum class GemmPath { kGemv, kSkinny, kTiled };
+
+// Kernel choice for M rows of pre-quantised codes.  The VALU GEMV's work grows
+// with M while the MFMA few-row kernel's does not; measured on MI355X the
+// few-row kernel is faster from 6 rows on.
+GemmPath pick_path(int64_t M, int64_t K)
 {
-    // The VALU GEMV's work grows with M while the MFMA few-row kernel's does
-    // not; measured on MI355X the few-row kernel is faster from 6 rows on.
     constexpr int64_t kGemvMaxRows = 5;
-    const bool pg = w.kind == CK_WS_PER_GROUP;
     const bool gemv = ck::w4_gemv_supports(M, K);
     const bool skinny = M <= 64 && ck::w4_skinny_supports(M, K);
-    if (!gemv && !skinny && ((M + 127) / 128) * ((w.N + 255) / 256) > kMaxGemmTiles)
-        return fail(CK_ERR_UNSUPPORTED, "%s: M * N too large for one launch (M=%lld, N=%lld)", fn,
-                    (long long)M, (long long)w.N);
-    int e;
     if (gemv && (M <= kGemvMaxRows || !skinny))
-        e = ck::launch_w4_gemv(nullptr, 0, 0, 0, codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw,
+        return GemmPath::kGemv;
+    return skinny ? GemmPath::kSkinny : GemmPath::kTiled;
+}
+
+int check_tiles(const char *fn, int64_t M, int64_t N)
+{
+    if (((M + 127) / 128) * ((N + 255) / 256) > kMaxGemmTiles)
+        return fail(CK_ERR_UNSUPPORTED, "%s: M * N too large for one launch (M=%lld, N=%lld)", fn,
+                    (long long)M, (long long)N);
+    return CK_OK;
+}
+
+// a4: the codes are W4A4 codes packed two per byte (ldq in bytes); only the
+// tiled GEMM takes them.
+int run_gemm(const char *fn, const void *codes, int64_t ldq, const float *rs, int64_t M, int64_t K,
+             const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
+             int32_t *acc, int64_t lda, bool a4, void *stream)
+{
+    const bool pg = w.kind == CK_WS_PER_GROUP;
+    const GemmPath path = a4 ? GemmPath::kTiled : pick_path(M, K);
+    const int8_t *c8 = static_cast<const int8_t *>(codes);
+    int e;
+    if (path == GemmPath::kGemv) {
+        e = ck::launch_w4_gemv(nullptr, 0, 0, 0, c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw,
                                w.scales, pg, (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
-    else if (skinny)
-        e = ck::launch_w4_skinny(codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
+    } else if (path == GemmPath::kSkinny) {
+        e = ck::launch_w4_skinny(c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
                                  (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
-    else
-        e = ck::launch_w4_gemm(codes, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
-                               (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
+    } else {
+        CK_TRY(check_tiles(fn, M, w.N));
+        e = ck::launch_w4_gemm(c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
+                               (int)w.N, bias, x_scale, out, ldo, acc, lda, a4, stream);
+    }
     return hip_status(e, fn);
 }
 
@@ -237,7 +258,7 @@ int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, c
         overlap(ro, span(w.packed, w.N, K / 2, w.ldw, 1)) || overlap(ro, scales_span(w, K)) ||
         overlap(ro, span(bias, 1, w.N, w.N, 2)))
         return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
-    return run_gemm(fn, codes, ldq, rs, M, K, w, bias, 1.0f, out, ldo, nullptr, 0, stream);
+    return run_gemm(fn, codes, ldq, rs, M, K, w, bias, 1.0f, out, ldo, nullptr, 0, false, stream);
 }
 
 int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
@@ -280,13 +301,20 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
                                          x_scale, out, ldo, nullptr, 0, stream);
         return hip_status(e, fn);
     }
+    // W4A4 codes bound for the tiled GEMM are stored two per byte, which
+    // halves the codes traffic on both sides of the workspace.
+    const GemmPath path = pick_path(M, K);
+    if (path == GemmPath::kTiled)
+        CK_TRY(check_tiles(fn, M, w.N));
+    const bool a4 = bits == 4 && path == GemmPath::kTiled;
+    const int64_t ldq = a4 ? K / 2 : K;
     int8_t *codes = static_cast<int8_t *>(ws);
     float *rs = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round_up((size_t)(M * K), kWsAlign));
-    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, qmax, codes, K, rs,
-                                          nullptr, 0, stream);
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, qmax, codes, ldq, rs, nullptr, 0, a4,
+                                          stream);
     if (e != 0)
         return hip_status(e, fn);
-    return run_gemm(fn, codes, K, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, stream);
+    return run_gemm(fn, codes, ldq, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, a4, stream);
 }
 
 }  // namespace
@@ -336,7 +364,7 @@ int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_
         overlap(span(codes, M, K, ldq, 1), span(row_scales, 1, M, M, 4)))
         return fail(CK_ERR_INVALID_ARG, "%s: codes, row_scales and x must not overlap", fn);
     const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, bits == 8 ? 127 : 7, codes, ldq,
-                                          row_scales, nullptr, 0, stream);
+                                          row_scales, nullptr, 0, false, stream);
     return hip_status(e, fn);
 }
 
@@ -354,7 +382,30 @@ int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int
         return fail(CK_ERR_INVALID_ARG, "%s: xr must be 16-byte aligned with ldr >= K, ldr %% 4 == 0", fn);
     if (overlap(span(x, M, K, ldx, 2), span(xr, M, K, ldr, 4)))
         return fail(CK_ERR_INVALID_ARG, "%s: xr overlaps x", fn);
-    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, 127, nullptr, 0, nullptr, xr, ldr, stream);
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, 127, nullptr, 0, nullptr, xr, ldr,
+                                          false, stream);
+    return hip_status(e, fn);
+}
+
+int ck_test_rotate_quant4_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                                 uint8_t *codes4, int64_t ldq, float *row_scales, void *stream)
+{
+    const char *fn = "ck_test_rotate_quant4_packed";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_g(fn, G, K));
+    if (M == 0)
+        return ok();
+    CK_TRY(check_x(fn, x, K, ldx));
+    CK_TRY(check_codes(fn, codes4, K / 2, ldq));
+    if (!row_scales || !aligned(row_scales, 4))
+        return fail(CK_ERR_INVALID_ARG, "%s: row_scales must be a non-NULL 4-byte aligned pointer", fn);
+    const Range rx = span(x, M, K, ldx, 2), rc = span(codes4, M, K / 2, ldq, 1);
+    const Range rr = span(row_scales, 1, M, M, 4);
+    if (overlap(rx, rc) || overlap(rx, rr) || overlap(rc, rr))
+        return fail(CK_ERR_INVALID_ARG, "%s: codes4, row_scales and x must not overlap", fn);
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, 7, reinterpret_cast<int8_t *>(codes4),
+                                          ldq, row_scales, nullptr, 0, true, stream);
     return hip_status(e, fn);
 }
 
@@ -439,7 +490,26 @@ int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, con
     const Range ra = span(acc, M, N, lda, 4);
     if (overlap(ra, span(codes, M, K, ldq, 1)) || overlap(ra, span(packed, N, K / 2, ldw, 1)))
         return fail(CK_ERR_INVALID_ARG, "%s: acc overlaps an input", fn);
-    return run_gemm(fn, codes, ldq, nullptr, M, K, w, nullptr, 1.0f, nullptr, 0, acc, lda, stream);
+    return run_gemm(fn, codes, ldq, nullptr, M, K, w, nullptr, 1.0f, nullptr, 0, acc, lda, false, stream);
+}
+
+int ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
+                        const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc, int64_t lda,
+                        void *stream)
+{
+    const char *fn = "ck_test_gemm_i32_a4";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    const Weights w{packed, ldw, nullptr, CK_WS_PER_CHANNEL, 64, N};
+    CK_TRY(check_weights(fn, w, K, false));
+    if (M == 0)
+        return ok();
+    CK_TRY(check_codes(fn, codes4, K / 2, ldq));
+    CK_TRY(check_out(fn, acc, N, lda, 4));
+    const Range ra = span(acc, M, N, lda, 4);
+    if (overlap(ra, span(codes4, M, K / 2, ldq, 1)) || overlap(ra, span(packed, N, K / 2, ldw, 1)))
+        return fail(CK_ERR_INVALID_ARG, "%s: acc overlaps an input", fn);
+    return run_gemm(fn, codes4, ldq, nullptr, M, K, w, nullptr, 1.0f, nullptr, 0, acc, lda, true, stream);
 }
 
 }  // extern "C"

@@ -94,6 +94,19 @@ __device__ __forceinline__ v4i act_perm16(uint32_t w0, uint32_t w1, uint32_t w2,
     return r;
 }
 
+// Signed 4-bit activation codes packed like the weights (two's complement
+// nibbles, low nibble = even k) become 16 * code in the same k order as
+// w4_operand_x16, so no reordering is needed on either side.
+__device__ __forceinline__ v4i a4_operand_x16(uint32_t d0, uint32_t d1)
+{
+    v4i r;
+    r[0] = (int)((d0 << 4) & 0xf0f0f0f0u);
+    r[1] = (int)(d0 & 0xf0f0f0f0u);
+    r[2] = (int)((d1 << 4) & 0xf0f0f0f0u);
+    r[3] = (int)(d1 & 0xf0f0f0f0u);
+    return r;
+}
+
 __device__ __forceinline__ v4i w4_operand_x16(uint32_t d0, uint32_t d1)
 {
     uint32_t l0, h0, l1, h1;

@@ -9,7 +9,7 @@ namespace ck {
 
 int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
-                        void *stream);
+                        bool packed4, void *stream);
 
 // Decode GEMV for 1 <= M <= 8 (VALU dot4, 1 KiB coalesced weight rows).  With
 // G != 0 (M = 1) it rotates and quantises the bf16 row x itself (fused linear); with
@@ -34,7 +34,7 @@ bool w4_skinny_supports(int64_t M, int64_t K);
 int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,
                    int N, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
-                   int32_t *acc_out, int64_t lda, void *stream);
+                   int32_t *acc_out, int64_t lda, bool a4, void *stream);
 
 int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed,
                       int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int N,

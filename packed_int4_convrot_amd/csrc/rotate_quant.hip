@@ -110,7 +110,12 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
     return perm(p23, p01, 0x05040100u);
 }
 
-template <int G, int BLOCK, int CPT, bool F32OUT>
+// Output of the kernel: int8 codes (one per byte), the rotated fp32 values
+// (test hook), or W4A4 codes packed two per byte (4-bit two's complement,
+// column 2j in bits 0..3), which halves the codes traffic of the W4A4 GEMM.
+enum OutMode { kCodes8 = 0, kF32 = 1, kPacked4 = 2 };
+
+template <int G, int BLOCK, int CPT, int MODE>
 __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int K, float qmax, int8_t *__restrict__ codes,
     int64_t ldq, float *__restrict__ row_scales, float *__restrict__ xr, int64_t ldr)
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     for (int w = 1; w < BLOCK / kWave; ++w)
         am = fmaxf(am, wmax[w]);
 
-    if constexpr (F32OUT) {
+    if constexpr (MODE == kF32) {
         float *orow = xr + m * ldr;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
@@ -184,10 +189,17 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
             for (int r = 0; r < 8; ++r)
                 b[r] = rne_byte(v[i][r] * inv);
             if (c < nchunk) {
-                uint2 o;
-                o.x = pack4(b[0], b[1], b[2], b[3]);
-                o.y = pack4(b[4], b[5], b[6], b[7]);
-                reinterpret_cast<uint2 *>(crow)[c] = o;
+                if constexpr (MODE == kPacked4) {
+                    // byte j = nibble of column 2j | nibble of column 2j + 1 << 4
+                    const uint32_t ev = pack4(b[0], b[2], b[4], b[6]);
+                    const uint32_t od = pack4(b[1], b[3], b[5], b[7]);
+                    reinterpret_cast<uint32_t *>(crow)[c] = (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
+                } else {
+                    uint2 o;
+                    o.x = pack4(b[0], b[1], b[2], b[3]);
+                    o.y = pack4(b[4], b[5], b[6], b[7]);
+                    reinterpret_cast<uint2 *>(crow)[c] = o;
+                }
             }
         }
         if (t == 0)
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 
 // BLOCK threads, CPT chunks of 8 columns per thread.  CPT is capped so that
 // the row stays in VGPRs without spilling: 8 at 256 threads, 4 at 1024.
-template <int G, int BLOCK, bool F32OUT>
+template <int G, int BLOCK, int MODE>
 hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_t ldx, int K,
                     float qmax, int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr)
 {
@@ -207,7 +219,7 @@ hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_
 #define CK_RQ_CASE(C)                                                                         \
     case C:                                                                                   \
         if constexpr (C <= kMaxCpt)                                                           \
-            hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, F32OUT>), grid, dim3(BLOCK), 0, \
+            hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE>), grid, dim3(BLOCK), 0, \
                                s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);                  \
         break;
     switch (cpt) {
@@ -226,7 +238,7 @@ hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_
     return hipGetLastError();
 }
 
-template <int G, bool F32OUT>
+template <int G, int MODE>
 hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t ldx, float qmax,
                      int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr)
 {
@@ -234,37 +246,37 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
     const dim3 grid((unsigned)M);
     if (nchunk <= 256 * 8) {
         const int cpt = (nchunk + 255) / 256;
-        return launch_g<G, 256, F32OUT>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
+        return launch_g<G, 256, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
     }
     const int cpt = (nchunk + 1023) / 1024;
-    return launch_g<G, 1024, F32OUT>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
+    return launch_g<G, 1024, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
 }
 
 }  // namespace
 
 int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
-                        void *stream)
+                        bool packed4, void *stream)
 {
     if (M <= 0)
         return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const float q = (float)qmax;
-    hipError_t e;
-    if (xr) {
-        switch (G) {
-        case 16: e = launch_rq<16, true>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
-        case 64: e = launch_rq<64, true>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
-        default: e = launch_rq<256, true>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
-        }
-    } else {
-        switch (G) {
-        case 16: e = launch_rq<16, false>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
-        case 64: e = launch_rq<64, false>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
-        default: e = launch_rq<256, false>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr); break;
-        }
+    const int mode = xr ? kF32 : packed4 ? kPacked4 : kCodes8;
+#define CK_RQ_G(MODE)                                                                                  \
+    switch (G) {                                                                                     \
+    case 16: return (int)launch_rq<16, MODE>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr);   \
+    case 64: return (int)launch_rq<64, MODE>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr);   \
+    default: return (int)launch_rq<256, MODE>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr);  \
     }
-    return (int)e;
+    if (mode == kF32) {
+        CK_RQ_G(kF32)
+    } else if (mode == kPacked4) {
+        CK_RQ_G(kPacked4)
+    } else {
+        CK_RQ_G(kCodes8)
+    }
+#undef CK_RQ_G
 }
 
 }  // namespace ck

@@ -32,6 +32,11 @@
 // D[8*(r/4) + 4*(l/32) + r%4][l % 32].  Lane half h and K-half s select
 // activation chunk 2h + s (codes k in [32h + 16s, +16)) and weight bytes
 // [16h + 8s, +8) of the row's 32 bytes, i.e. the same 16 k values.
+//
+// A4 variant (W4A4): the activation codes arrive packed two per byte like the
+// weights ([M][K/2] bytes, two's complement nibbles in [-7, 7]), so the
+// activation stage, its DMA and its LDS reads are half as large, and both
+// operands are decoded to 16 * value: the accumulator carries a factor 256.
 #include "ck_device.h"
 #include "launch.h"
 
@@ -57,7 +62,7 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int WGM, int WGN, int WM, int WN, int NST, bool PER_GROUP, bool OUT_I32>
+template <int WGM, int WGN, int WM, int WN, int NST, bool PER_GROUP, bool OUT_I32, bool A4>
 __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int M,
     int K, const uint8_t *__restrict__ packed, int64_t ldw, const uint16_t *__restrict__ w_scales,
@@ -72,11 +77,19 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     constexpr int NWAVES = WGM * WGN;
     constexpr int BM = WGM * WM * 32;
     constexpr int BN = WGN * WN * 32;
-    constexpr int A_BYTES = BM * 64;
+    constexpr int A_ROW = A4 ? 32 : 64;            // activation bytes per row and K step
+    constexpr int A_BYTES = BM * A_ROW;
     constexpr int STAGE = A_BYTES + BN * 32;
-    constexpr int A_LD = BM * 64 / 1024 / NWAVES;  // 1 KiB DMA instructions per wave per stage
-    constexpr int B_LD = BN * 32 / 1024 / NWAVES;
-    static_assert(A_LD * NWAVES * 1024 == BM * 64 && B_LD * NWAVES * 1024 == BN * 32, "DMA split");
+    // Activation DMA per wave and stage: A_LD instructions of A_LANES lanes
+    // (a packed activation tile smaller than 1 KiB per wave leaves lanes idle).
+    constexpr int A_PER = A_BYTES / NWAVES;
+    constexpr int A_LANES = A_PER >= 1024 ? kWave : A_PER / 16;
+    constexpr int A_LD = A_PER >= 1024 ? A_PER / 1024 : 1;
+    constexpr int B_LD = BN * 32 / 1024 / NWAVES;  // 1 KiB DMA instructions per wave per stage
+    static_assert(A_LD * NWAVES * A_LANES * 16 == A_BYTES && B_LD * NWAVES * 1024 == BN * 32, "DMA split");
+    // Accumulator factor of the decoded operands: 16 (weights) or 256 (both).
+    constexpr int ACC_SHIFT = A4 ? 8 : 4;
+    constexpr float ACC_SCALE = A4 ? 1.f / 256.f : 1.f / 16.f;
     constexpr int L = A_LD + B_LD;
     static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the block");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
@@ -102,11 +115,20 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
         lds_u8 *sa = smem + st * STAGE;
 #pragma unroll
         for (int j = 0; j < A_LD; ++j) {
-            const int q = (wave * A_LD + j) * kWave + lane;
-            const int r = q >> 2, c = (q & 3) ^ swz_a(q >> 2);
-            const int m = min(m0 + r, M - 1);
-            __builtin_amdgcn_global_load_lds(codes + (int64_t)m * ldq + kt * 64 + 16 * c,
-                                             sa + (wave * A_LD + j) * 1024, 16, 0, 0);
+            const int q = (wave * A_LD + j) * A_LANES + lane;
+            if (A_LANES == kWave || lane < A_LANES) {
+                int r, c;
+                if constexpr (A4) {
+                    r = q >> 1;
+                    c = (q & 1) ^ swz_b(r);
+                } else {
+                    r = q >> 2;
+                    c = (q & 3) ^ swz_a(r);
+                }
+                const int m = min(m0 + r, M - 1);
+                __builtin_amdgcn_global_load_lds(codes + (int64_t)m * ldq + kt * A_ROW + 16 * c,
+                                                 sa + (wave * A_LD + j) * A_LANES * 16, 16, 0, 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < B_LD; ++j) {
@@ -169,14 +191,18 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
             const int n = wn * WN * 32 + j * 32 + l32;
             bq[j] = *(const __attribute__((address_space(3))) u32x4 *)(sb + n * 32 + 16 * (h ^ swz_b(n)));
         }
-        u32x4 aq[2][WM];
+        u32x4 aq[A4 ? 1 : 2][WM];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < (A4 ? 1 : 2); ++s)
 #pragma unroll
             for (int i = 0; i < WM; ++i) {
                 const int r = wm * WM * 32 + i * 32 + l32;
-                aq[s][i] = *(const __attribute__((address_space(3))) u32x4 *)(
-                    sa + r * 64 + 16 * ((2 * h + s) ^ swz_a(r)));
+                if constexpr (A4)  // the lane's 32 k values, like a weight fragment
+                    aq[s][i] = *(const __attribute__((address_space(3))) u32x4 *)(
+                        sa + r * 32 + 16 * (h ^ swz_b(r)));
+                else
+                    aq[s][i] = *(const __attribute__((address_space(3))) u32x4 *)(
+                        sa + r * 64 + 16 * ((2 * h + s) ^ swz_a(r)));
             }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
@@ -187,7 +213,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                 bf[j] = w4_operand_x16(bq[j][2 * s], bq[j][2 * s + 1]);
 #pragma unroll
             for (int i = 0; i < WM; ++i) {
-                const v4i af = act_perm16(aq[s][i][0], aq[s][i][1], aq[s][i][2], aq[s][i][3]);
+                v4i af;
+                if constexpr (A4)
+                    af = a4_operand_x16(aq[0][i][2 * s], aq[0][i][2 * s + 1]);
+                else
+                    af = act_perm16(aq[s][i][0], aq[s][i][1], aq[s][i][2], aq[s][i][3]);
 #pragma unroll
                 for (int j = 0; j < WN; ++j) {
                     if constexpr (TRANS)  // D^T[n][m]: lane = row m, registers = columns n
@@ -228,8 +258,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                         for (int q = 0; q < 4; ++q) {
                             const int n = n0w + j * 32 + 8 * q + 4 * h;
                             if (n < N) {
-                                const v4i v = {acc[i][j][4 * q] >> 4, acc[i][j][4 * q + 1] >> 4,
-                                               acc[i][j][4 * q + 2] >> 4, acc[i][j][4 * q + 3] >> 4};
+                                const v4i v = {acc[i][j][4 * q] >> ACC_SHIFT, acc[i][j][4 * q + 1] >> ACC_SHIFT,
+                                               acc[i][j][4 * q + 2] >> ACC_SHIFT, acc[i][j][4 * q + 3] >> ACC_SHIFT};
                                 *reinterpret_cast<v4i *>(acc_out + (int64_t)m * lda + n) = v;
                             }
                         }
@@ -237,7 +267,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
         } else {
             // Stage the wave's 32 WM x 32 WN bf16 tile in LDS (rows padded to
             // 16 bytes past the tile width) and write it back with 16-byte
-            // row-contiguous stores.  Column factors (weight scale / 16) and
+            // row-contiguous stores.  Column factors (weight scale over the
+            // accumulator factor) and
             // bias are loaded one 32-column tile at a time to bound registers.
             constexpr int TW = WN * 32;          // tile width (columns)
             constexpr int PITCH = TW * 2 + 16;   // bytes per staged row
@@ -255,7 +286,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int n = min(n0w + j * 32 + 8 * q + 4 * h + t, N - 1);
-                        cs[q][t] = 0.0625f * bf16_to_f32(w_scales[n]);
+                        cs[q][t] = ACC_SCALE * bf16_to_f32(w_scales[n]);
                         bc[q][t] = bias ? bf16_to_f32(bias[n]) : 0.f;
                     }
 #pragma unroll
@@ -297,7 +328,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                 for (int r = 0; r < 16; ++r) {
                     const int m = m0 + wm * WM * 32 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                     if (m < M) {
-                        const float v = y[i][j][r] * 0.0625f * (row_scales[m] * x_scale) + bn;
+                        const float v = y[i][j][r] * ACC_SCALE * (row_scales[m] * x_scale) + bn;
                         out[(int64_t)m * ldo + n] = f32_to_bf16(v);
                     }
                 }
@@ -305,17 +336,17 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     }
 }
 
-template <int WGM, int WGN, int WM, int WN, bool PG, bool I32>
+template <int WGM, int WGN, int WM, int WN, bool PG, bool I32, bool A4>
 hipError_t launch_t(const int8_t *codes, int64_t ldq, const float *rs, int M, int K,
                     const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N,
                     const uint16_t *bias, float xs, uint16_t *out, int64_t ldo, int32_t *acc,
                     int64_t lda, hipStream_t s)
 {
     constexpr int BM = WGM * WM * 32, BN = WGN * WN * 32;
-    constexpr size_t stages = (size_t)kStages * (BM * 64 + BN * 32);
+    constexpr size_t stages = (size_t)kStages * (BM * (A4 ? 32 : 64) + BN * 32);
     constexpr size_t staging = PG ? 0 : (size_t)WGM * WGN * (WM * 32) * (WN * 32 * 2 + 16);
     constexpr size_t smem = stages > staging ? stages : staging;
-    auto kern = w4_gemm_kernel<WGM, WGN, WM, WN, kStages, PG, I32>;
+    auto kern = w4_gemm_kernel<WGM, WGN, WM, WN, kStages, PG, I32, A4>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (attr != hipSuccess)
@@ -331,22 +362,28 @@ hipError_t launch_t(const int8_t *codes, int64_t ldq, const float *rs, int M, in
 int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,
                    int N, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
-                   int32_t *acc_out, int64_t lda, void *stream)
+                   int32_t *acc_out, int64_t lda, bool a4, void *stream)
 {
     if (M <= 0)
         return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (acc_out)
-        e = launch_t<2, 4, 4, 2, false, true>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
-                                        bias, x_scale, out, ldo, acc_out, lda, s);
-    else if (per_group)
-        e = launch_t<2, 4, 2, 2, true, false>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
-                                        bias, x_scale, out, ldo, acc_out, lda, s);
-    else
-        e = launch_t<2, 4, 4, 2, false, false>(codes, ldq, row_scales, M, K, packed, ldw, w_scales, N,
-                                         bias, x_scale, out, ldo, acc_out, lda, s);
-    return (int)e;
+#define CK_GEMM_LAUNCH(A4)                                                                              \
+    if (acc_out)                                                                                        \
+        return (int)launch_t<2, 4, 4, 2, false, true, A4>(codes, ldq, row_scales, M, K, packed, ldw,    \
+                                                          w_scales, N, bias, x_scale, out, ldo,         \
+                                                          acc_out, lda, s);                             \
+    if (per_group)                                                                                      \
+        return (int)launch_t<2, 4, 2, 2, true, false, A4>(codes, ldq, row_scales, M, K, packed, ldw,    \
+                                                          w_scales, N, bias, x_scale, out, ldo,         \
+                                                          acc_out, lda, s);                             \
+    return (int)launch_t<2, 4, 4, 2, false, false, A4>(codes, ldq, row_scales, M, K, packed, ldw,       \
+                                                       w_scales, N, bias, x_scale, out, ldo, acc_out,   \
+                                                       lda, s);
+    if (a4) {
+        CK_GEMM_LAUNCH(true)
+    }
+    CK_GEMM_LAUNCH(false)
+#undef CK_GEMM_LAUNCH
 }
 
 }  // namespace ck

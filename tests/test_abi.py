@@ -154,6 +154,18 @@ def test_awq_rejects():
 def test_test_hooks_reject():
     assert lib.ck_test_rotate_f32(P, 4, 256, 256, 64, P2 + 4, 256, None) == ck.CK_ERR_INVALID_ARG
     assert lib.ck_test_gemm_i32(P, 256, 4, 256, P3, 128, 64, P3, 64, None) == ck.CK_ERR_INVALID_ARG
+    f = lib.ck_test_rotate_quant4_packed
+    assert f(P, 4, 256, 256, 64, P2, 112, P3, None) == ck.CK_ERR_INVALID_ARG   # ldq < K/2
+    assert f(P, 4, 256, 256, 64, P2, 136, P3, None) == ck.CK_ERR_INVALID_ARG   # ldq % 16
+    assert f(P, 4, 256, 256, 64, P2 + 8, 128, P3, None) == ck.CK_ERR_INVALID_ARG
+    assert f(P, 4, 256, 256, 64, P + 256, 128, P3, None) == ck.CK_ERR_INVALID_ARG  # overlaps x
+    assert f(P, 4, 256, 256, 32, P2, 128, P3, None) == ck.CK_ERR_UNSUPPORTED
+    assert f(None, 0, 256, 256, 64, None, 128, None, None) == ck.CK_OK
+    g = lib.ck_test_gemm_i32_a4
+    assert g(P, 112, 4, 256, P3, 128, 64, P4, 64, None) == ck.CK_ERR_INVALID_ARG    # ldq < K/2
+    assert g(P, 128, 4, 256, P3, 128, 40, P4, 64, None) == ck.CK_ERR_UNSUPPORTED    # N % 16
+    assert g(P, 128, 4, 256, P3, 128, 64, P3, 64, None) == ck.CK_ERR_INVALID_ARG    # acc overlaps
+    assert g(P, 128, (1 << 22), 256, P3, 128, (1 << 22), P5, (1 << 22), None) == ck.CK_ERR_UNSUPPORTED
 
 
 def test_error_message_is_thread_local():

@@ -121,6 +121,95 @@ def test_accumulators_extremes(M):
     assert np.abs(ref).max() == 127 * 8 * K
 
 
+# ------------------------------------------- W4A4 codes packed two per byte
+
+
+def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """int8 codes in [-8, 7], [M, K] -> bytes [M, K/2]: column 2j in bits 0..3,
+    column 2j + 1 in bits 4..7, each as 4-bit two's complement."""
+    c = codes.astype(np.uint8) & 0x0F
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    out = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.int16)
+    out[:, 0::2] = lo - 16 * (lo >= 8)
+    out[:, 1::2] = hi - 16 * (hi >= 8)
+    return out.astype(np.int8)
+
+
+def test_nibble_helpers_round_trip():
+    c = _rand_codes(3, 64, 8, seed=1).clip(-8, 7)
+    assert np.array_equal(_unpack_nibbles(_pack_nibbles(c)), c)
+    assert _pack_nibbles(np.array([[1, -1]], dtype=np.int8))[0, 0] == 0xF1
+
+
+@pytest.mark.parametrize("G", [16, 64, 256])
+@pytest.mark.parametrize("M,K", [(67, 3840), (1, 256), (300, 1024)])
+def test_packed_w4a4_codes_equal_byte_codes(G, M, K):
+    """The packed store of rotate-quant holds exactly the bits=4 codes and scales."""
+    x = workloads.activations(M, K, seed=G + M, outliers=max(1, K // 100), zero_rows=(0,))
+    xd = bf16_dev(x)
+    codes4, s4 = ck.rotate_quant4_packed(xd, G)
+    codes, s = ck.rotate_quant(xd, G, 4)
+    assert np.array_equal(_unpack_nibbles(host(codes4)), host(codes))
+    assert np.array_equal(host(s4), host(s))
+    ref_codes, _ = oracle.rotate_quant(x, G, 4)
+    assert_codes_close(_unpack_nibbles(host(codes4)), ref_codes)
+
+
+def test_packed_w4a4_codes_strided_input():
+    M, K, ld = 9, 1024, 1152  # padding columns hold NaN
+    x = workloads.activations(M, K, seed=6, outliers=10, ld=ld)
+    xd = bf16_dev(x)[:, :K]
+    c1, s1 = ck.rotate_quant4_packed(xd, 64)
+    c2, s2 = ck.rotate_quant(bf16_dev(np.ascontiguousarray(x[:, :K])), 64, 4)
+    assert np.array_equal(_unpack_nibbles(host(c1)), host(c2)) and np.array_equal(host(s1), host(s2))
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 16), (5, 384, 272), (64, 4096, 32), (65, 384, 528), (300, 1152, 272),
+    (513, 128, 16), (257, 3840, 544), (1000, 640, 48),
+])
+def test_accumulators_a4_bit_exact(M, K, N):
+    codes = _rand_codes(M, K, 7, seed=M + K + N + 1)
+    packed = workloads.packed_weights(N, K, seed=N + 1)
+    acc = host(ck.accumulators_i32_a4(u8_dev(_pack_nibbles(codes)), K, u8_dev(packed)))
+    ref = oracle.int_gemm(codes, oracle.unpack(packed))
+    assert np.array_equal(acc.astype(np.int64), ref)
+
+
+def test_accumulators_a4_extremes():
+    """Every code +-7 against every weight -8 or +7, longest K."""
+    M, K, N = 70, 32768, 32
+    codes = np.full((M, K), 7, dtype=np.int8)
+    codes[1::2] = -7
+    packed = np.zeros((N, K // 2), dtype=np.uint8)   # all weights -8
+    packed[N // 2:] = 0xFF                            # all weights +7
+    acc = host(ck.accumulators_i32_a4(u8_dev(_pack_nibbles(codes)), K, u8_dev(packed)))
+    ref = oracle.int_gemm(codes, oracle.unpack(packed))
+    assert np.array_equal(acc.astype(np.int64), ref)
+    assert np.abs(ref).max() == 7 * 8 * K
+
+
+@pytest.mark.parametrize("per_group", [True, False])
+@pytest.mark.parametrize("M", [65, 129, 300])
+def test_w4a4_linear_tiled_path(M, per_group):
+    """The tiled path of the W4A4 linear (packed codes in the workspace) against
+    the oracle epilogue on the GPU's own byte codes, at ragged M and N."""
+    K, N = 2304, 400
+    inp = workloads.linear_inputs(M, K, N, seed=M + 3, outliers=20, scale="group" if per_group else "channel",
+                                  zero_rows=(M - 1,), with_bias=True)
+    xd = bf16_dev(inp["x"])
+    out = host(ck.linear(xd, 256, 4, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), per_group,
+                         bias=bf16_dev(inp["bias"])))
+    codes, scales = ck.rotate_quant(xd, 256, 4)
+    ref = oracle.gemm_q(host(codes), host(scales), inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
+    assert_output_close(out, ref)
+
+
 # ------------------------------------------------------------ matmul outputs
 
 
