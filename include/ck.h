@@ -49,7 +49,8 @@
  *    CK_ERR_INVALID_ARG: a row must split into whole groups);
  *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales;
  *    M, N <= 2^22 (one launch's grid), and for shapes that run the tiled
- *    GEMM ceil(M / 128) * ceil(N / 256) < 2^23.
+ *    GEMM ceil(M / 128) * ceil(N / 256) < 2^23; row strides of codes and
+ *    packed weights ldq, ldw <= 2^23 bytes.
  *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
  *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
  *    ldw % 16 == 0; AWQ scales and zero points 16-byte aligned; outputs

@@ -59,6 +59,9 @@ Range span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t esize)
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 constexpr int64_t kMaxK = 32768;
+// Row strides of codes and packed weights, in bytes: the tiled GEMM addresses
+// a block's 256 rows with 32-bit buffer offsets.
+constexpr int64_t kMaxLd = int64_t(1) << 23;
 // A launch covers at most 2^32 - 1 work-items per grid dimension; one
 // workgroup of up to 1024 threads per activation row bounds the rows to 2^22.
 constexpr int64_t kMaxRows = int64_t(1) << 22;
@@ -113,6 +116,9 @@ int check_codes(const char *fn, const void *codes, int64_t K, int64_t ldq)
     if (ldq < K || ldq % 16 != 0)
         return fail(CK_ERR_INVALID_ARG, "%s: ldq (%lld) must be >= K and a multiple of 16", fn,
                     (long long)ldq);
+    if (ldq > kMaxLd)
+        return fail(CK_ERR_UNSUPPORTED, "%s: ldq (%lld) must be at most %lld bytes", fn, (long long)ldq,
+                    (long long)kMaxLd);
     if (!aligned(codes, 16))
         return fail(CK_ERR_INVALID_ARG, "%s: codes must be 16-byte aligned", fn);
     return CK_OK;
@@ -138,6 +144,9 @@ int check_weights(const char *fn, const Weights &w, int64_t K, bool need_scales)
     if (w.ldw < K / 2 || w.ldw % 16 != 0)
         return fail(CK_ERR_INVALID_ARG, "%s: ldw (%lld) must be >= K/2 and a multiple of 16", fn,
                     (long long)w.ldw);
+    if (w.ldw > kMaxLd)
+        return fail(CK_ERR_UNSUPPORTED, "%s: ldw (%lld) must be at most %lld bytes", fn, (long long)w.ldw,
+                    (long long)kMaxLd);
     if (!aligned(w.packed, 16))
         return fail(CK_ERR_INVALID_ARG, "%s: packed weights must be 16-byte aligned", fn);
     if (need_scales) {

@@ -9,22 +9,28 @@
 // right before CDNA4 int8 MFMA instead of being unpacked to memory.
 //
 // Tiling (block = WGM x WGN waves):
-//   * block tile BM x BN = (WGM*WM*32) x (WGN*WN*32), K step BK = 64 (one group);
-//   * v_mfma_i32_32x32x32_i8, each wave owns WM x WN 32x32 accumulator tiles
-//     (in AGPRs); the per-channel kernel runs 8 waves (two per SIMD) on a
-//     256 x 256 tile, so one wave's LDS and barrier waits are covered by the
-//     other wave's MFMAs;
+//   * block tile BM x BN = (WGM*WM*32) x (WGN*WN*32); MFMA K step 64 (one
+//     weight-scale group); a stage holds KSUB K steps;
+//   * v_mfma_i32_32x32x32_i8, each wave owns WM x WN 32x32 accumulator tiles;
+//     the per-channel kernel runs 8 waves (two per SIMD) on a 256 x 256 tile;
 //   * operands move global -> LDS directly (global_load_lds_dwordx4, no VGPR
-//     staging) into a ring of NST stages, so the loads of K step t + NST - 1
-//     are in flight while step t is multiplied;
-//   * LDS rows are unpadded ([BM][64] activation bytes, [BN][32] packed weight
-//     bytes); the 16-byte slots inside a row are XOR-swizzled by row so that
-//     the 16-byte fragment reads are bank-conflict free; the DMA writes lanes
-//     contiguously, so each lane loads the global chunk that belongs in its
-//     slot;
+//     staging) into two stage buffers.  A stage covers 128 bytes of every
+//     operand row where it can (4 K steps of packed nibbles): the DMA's cost
+//     on gfx950 grows with the number of distinct rows (cache lines) an
+//     instruction touches far more than with its bytes, so 32-byte row
+//     pieces per instruction ran the fill at a quarter of the rate;
+//   * one barrier per stage.  Fragment reads run one K step ahead of the
+//     MFMAs (two register sets), and the first step of the next stage is read
+//     right after that barrier, so LDS latency is never waited on between
+//     MFMAs; the DMA of stage t + 2 is issued at the same barrier into the
+//     buffer that stage t has just finished reading;
+//   * LDS rows are unpadded; the 16-byte slots inside a row are XOR-swizzled
+//     by row (swizzles measured conflict-free with SQ_LDS_BANK_CONFLICT for
+//     these read patterns); the DMA writes lanes contiguously, so each lane
+//     loads the global chunk that belongs in its slot;
 //   * each lane reads one 16-byte weight fragment per K step (both 32-wide k
-//     halves) and decodes it in VGPRs; activation fragments are permuted to
-//     the decode's even/odd k order as they are read;
+//     halves) and decodes it in VGPRs; int8 activation fragments are permuted
+//     to the decode's even/odd k order as they are read;
 //   * blocks are renumbered so that each XCD (blocks are dealt to the 8 XCDs
 //     round-robin) gets a contiguous run of tiles that share activation rows.
 // Operand layouts of v_mfma_i32_32x32x32_i8: lane l holds 16 int8 of row
@@ -43,16 +49,25 @@
 namespace ck {
 namespace {
 
-constexpr int kStages = 4;
-
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
-// Slot swizzles, chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950 for the
-// fragment read patterns: (r >> 2) & 3 for the 64-byte activation rows and
-// ((n >> 2) ^ (n >> 3)) & 1 for the 32-byte weight rows read without conflicts
-// (e.g. ((r >> 1) ^ (r >> 3)) & 3 gave 2-way conflicts).
-__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int swz_b(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
+// Slot swizzle of an LDS row of S 16-byte slots, for fragment reads in which
+// 32 consecutive rows read one logical slot (lane half h in bit 0 of the
+// slot).  Chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950: 2 slots
+// ((r >> 2) ^ (r >> 3)) & 1, 8 slots (r >> 1) & 7 read without conflicts
+// (e.g. r & 7 gave 2-way conflicts).
+template <int S>
+__device__ __forceinline__ int swz(int r)
+{
+    static_assert(S == 2 || S == 4 || S == 8, "slot count");
+    if constexpr (S == 2)
+        return ((r >> 2) ^ (r >> 3)) & 1;
+    else if constexpr (S == 4)
+        return (r >> 2) & 3;
+    else
+        return (r >> 1) & 7;
+}
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -62,7 +77,10 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int WGM, int WGN, int WM, int WN, int NST, bool PER_GROUP, bool OUT_I32, bool A4>
+// s_waitcnt lgkmcnt(0) leaving vmcnt alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+template <int WGM, int WGN, int WM, int WN, int KSUB, bool PER_GROUP, bool OUT_I32, bool A4>
 __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int M,
     int K, const uint8_t *__restrict__ packed, int64_t ldw, const uint16_t *__restrict__ w_scales,
@@ -77,21 +95,26 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     constexpr int NWAVES = WGM * WGN;
     constexpr int BM = WGM * WM * 32;
     constexpr int BN = WGN * WN * 32;
-    constexpr int A_ROW = A4 ? 32 : 64;            // activation bytes per row and K step
+    constexpr int A_STEP = A4 ? 32 : 64;          // activation bytes per row and K step
+    constexpr int A_ROW = A_STEP * KSUB;          // ... per row and stage
+    constexpr int B_ROW = 32 * KSUB;
+    constexpr int A_SLOTS = A_ROW / 16, B_SLOTS = B_ROW / 16;
     constexpr int A_BYTES = BM * A_ROW;
-    constexpr int STAGE = A_BYTES + BN * 32;
-    // Activation DMA per wave and stage: A_LD instructions of A_LANES lanes
-    // (a packed activation tile smaller than 1 KiB per wave leaves lanes idle).
-    constexpr int A_PER = A_BYTES / NWAVES;
+    constexpr int STAGE = A_BYTES + BN * B_ROW;
+    // DMA per wave and stage: X_LD instructions of X_LANES lanes (a tile
+    // smaller than 1 KiB per wave leaves lanes idle).
+    constexpr int A_PER = A_BYTES / NWAVES, B_PER = BN * B_ROW / NWAVES;
     constexpr int A_LANES = A_PER >= 1024 ? kWave : A_PER / 16;
+    constexpr int B_LANES = B_PER >= 1024 ? kWave : B_PER / 16;
     constexpr int A_LD = A_PER >= 1024 ? A_PER / 1024 : 1;
-    constexpr int B_LD = BN * 32 / 1024 / NWAVES;  // 1 KiB DMA instructions per wave per stage
-    static_assert(A_LD * NWAVES * A_LANES * 16 == A_BYTES && B_LD * NWAVES * 1024 == BN * 32, "DMA split");
+    constexpr int B_LD = B_PER >= 1024 ? B_PER / 1024 : 1;
+    static_assert(A_LD * NWAVES * A_LANES * 16 == A_BYTES, "A DMA split");
+    static_assert(B_LD * NWAVES * B_LANES * 16 == BN * B_ROW, "B DMA split");
+    static_assert(KSUB % 2 == 0, "two fragment sets alternate across stages");
     // Accumulator factor of the decoded operands: 16 (weights) or 256 (both).
     constexpr int ACC_SHIFT = A4 ? 8 : 4;
     constexpr float ACC_SCALE = A4 ? 1.f / 256.f : 1.f / 16.f;
-    constexpr int L = A_LD + B_LD;
-    static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the block");
+    constexpr int AQ = A4 ? 1 : 2;                // 16-byte activation fragments per tile and K step
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8 *smem = (lds_u8 *)smem_generic;
 
@@ -108,35 +131,79 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     const int wm = wave / WGN, wn = wave % WGN;
     const int l32 = lane % 32, h = lane / 32;
     const int ksteps = K / 64;
+    const int nstages = (ksteps + KSUB - 1) / KSUB;
+    const int arow_bytes = A4 ? K / 2 : K;         // valid bytes of a codes row
 
-    // Global -> LDS for K step kt into ring slot st.  Rows past M / N re-read
-    // the last valid row; their results are never stored.
-    auto issue_stage = [&](int kt, int st) {
-        lds_u8 *sa = smem + st * STAGE;
+    // Logical slot of a row's 16-byte chunk g (K step g / (A_STEP / 16)):
+    // int8 activation chunks 2h + s of a K step are stored as slot 2s + h so
+    // that, like the packed rows, the lane half is bit 0 of the slot.
+    auto a_slot = [](int g) {
+        if constexpr (A4)
+            return g;
+        else
+            return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1);
+    };
+
+    // Global -> LDS for stage st into buffer b, through buffer resources that
+    // span exactly the block's operand rows: a row past M / N or a chunk past
+    // the end of the last row reads as zero, and such results are never used.
+    // (MUBUF rather than global loads: a FLAT load into LDS still in flight
+    // makes the compiler wait for every LDS read, not just the ones needed.)
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(codes + (int64_t)m0 * ldq), (short)0,
+        (int)((int64_t)(min(M - m0, BM) - 1) * ldq + arow_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(packed + (int64_t)n0 * ldw), (short)0,
+        (int)((int64_t)(min(N - n0, BN) - 1) * ldw + K / 2), 0x00020000);
+    auto issue_stage = [&](int st, int b) {
+        lds_u8 *sa = smem + b * STAGE;
 #pragma unroll
         for (int j = 0; j < A_LD; ++j) {
             const int q = (wave * A_LD + j) * A_LANES + lane;
             if (A_LANES == kWave || lane < A_LANES) {
-                int r, c;
-                if constexpr (A4) {
-                    r = q >> 1;
-                    c = (q & 1) ^ swz_b(r);
-                } else {
-                    r = q >> 2;
-                    c = (q & 3) ^ swz_a(r);
-                }
-                const int m = min(m0 + r, M - 1);
-                __builtin_amdgcn_global_load_lds(codes + (int64_t)m * ldq + kt * A_ROW + 16 * c,
-                                                 sa + (wave * A_LD + j) * A_LANES * 16, 16, 0, 0);
+                const int r = q / A_SLOTS;
+                const int g = a_slot((q % A_SLOTS) ^ swz<A_SLOTS>(r));  // a_slot is an involution
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    a_rsrc, (__attribute__((address_space(3))) void *)(sa + (wave * A_LD + j) * A_LANES * 16), 16,
+                    (int)(r * ldq) + st * A_ROW + 16 * g, 0, 0, 0);
             }
         }
 #pragma unroll
         for (int j = 0; j < B_LD; ++j) {
-            const int q = (wave * B_LD + j) * kWave + lane;
-            const int n = q >> 1, c = (q & 1) ^ swz_b(q >> 1);
-            const int nn = min(n0 + n, N - 1);
-            __builtin_amdgcn_global_load_lds(packed + (int64_t)nn * ldw + kt * 32 + 16 * c,
-                                             sa + A_BYTES + (wave * B_LD + j) * 1024, 16, 0, 0);
+            const int q = (wave * B_LD + j) * B_LANES + lane;
+            if (B_LANES == kWave || lane < B_LANES) {
+                const int n = q / B_SLOTS;
+                const int c = (q % B_SLOTS) ^ swz<B_SLOTS>(n);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    b_rsrc, (__attribute__((address_space(3))) void *)(sa + A_BYTES + (wave * B_LD + j) * B_LANES * 16), 16,
+                    (int)(n * ldw) + st * B_ROW + 16 * c, 0, 0, 0);
+            }
+        }
+    };
+
+    // Fragments of one K step: weight row pieces and activation row pieces.
+    struct Frag {
+        u32x4 b[WN];
+        u32x4 a[AQ][WM];
+    };
+    // Fragment addresses: the row swizzles depend only on the low five bits
+    // of the row (32-row tiles), so every tile of a wave shares one slot
+    // offset per K step and the tiles differ by immediate offsets.
+    const int swa = swz<A_SLOTS>(l32), swb = swz<B_SLOTS>(l32);
+    const int a_base = (wm * WM * 32 + l32) * A_ROW;
+    const int b_base = A_BYTES + (wn * WN * 32 + l32) * B_ROW;
+    auto read_frag = [&](Frag &f, int b, int u) {
+        const lds_u8 *sb = smem + b * STAGE + b_base + 16 * ((2 * u + h) ^ swb);
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+            f.b[j] = *(lds_u32x4 *)(sb + j * 32 * B_ROW);
+#pragma unroll
+        for (int s = 0; s < AQ; ++s) {
+            const int slot = A4 ? 2 * u + h : 4 * u + 2 * s + h;
+            const lds_u8 *sa = smem + b * STAGE + a_base + 16 * (slot ^ swa);
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+                f.a[s][i] = *(lds_u32x4 *)(sa + i * 32 * A_ROW);
         }
     };
 
@@ -153,71 +220,27 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                     y[i][j][r] = 0.f;
             }
 
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-        if (s < ksteps)
-            issue_stage(s, s);
-
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const int st = kt % NST;
-        // This wave's DMA for step kt has landed once at most the later
-        // stages' loads are outstanding; the barrier extends that to all
-        // waves and also retires every read of the slot refilled below.
-        if (kt + NST - 2 < ksteps)
-            wait_vmcnt<(NST - 2) * L>();
-        else
-            wait_vmcnt<0>();
-        // A bare barrier: __syncthreads() would also wait for every DMA still
-        // in flight (vmcnt(0)) and drain the ring.  LDS reads of the previous
-        // step were consumed by its MFMAs, so no LDS fence is needed.
-        __builtin_amdgcn_s_barrier();
+    // One K step on fragments f; kt is the global K step (per-group scale row).
+    auto compute = [&](const Frag &f, int kt) {
         uint16_t sc[PER_GROUP ? WN : 1];
         if constexpr (PER_GROUP) {
 #pragma unroll
             for (int j = 0; j < WN; ++j)
                 sc[j] = w_scales[(int64_t)kt * N + min(n0 + wn * WN * 32 + j * 32 + l32, N - 1)];
         }
-        if (kt + NST - 1 < ksteps)
-            issue_stage(kt + NST - 1, (kt + NST - 1) % NST);
-
-        // All fragment reads of this K step are issued before the first MFMA,
-        // so a single LDS latency is exposed per step instead of one per
-        // fragment.
-        const lds_u8 *sa = smem + st * STAGE;
-        const lds_u8 *sb = sa + A_BYTES;
-        u32x4 bq[WN];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-            const int n = wn * WN * 32 + j * 32 + l32;
-            bq[j] = *(const __attribute__((address_space(3))) u32x4 *)(sb + n * 32 + 16 * (h ^ swz_b(n)));
-        }
-        u32x4 aq[A4 ? 1 : 2][WM];
-#pragma unroll
-        for (int s = 0; s < (A4 ? 1 : 2); ++s)
-#pragma unroll
-            for (int i = 0; i < WM; ++i) {
-                const int r = wm * WM * 32 + i * 32 + l32;
-                if constexpr (A4)  // the lane's 32 k values, like a weight fragment
-                    aq[s][i] = *(const __attribute__((address_space(3))) u32x4 *)(
-                        sa + r * 32 + 16 * (h ^ swz_b(r)));
-                else
-                    aq[s][i] = *(const __attribute__((address_space(3))) u32x4 *)(
-                        sa + r * 64 + 16 * ((2 * h + s) ^ swz_a(r)));
-            }
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             v4i bf[WN];
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-                bf[j] = w4_operand_x16(bq[j][2 * s], bq[j][2 * s + 1]);
+                bf[j] = w4_operand_x16(f.b[j][2 * s], f.b[j][2 * s + 1]);
 #pragma unroll
             for (int i = 0; i < WM; ++i) {
                 v4i af;
                 if constexpr (A4)
-                    af = a4_operand_x16(aq[0][i][2 * s], aq[0][i][2 * s + 1]);
+                    af = a4_operand_x16(f.a[0][i][2 * s], f.a[0][i][2 * s + 1]);
                 else
-                    af = act_perm16(aq[s][i][0], aq[s][i][1], aq[s][i][2], aq[s][i][3]);
+                    af = act_perm16(f.a[s][i][0], f.a[s][i][1], f.a[s][i][2], f.a[s][i][3]);
 #pragma unroll
                 for (int j = 0; j < WN; ++j) {
                     if constexpr (TRANS)  // D^T[n][m]: lane = row m, registers = columns n
@@ -239,7 +262,70 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                         y[i][j][r] = __builtin_fmaf(scf, (float)acc[i][j][r], y[i][j][r]);
             }
         }
+    };
+
+    constexpr int L = A_LD + B_LD;  // DMA instructions per wave and stage
+    Frag fr[2];
+    issue_stage(0, 0);
+    if (nstages > 1) {
+        issue_stage(1, 1);
+        wait_vmcnt<L>();
+    } else {
+        wait_vmcnt<0>();
     }
+    // The epilogue's kernel arguments are read here, so that no scalar load
+    // (which returns out of order) is pending in the loop: the LDS waits
+    // there can then count just the fragment reads in flight.
+    asm volatile("" ::"s"(out), "s"(bias), "s"(row_scales), "s"(w_scales), "s"(acc_out), "s"(ldo),
+                 "s"(lda), "s"(x_scale));
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    read_frag(fr[0], 0, 0);
+
+    // Stages that have a successor: straight-line K steps.
+    int st = 0;
+    for (; st + 1 < nstages; ++st) {
+        const int b = st & 1;
+#pragma unroll
+        for (int u = 0; u + 1 < KSUB; ++u) {
+            // The fences keep the reads of step u + 1 ahead of the MFMAs of
+            // step u, so that those MFMAs wait only for their own fragments.
+            read_frag(fr[(u + 1) & 1], b, u + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(fr[u & 1], st * KSUB + u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Every read of this buffer has returned once each wave has waited
+        // for its own, and the next stage has landed once each wave has
+        // waited for its own DMA; the barrier extends both to the block, so
+        // the buffer can be refilled with stage st + 2 and the next stage's
+        // first fragments read.
+        wait_lgkm0();
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (st + 2 < nstages)
+            issue_stage(st + 2, b);
+        read_frag(fr[0], b ^ 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(fr[(KSUB - 1) & 1], st * KSUB + KSUB - 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // The last stage, possibly partial.
+    {
+        const int b = st & 1;
+        const int nsub = ksteps - st * KSUB;
+#pragma unroll
+        for (int u = 0; u < KSUB; ++u) {
+            if (u < nsub) {
+                if (u + 1 < nsub)
+                    read_frag(fr[(u + 1) & 1], b, u + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(fr[u & 1], st * KSUB + u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // Epilogue.
     if constexpr (TRANS) {
@@ -336,17 +422,18 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     }
 }
 
-template <int WGM, int WGN, int WM, int WN, bool PG, bool I32, bool A4>
+template <int WGM, int WGN, int WM, int WN, int KSUB, bool PG, bool I32, bool A4>
 hipError_t launch_t(const int8_t *codes, int64_t ldq, const float *rs, int M, int K,
                     const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N,
                     const uint16_t *bias, float xs, uint16_t *out, int64_t ldo, int32_t *acc,
                     int64_t lda, hipStream_t s)
 {
     constexpr int BM = WGM * WM * 32, BN = WGN * WN * 32;
-    constexpr size_t stages = (size_t)kStages * (BM * (A4 ? 32 : 64) + BN * 32);
+    constexpr size_t stages = (size_t)2 * KSUB * (BM * (A4 ? 32 : 64) + BN * 32);
     constexpr size_t staging = PG ? 0 : (size_t)WGM * WGN * (WM * 32) * (WN * 32 * 2 + 16);
     constexpr size_t smem = stages > staging ? stages : staging;
-    auto kern = w4_gemm_kernel<WGM, WGN, WM, WN, kStages, PG, I32, A4>;
+    static_assert(smem <= 160 * 1024, "LDS");
+    auto kern = w4_gemm_kernel<WGM, WGN, WM, WN, KSUB, PG, I32, A4>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (attr != hipSuccess)
@@ -369,16 +456,16 @@ int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, in
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 #define CK_GEMM_LAUNCH(A4)                                                                              \
     if (acc_out)                                                                                        \
-        return (int)launch_t<2, 4, 4, 2, false, true, A4>(codes, ldq, row_scales, M, K, packed, ldw,    \
-                                                          w_scales, N, bias, x_scale, out, ldo,         \
-                                                          acc_out, lda, s);                             \
+        return (int)launch_t<2, 4, 4, 2, (A4 ? 4 : 2), false, true, A4>(codes, ldq, row_scales, M, K, packed, ldw, \
+                                                             w_scales, N, bias, x_scale, out, ldo,      \
+                                                             acc_out, lda, s);                          \
     if (per_group)                                                                                      \
-        return (int)launch_t<2, 4, 2, 2, true, false, A4>(codes, ldq, row_scales, M, K, packed, ldw,    \
+        return (int)launch_t<2, 4, 2, 2, 2, true, false, A4>(codes, ldq, row_scales, M, K, packed, ldw, \
+                                                             w_scales, N, bias, x_scale, out, ldo,      \
+                                                             acc_out, lda, s);                          \
+    return (int)launch_t<2, 4, 4, 2, (A4 ? 4 : 2), false, false, A4>(codes, ldq, row_scales, M, K, packed, ldw,    \
                                                           w_scales, N, bias, x_scale, out, ldo,         \
-                                                          acc_out, lda, s);                             \
-    return (int)launch_t<2, 4, 4, 2, false, false, A4>(codes, ldq, row_scales, M, K, packed, ldw,       \
-                                                       w_scales, N, bias, x_scale, out, ldo, acc_out,   \
-                                                       lda, s);
+                                                          acc_out, lda, s);
     if (a4) {
         CK_GEMM_LAUNCH(true)
     }

@@ -113,6 +113,9 @@ def test_launch_size_limits():
     assert gq(M=(1 << 22), N=(1 << 22), ldo=(1 << 22)) == ck.CK_ERR_UNSUPPORTED
     assert b"too large" in lib.ck_last_error_msg()
     assert gq(N=(1 << 22) + 16) == ck.CK_ERR_UNSUPPORTED
+    # row strides beyond 32-bit buffer offsets of a 256-row tile
+    assert gq(ldq=(1 << 23) + 16) == ck.CK_ERR_UNSUPPORTED
+    assert gq(ldw=(1 << 23) + 16) == ck.CK_ERR_UNSUPPORTED
 
 
 def test_gemv_rejects_large_m():
