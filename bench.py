@@ -369,19 +369,25 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
         packed = u8(inp["packed"])
         scl = bf16(inp["w_scales"])
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        codes, rs = ck.rotate_quant(x, G, 4)
-        lin = _time(lambda i: ck.linear(x, G, 4, packed, scl, False, out=out), stream, 20)
-        rq = _time(lambda i: ck.rotate_quant(x, G, 4, codes, rs), stream, 20)
-        gm = _time(lambda i: ck.gemm_q(codes, rs, packed, scl, False, out=out), stream, 20)
+        work = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=dev)  # held by the caller
+        # the linear's own two launches: packed rotate-quant, then the GEMM on packed codes
+        codes4, rs = ck.rotate_quant_packed4(x, G)
+        lin = _time(lambda i: ck.linear(x, G, 4, packed, scl, False, out=out, workspace=work), stream, 20)
+        rq = _time(lambda i: ck.rotate_quant_packed4(x, G, codes4, rs), stream, 20)
+        gm = _time(lambda i: ck.gemm_packed4(codes4, rs, packed, scl, False, out=out), stream, 20)
+        # codes one per byte (ck_rotate_quant + ck_w4_gemm_q), for comparison
+        codes, rs8 = ck.rotate_quant(x, G, 4)
+        gm8 = _time(lambda i: ck.gemm_q(codes, rs8, packed, scl, False, out=out), stream, 20)
         ops = 2.0 * M * N * K
-        rq_bytes = M * K * 2 + M * K + M * 4
+        rq_bytes = M * K * 2 + M * K // 2 + M * 4
         res[name] = {"linear_us": round(lin, 2), "rotate_quant_us": round(rq, 2), "gemm_us": round(gm, 2),
                      "gemm_int8_TOPS": round(ops / gm / 1e6, 1),
                      "gemm_frac_int8_peak": round(ops / gm / 1e6 / INT8_PEAK_TOPS, 4),
                      "linear_int8_TOPS": round(ops / lin / 1e6, 1),
                      "rotate_quant_GBps": round(rq_bytes / rq / 1e3, 1),
-                     "rotate_quant_frac_hbm": round(rq_bytes / rq / 1e3 / HBM_PEAK_GBS, 4)}
-        del x, packed, out, codes
+                     "rotate_quant_frac_hbm": round(rq_bytes / rq / 1e3 / HBM_PEAK_GBS, 4),
+                     "byte_codes_gemm_us": round(gm8, 2)}
+        del x, packed, out, codes, codes4, work
         log("bench: %s done" % name)
 
     # standalone rotate-quant, strided [8192, 10240] in [8192, 10752]
@@ -400,6 +406,21 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
             "frac_hbm": round(rq_bytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     del xs
     log("bench: rotate-quant done")
+
+    # offline weight producer: rotate + quantise + pack a bf16 [N, K] weight
+    N, K = 10240, 3840
+    rng = torch.Generator(device=dev).manual_seed(0)
+    wsrc = [(torch.randn((N, K), generator=rng, device=dev) * 0.02).to(torch.bfloat16) for _ in range(4)]  # 315 MB > the 256 MB Infinity Cache
+    pk = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    for pg in (False, True):
+        sc = torch.empty((K // 64, N) if pg else (N,), dtype=torch.bfloat16, device=dev)
+        us = _time(lambda i: ck.quantize_weights(wsrc[i % 4], 64, pg, pk, sc), stream, 20)
+        nbytes = N * K * 2 + N * K // 2 + sc.numel() * 2
+        res["quantize_weights_n%d_k%d_g64_%s" % (N, K, "per_group" if pg else "per_channel")] = {
+            "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+            "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del wsrc, pk
+    log("bench: weight producer done")
 
     # AWQ W4A16 GEMV
     name = "awq_w4a16_gemv_m1_k3072_n18432"

@@ -145,6 +145,35 @@ int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_
                int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                uint16_t *out, int64_t ldo, void *stream);
 
+/*
+ * ck_rotate_quant_packed4  [RQ] [W4A4]
+ * ck_rotate_quant(bits = 4) with the codes stored two per byte:
+ *   codes4  uint8 [M, ldq], ldq >= K/2 bytes and a multiple of 16, 16-byte
+ *           aligned; byte j of a row holds column 2j in bits 0..3 and column
+ *           2j + 1 in bits 4..7, each code in [-7, 7] as 4-bit two's
+ *           complement;
+ *   row_scales fp32 [M] as in ck_rotate_quant.
+ * The codes are the same as ck_rotate_quant's.  Quantised once, they can be
+ * reused by every ck_w4a4_gemm_packed that shares the input (the activation
+ * cache of [SD], for inputs of scale 1).
+ */
+int ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                            uint8_t *codes4, int64_t ldq, float *row_scales, void *stream);
+
+/*
+ * ck_w4a4_gemm_packed  [W4A4] [SD]
+ * ck_w4_gemm_q on W4A4 codes packed two per byte (as ck_rotate_quant_packed4
+ * writes them), on the tiled MFMA GEMM for every M >= 1:
+ *   out[m,n] = bf16( acc[m,n] * row_scales[m] * s_w(n) (+ bias[n]) ),
+ *   acc[m,n] = sum_k code[m,k] * (q[n,k] - 8).
+ * Weights, scales, bias and out as in ck_w4_gemm_q; codes4 uint8 [M, ldq],
+ * ldq >= K/2.  This is the matmul half of ck_w4a4_linear for M > 64.
+ */
+int ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t M,
+                        int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                        int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                        uint16_t *out, int64_t ldo, void *stream);
+
 /* Bytes of workspace ck_w4a8_linear / ck_w4a4_linear need for M rows of K
  * columns: the int8 codes [M, K] plus the fp32 row scales, each 256-byte
  * aligned inside the workspace. */
@@ -173,7 +202,7 @@ int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
  * As ck_w4a8_linear with int4 activations (qmax 7, symmetric).  When the
  * tiled GEMM serves M (more rows than the few-row kernels take), the codes are
  * held in the workspace two per byte (4-bit two's complement, column 2j in
- * the low nibble), as ck_test_rotate_quant4_packed writes them; the result is
+ * the low nibble), as ck_rotate_quant_packed4 writes them; the result is
  * the same as with one code per byte.
  */
 int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
@@ -200,6 +229,30 @@ int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   const uint16_t *zeros, int32_t Gw, int64_t N, const uint16_t *bias,
                   uint16_t *out, int64_t ldo, void *stream);
 
+/*
+ * ck_quantize_weights  [SD] [AWQ]
+ * Offline producer of the packed weights the matmuls consume, for a bf16
+ * weight W [N, K] (row n = output column n):
+ *   wr = each contiguous G-column group of each row times H_G / sqrt(G)
+ *        (the rotation ck_rotate_quant applies to activations, so that the
+ *        product of rotated activations and rotated weights is x . W^T);
+ *   a  = max |wr| over the row (CK_WS_PER_CHANNEL) or over each 64-column
+ *        group of the row (CK_WS_PER_GROUP, Gw = 64);
+ *   s  = bf16(fp32(a / 7)); code = clamp(rne(fp32(wr * fp32(1 / s))), -7, 7)
+ *        (code 0 where s == 0); stored q = code + 8, packed two per byte:
+ *        byte j of row n = q[n, 2j] | q[n, 2j + 1] << 4.
+ * The pages hold packed checkpoints ([SD] summary) and the packed layout
+ * ([AWQ] module docstring) but no weight-quantiser formula; symmetric
+ * absmax / 7 is the reading taken.
+ *   w       bf16 [N, ldw_in], ldw_in >= K, ldw_in % 8 == 0, 16-byte aligned
+ *   packed  uint8 [N, ldp], ldp >= K/2, ldp % 16 == 0, 16-byte aligned
+ *   scales  bf16 [N] (per channel) or [K/64, N] (per group)
+ * G and K as in ck_rotate_quant; N <= 2^22.  Runs on `stream`.
+ */
+int ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
+                        int32_t scale_kind, uint8_t *packed, int64_t ldp, uint16_t *scales,
+                        void *stream);
+
 /* ---------------------------------------------------------------- test hooks
  * Same device code paths as above with a debug epilogue, so that each stage
  * can be compared exactly with the oracle. */
@@ -215,17 +268,8 @@ int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,
                      const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,
                      int64_t lda, void *stream);
 
-/* The W4A4 codes of ck_rotate_quant(bits = 4) packed two per byte:
- * codes4 uint8 [M, ldq], ldq >= K/2 bytes and a multiple of 16, 16-byte
- * aligned; byte j of a row holds column 2j in bits 0..3 and column 2j + 1 in
- * bits 4..7, each code in [-7, 7] as 4-bit two's complement.  row_scales as
- * in ck_rotate_quant.  The workspace layout of ck_w4a4_linear's tiled path. */
-int ck_test_rotate_quant4_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                                 int32_t G, uint8_t *codes4, int64_t ldq, float *row_scales,
-                                 void *stream);
-
 /* The integer accumulators of the tiled GEMM on packed W4A4 codes (codes4 as
- * written by ck_test_rotate_quant4_packed), for any M >= 1:
+ * written by ck_rotate_quant_packed4), for any M >= 1:
  * acc[m,n] = sum_k code[m,k] * (q[n,k] - 8), acc int32 [M, lda]. */
 int ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
                         const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,

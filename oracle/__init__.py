@@ -11,6 +11,9 @@ order the pages give them:
   absmax, fp32 decision) -> unpack (q - 8) -> exact integer matmul ->
   scale epilogue (fp64)
 
+and, for the weights, rotate -> quantize_weights (absmax/7 per row or per
+64-column group, bf16 scale, fp32 decision) -> pack.
+
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, library routines and the worked examples in ``tests/golden/``.
 """
@@ -54,6 +57,7 @@ def _load():
             "oracle_int_gemm": [p, i64, i64, i64, p, i64, i64, p],
             "oracle_epilogue": [p, i64, i64, i64, p, p, i32, p, p],
             "oracle_awq_gemv": [p, i64, i64, i64, p, i64, p, p, i64, i64, p, p],
+            "oracle_quantize_weights": [p, i64, i64, i64, i32, p, i64, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -116,6 +120,23 @@ def quantize(xr: np.ndarray, bits: int):
 def rotate_quant(x, G: int, bits: int, K: int | None = None):
     """Rotation followed by rowwise quantisation: (codes, scales)."""
     return quantize(rotate(x, G, K), bits)
+
+
+def quantize_weights(wr: np.ndarray, per_group: bool, Gw: int = 64):
+    """(packed uint8 [N, K/2], bf16 scale bits uint16 [N] or [K/Gw, N]) from rotated
+    fp32 weight rows: symmetric absmax/7 codes, stored as q = code + 8."""
+    wr = np.ascontiguousarray(wr, dtype=np.float32)
+    N, K = wr.shape
+    packed = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((K // Gw, N) if per_group else (N,), dtype=np.uint16)
+    _check(_load().oracle_quantize_weights(_ptr(wr), N, K, K, Gw if per_group else 0, _ptr(packed),
+                                           K // 2, _ptr(scales)), "quantize_weights")
+    return packed, scales
+
+
+def rotate_quantize_weights(w, G: int, per_group: bool, Gw: int = 64):
+    """The offline weight producer: rotation by H_G, then quantize_weights."""
+    return quantize_weights(rotate(w, G), per_group, Gw)
 
 
 def unpack(packed, K: int | None = None) -> np.ndarray:

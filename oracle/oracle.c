@@ -146,6 +146,71 @@ int oracle_quantize(const float *xr, int64_t M, int64_t K, int64_t ldr,
     return OK;
 }
 
+/* fp32 -> bf16 bit pattern, round to nearest even on the 16 dropped bits
+ * (finite values only). */
+static uint16_t bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    return (uint16_t)upper;
+}
+
+/*
+ * Weight quantisation of already rotated weight rows (the producer of the
+ * packed format; the pages hold packed checkpoints but no formula, so this is
+ * the plain symmetric reading, listed in the design doc):
+ *   a = max |wr| over the row (group == 0) or over each run of `group`
+ *       columns (group == 64);
+ *   s = bf16(fp32(a / 7)) and, where s > 0,
+ *   code = clamp(rne(fp32(wr * fp32(1 / s))), -7, 7), else code = 0;
+ *   stored q = code + 8, byte j of a row = q[2j] | q[2j + 1] << 4.
+ * scales: bf16 bits, [N] (group == 0) or [K/group, N] (N contiguous).
+ */
+int oracle_quantize_weights(const float *wr, int64_t N, int64_t K, int64_t ldr, int32_t group,
+                            uint8_t *packed, int64_t ldp, uint16_t *scales)
+{
+    if (!wr || !packed || !scales || N < 0 || K <= 0 || K % 2 != 0 || ldr < K || ldp < K / 2 ||
+        group < 0 || (group > 0 && (group % 2 != 0 || K % group != 0)))
+        return BAD_ARG;
+    const int64_t glen = group > 0 ? group : K;
+    for (int64_t n = 0; n < N; ++n) {
+        const float *row = wr + n * ldr;
+        uint8_t *prow = packed + n * ldp;
+        for (int64_t g0 = 0; g0 < K; g0 += glen) {
+            float a = 0.0f;
+            for (int64_t k = g0; k < g0 + glen; ++k) {
+                float v = fabsf(row[k]);
+                if (v > a)
+                    a = v;
+            }
+            const uint16_t sb = bf16_round(a / 7.0f);
+            const float sf = (float)bf16_value(sb);
+            const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+            for (int64_t k = g0; k < g0 + glen; k += 2) {
+                int q[2];
+                for (int e = 0; e < 2; ++e) {
+                    float r = nearbyintf(row[k + e] * inv);
+                    if (r > 7.0f)
+                        r = 7.0f;
+                    if (r < -7.0f)
+                        r = -7.0f;
+                    q[e] = (int)r + 8;
+                }
+                prow[k / 2] = (uint8_t)(q[0] | (q[1] << 4));
+            }
+            if (group > 0)
+                scales[(g0 / glen) * N + n] = sb;
+            else
+                scales[n] = sb;
+        }
+    }
+    return OK;
+}
+
 /*
  * Packed uint4 weight decode: byte j of row n holds column 2j in bits 0..3
  * and column 2j+1 in bits 4..7; the stored code q stands for q - 8.

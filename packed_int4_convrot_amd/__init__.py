@@ -43,9 +43,12 @@ SIGNATURES = {
                         _i64, _p, _sz, _p], ctypes.c_int),
     "ck_w4a16_gemv": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _i64, _p, _p, _i64, _p],
                       ctypes.c_int),
+    "ck_quantize_weights": ([_p, _i64, _i64, _i64, _i32, _i32, _p, _i64, _p, _p], ctypes.c_int),
     "ck_test_rotate_f32": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p], ctypes.c_int),
     "ck_test_gemm_i32": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
-    "ck_test_rotate_quant4_packed": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _p], ctypes.c_int),
+    "ck_rotate_quant_packed4": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _p], ctypes.c_int),
+    "ck_w4a4_gemm_packed": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i32, _i64, _p, _p, _i64, _p],
+                            ctypes.c_int),
     "ck_test_gemm_i32_a4": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
 
@@ -171,6 +174,24 @@ def rotate_quant(x, G: int, bits: int, codes=None, row_scales=None):
     return codes, row_scales
 
 
+def quantize_weights(w, G: int, per_group: bool, packed=None, scales=None):
+    """Packed uint4 weights uint8 [N, K/2] and bf16 scales ([N] or [K/64, N]) of a
+    bf16 weight [N, K] rotated by H_G: the producer of the matmuls' weight format."""
+    _matrix(w, "w", (torch.bfloat16,))
+    N, K = w.shape
+    if packed is None:
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        shape = (K // 64, N) if per_group else (N,)
+        scales = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
+    _out(packed, "packed", torch.uint8, N, K // 2)
+    _dense(scales, "scales", torch.bfloat16, (K // 64, N) if per_group else (N,))
+    _same_device(w, ("packed", packed), ("scales", scales))
+    _check(lib.ck_quantize_weights(_ptr(w), N, K, _ld(w), G, 1 if per_group else 0, _ptr(packed),
+                                   _ld(packed), _ptr(scales), _stream(w)))
+    return packed, scales
+
+
 def rotated_f32(x, G: int):
     """Rotated rows as the rotate-quant kernel holds them (divided by sqrt(G)), fp32 [M, K]."""
     _matrix(x, "x", (torch.bfloat16,))
@@ -260,16 +281,41 @@ def w4a16_gemv(x, packed, scales, zeros, bias=None, out=None):
     return out
 
 
-def rotate_quant4_packed(x, G: int):
+def rotate_quant_packed4(x, G: int, codes4=None, row_scales=None):
     """W4A4 codes packed two per byte, uint8 [M, K/2] (column 2j in the low
     nibble, 4-bit two's complement), and fp32 row scales [M]."""
     _matrix(x, "x", (torch.bfloat16,))
     M, K = x.shape
-    codes4 = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-    row_scales = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _check(lib.ck_test_rotate_quant4_packed(_ptr(x), M, K, _ld(x), G, _ptr(codes4), _ld(codes4),
-                                            _ptr(row_scales), _stream(x)))
+    if codes4 is None:
+        codes4 = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if row_scales is None:
+        row_scales = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _out(codes4, "codes4", torch.uint8, M, K // 2)
+    _dense(row_scales, "row_scales", torch.float32, (M,))
+    _same_device(x, ("codes4", codes4), ("row_scales", row_scales))
+    _check(lib.ck_rotate_quant_packed4(_ptr(x), M, K, _ld(x), G, _ptr(codes4), _ld(codes4),
+                                       _ptr(row_scales), _stream(x)))
     return codes4, row_scales
+
+
+def gemm_packed4(codes4, row_scales, packed, w_scales, per_group: bool, bias=None, out=None):
+    """bf16 [M, N] linear output from packed W4A4 codes (rotate_quant_packed4) on the tiled GEMM."""
+    _matrix(codes4, "codes4", (torch.uint8,))
+    M = codes4.shape[0]
+    K = 2 * codes4.shape[1]
+    N = _weights(packed, w_scales, per_group, K)
+    _dense(row_scales, "row_scales", torch.float32, (M,))
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=codes4.device)
+    _out(out, "out", torch.bfloat16, M, N)
+    _same_device(codes4, ("row_scales", row_scales), ("packed", packed), ("w_scales", w_scales),
+                 ("bias", bias), ("out", out))
+    _check(lib.ck_w4a4_gemm_packed(_ptr(codes4), _ld(codes4), _ptr(row_scales), M, K, _ptr(packed),
+                                   _ld(packed), _ptr(w_scales), 1 if per_group else 0, 64, N, _ptr(bias),
+                                   _ptr(out), _ld(out), _stream(codes4)))
+    return out
 
 
 def accumulators_i32_a4(codes4, K: int, packed):

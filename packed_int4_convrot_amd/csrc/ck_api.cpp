@@ -377,6 +377,37 @@ int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_
     return hip_status(e, fn);
 }
 
+int ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
+                        int32_t scale_kind, uint8_t *packed, int64_t ldp, uint16_t *scales, void *stream)
+{
+    const char *fn = "ck_quantize_weights";
+    if (N < 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: N must be >= 0 (got %lld)", fn, (long long)N);
+    if (N > kMaxRows)
+        return fail(CK_ERR_UNSUPPORTED, "%s: N above %lld", fn, (long long)kMaxRows);
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_g(fn, G, K));
+    if (scale_kind != CK_WS_PER_CHANNEL && scale_kind != CK_WS_PER_GROUP)
+        return fail(CK_ERR_INVALID_ARG, "%s: unknown weight-scale kind %d", fn, scale_kind);
+    if (N == 0)
+        return ok();
+    if (!w || ldw_in < K || ldw_in % 8 != 0 || !aligned(w, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: w must be non-NULL and 16-byte aligned with ldw_in >= K, "
+                    "ldw_in %% 8 == 0", fn);
+    if (!packed || ldp < K / 2 || ldp % 16 != 0 || !aligned(packed, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: packed must be non-NULL and 16-byte aligned with ldp >= K/2, "
+                    "ldp %% 16 == 0", fn);
+    if (!scales || !aligned(scales, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: scales must be a non-NULL 2-byte aligned pointer", fn);
+    const bool pg = scale_kind == CK_WS_PER_GROUP;
+    const Range rw = span(w, N, K, ldw_in, 2), rp = span(packed, N, K / 2, ldp, 1);
+    const Range rs = pg ? span(scales, K / 64, N, N, 2) : span(scales, 1, N, N, 2);
+    if (overlap(rw, rp) || overlap(rw, rs) || overlap(rp, rs))
+        return fail(CK_ERR_INVALID_ARG, "%s: w, packed and scales must not overlap", fn);
+    const int e = ck::launch_quantize_weights(w, N, (int)K, ldw_in, G, pg, packed, ldp, scales, stream);
+    return hip_status(e, fn);
+}
+
 int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, float *xr,
                        int64_t ldr, void *stream)
 {
@@ -396,10 +427,10 @@ int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int
     return hip_status(e, fn);
 }
 
-int ck_test_rotate_quant4_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+int ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                                  uint8_t *codes4, int64_t ldq, float *row_scales, void *stream)
 {
-    const char *fn = "ck_test_rotate_quant4_packed";
+    const char *fn = "ck_rotate_quant_packed4";
     CK_TRY(check_m(fn, M));
     CK_TRY(check_k(fn, K));
     CK_TRY(check_g(fn, G, K));
@@ -424,6 +455,32 @@ int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int6
 {
     const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
     return gemm_q_common("ck_w4_gemm_q", false, codes, ldq, row_scales, M, K, w, bias, out, ldo, stream);
+}
+
+int ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t M,
+                        int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                        int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                        uint16_t *out, int64_t ldo, void *stream)
+{
+    const char *fn = "ck_w4a4_gemm_packed";
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    CK_TRY(check_weights(fn, w, K, true));
+    if (M == 0)
+        return ok();
+    CK_TRY(check_codes(fn, codes4, K / 2, ldq));
+    if (!row_scales || !aligned(row_scales, 4))
+        return fail(CK_ERR_INVALID_ARG, "%s: row_scales must be a non-NULL 4-byte aligned pointer", fn);
+    if (bias && !aligned(bias, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
+    CK_TRY(check_out(fn, out, N, ldo, 2));
+    const Range ro = span(out, M, N, ldo, 2);
+    if (overlap(ro, span(codes4, M, K / 2, ldq, 1)) || overlap(ro, span(row_scales, 1, M, M, 4)) ||
+        overlap(ro, span(packed, N, K / 2, ldw, 1)) || overlap(ro, scales_span(w, K)) ||
+        overlap(ro, span(bias, 1, N, N, 2)))
+        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    return run_gemm(fn, codes4, ldq, row_scales, M, K, w, bias, 1.0f, out, ldo, nullptr, 0, true, stream);
 }
 
 int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,

@@ -11,6 +11,12 @@ int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
                         bool packed4, void *stream);
 
+// Offline weight producer: rotate N bf16 weight rows of K columns by H_G,
+// quantise to codes in [-7, 7] with bf16 scales per row (per_group false) or
+// per 64-column group ([K/64, N]), and pack q = code + 8 two per byte.
+int launch_quantize_weights(const uint16_t *w, int64_t N, int K, int64_t ldw_in, int G, bool per_group,
+                            uint8_t *packed, int64_t ldp, uint16_t *scales, void *stream);
+
 // Decode GEMV for 1 <= M <= 8 (VALU dot4, 1 KiB coalesced weight rows).  With
 // G != 0 (M = 1) it rotates and quantises the bf16 row x itself (fused linear); with
 // G == 0 it reads given codes and row_scales.  acc_out != nullptr (G == 0

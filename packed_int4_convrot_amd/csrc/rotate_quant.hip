@@ -111,14 +111,34 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 }
 
 // Output of the kernel: int8 codes (one per byte), the rotated fp32 values
-// (test hook), or W4A4 codes packed two per byte (4-bit two's complement,
-// column 2j in bits 0..3), which halves the codes traffic of the W4A4 GEMM.
-enum OutMode { kCodes8 = 0, kF32 = 1, kPacked4 = 2 };
+// (test hook), W4A4 codes packed two per byte (4-bit two's complement,
+// column 2j in bits 0..3), which halves the codes traffic of the W4A4 GEMM,
+// or packed weights (stored code q = value + 8) with bf16 scales per row or
+// per 64-column group.
+enum OutMode { kCodes8 = 0, kF32 = 1, kPacked4 = 2, kWeightRow = 3, kWeightGroup = 4 };
+
+// Weight quantisation of rotated values y = sqrt(G) * wr (see the launcher):
+// scale s = bf16(fp32(a / 7)) for the absmax a of wr over the scale group,
+// code = clamp(rne(fp32(wr * fp32(1 / s))), -7, 7).  am is max|y|.
+struct WeightScale {
+    float inv_y;     // fp32(1 / s) / sqrt(G): y * inv_y == wr * fp32(1 / s) exactly
+    uint16_t bits;   // s as bf16
+};
+template <int G>
+__device__ __forceinline__ WeightScale weight_scale(float am)
+{
+    constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
+    const float a = am * kInvSqrtG;
+    const uint16_t sb = f32_to_bf16(a / 7.0f);
+    const float sf = bf16_to_f32(sb);
+    return WeightScale{sf > 0.f ? (1.0f / sf) * kInvSqrtG : 0.f, sb};
+}
 
 template <int G, int BLOCK, int CPT, int MODE>
 __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int K, float qmax, int8_t *__restrict__ codes,
-    int64_t ldq, float *__restrict__ row_scales, float *__restrict__ xr, int64_t ldr)
+    int64_t ldq, float *__restrict__ row_scales, float *__restrict__ xr, int64_t ldr,
+    uint16_t *__restrict__ wscales, int64_t ldsc)
 {
     constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
     static_assert(G == 16 || G == 64 || G == 256, "G");
@@ -164,7 +184,42 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     for (int w = 1; w < BLOCK / kWave; ++w)
         am = fmaxf(am, wmax[w]);
 
-    if constexpr (MODE == kF32) {
+    if constexpr (MODE == kWeightRow || MODE == kWeightGroup) {
+        // Packed weights: byte j of a row = q(2j) | q(2j + 1) << 4, q = code + 8.
+        WeightScale ws = weight_scale<G>(am);
+        uint8_t *prow = reinterpret_cast<uint8_t *>(codes) + m * ldq;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = t + i * BLOCK;
+            if constexpr (MODE == kWeightGroup) {
+                // A 64-column group is 8 chunks held by 8 neighbouring lanes.
+                float gm = 0.f;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    gm = fmaxf(gm, fabsf(v[i][r]));
+                gm = fmaxf(gm, lane_xor<1>(gm));
+                gm = fmaxf(gm, lane_xor<2>(gm));
+                gm = fmaxf(gm, lane_xor<4>(gm));
+                ws = weight_scale<G>(gm);
+                if (c < nchunk && (c & 7) == 0)
+                    wscales[(int64_t)(c >> 3) * ldsc + m] = ws.bits;
+            }
+            uint32_t b[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                b[r] = rne_byte(fminf(fmaxf(v[i][r] * ws.inv_y, -7.f), 7.f));
+            if (c < nchunk) {
+                const uint32_t ev = pack4(b[0], b[2], b[4], b[6]);
+                const uint32_t od = pack4(b[1], b[3], b[5], b[7]);
+                // two's-complement nibble ^ 8 = value + 8
+                reinterpret_cast<uint32_t *>(prow)[c] =
+                    ((ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u)) ^ 0x88888888u;
+            }
+        }
+        if constexpr (MODE == kWeightRow)
+            if (t == 0)
+                wscales[m] = ws.bits;
+    } else if constexpr (MODE == kF32) {
         float *orow = xr + m * ldr;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
@@ -211,7 +266,8 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 // the row stays in VGPRs without spilling: 8 at 256 threads, 4 at 1024.
 template <int G, int BLOCK, int MODE>
 hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_t ldx, int K,
-                    float qmax, int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr)
+                    float qmax, int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr,
+                    uint16_t *wsc, int64_t ldsc)
 {
     constexpr int kMaxCpt = BLOCK >= 1024 ? 4 : 8;
     if (cpt < 1 || cpt > kMaxCpt)
@@ -220,7 +276,7 @@ hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_
     case C:                                                                                   \
         if constexpr (C <= kMaxCpt)                                                           \
             hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE>), grid, dim3(BLOCK), 0, \
-                               s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);                  \
+                               s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);       \
         break;
     switch (cpt) {
         CK_RQ_CASE(1)
@@ -240,16 +296,17 @@ hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_
 
 template <int G, int MODE>
 hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t ldx, float qmax,
-                     int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr)
+                     int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr,
+                     uint16_t *wsc = nullptr, int64_t ldsc = 0)
 {
     const int nchunk = K / 8;
     const dim3 grid((unsigned)M);
     if (nchunk <= 256 * 8) {
         const int cpt = (nchunk + 255) / 256;
-        return launch_g<G, 256, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
+        return launch_g<G, 256, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
     }
     const int cpt = (nchunk + 1023) / 1024;
-    return launch_g<G, 1024, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr);
+    return launch_g<G, 1024, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
 }
 
 }  // namespace
@@ -277,6 +334,27 @@ int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G,
         CK_RQ_G(kCodes8)
     }
 #undef CK_RQ_G
+}
+
+int launch_quantize_weights(const uint16_t *w, int64_t N, int K, int64_t ldw_in, int G, bool per_group,
+                            uint8_t *packed, int64_t ldp, uint16_t *scales, void *stream)
+{
+    if (N <= 0)
+        return 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int8_t *dst = reinterpret_cast<int8_t *>(packed);
+#define CK_WQ_G(MODE)                                                                                     \
+    switch (G) {                                                                                        \
+    case 16: return (int)launch_rq<16, MODE>(N, K, s, w, ldw_in, 7.f, dst, ldp, nullptr, nullptr, 0, scales, N);  \
+    case 64: return (int)launch_rq<64, MODE>(N, K, s, w, ldw_in, 7.f, dst, ldp, nullptr, nullptr, 0, scales, N);  \
+    default: return (int)launch_rq<256, MODE>(N, K, s, w, ldw_in, 7.f, dst, ldp, nullptr, nullptr, 0, scales, N); \
+    }
+    if (per_group) {
+        CK_WQ_G(kWeightGroup)
+    } else {
+        CK_WQ_G(kWeightRow)
+    }
+#undef CK_WQ_G
 }
 
 }  // namespace ck

@@ -154,10 +154,41 @@ def test_awq_rejects():
     assert f(P, 1, 256, 256, P3, 128, P4, P2 + 8, 64, 64, None, P5, 64, None) == ck.CK_ERR_INVALID_ARG
 
 
+def test_gemm_packed4_rejects():
+    f = lib.ck_w4a4_gemm_packed
+    ok = dict(c=P, ldq=128, rs=P2, M=4, K=256, w=P3, ldw=128, s=P4, kind=0, Gw=64, N=64, b=None, o=P5, ldo=64)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["c"], a["ldq"], a["rs"], a["M"], a["K"], a["w"], a["ldw"], a["s"], a["kind"], a["Gw"], a["N"],
+                 a["b"], a["o"], a["ldo"], None)
+    assert call(ldq=112) == ck.CK_ERR_INVALID_ARG        # ldq < K/2
+    assert call(rs=None) == ck.CK_ERR_INVALID_ARG
+    assert call(N=40) == ck.CK_ERR_UNSUPPORTED
+    assert call(o=P + 64) == ck.CK_ERR_INVALID_ARG       # output overlaps the codes
+    assert call(ldo=32) == ck.CK_ERR_INVALID_ARG
+    assert call(M=0, c=None, rs=None, o=None) == ck.CK_OK
+
+
+def test_quantize_weights_rejects():
+    f = lib.ck_quantize_weights
+    assert f(P, 4, 256, 256, 32, 0, P2, 128, P3, None) == ck.CK_ERR_UNSUPPORTED     # G
+    assert f(P, 4, 320, 320, 256, 0, P2, 160, P3, None) == ck.CK_ERR_INVALID_ARG    # K % G
+    assert f(P, 4, 256, 256, 64, 2, P2, 128, P3, None) == ck.CK_ERR_INVALID_ARG     # scale kind
+    assert f(P, 4, 256, 200, 64, 0, P2, 128, P3, None) == ck.CK_ERR_INVALID_ARG     # ldw_in < K
+    assert f(P + 8, 4, 256, 256, 64, 0, P2, 128, P3, None) == ck.CK_ERR_INVALID_ARG
+    assert f(P, 4, 256, 256, 64, 0, P2, 120, P3, None) == ck.CK_ERR_INVALID_ARG     # ldp < K/2
+    assert f(P, 4, 256, 256, 64, 0, P2, 136, P3, None) == ck.CK_ERR_INVALID_ARG     # ldp % 16
+    assert f(P, 4, 256, 256, 64, 0, P2, 128, None, None) == ck.CK_ERR_INVALID_ARG
+    assert f(P, 4, 256, 256, 64, 0, P + 64, 128, P3, None) == ck.CK_ERR_INVALID_ARG  # overlaps w
+    assert f(P, 4, 256, 256, 64, 1, P2, 128, P2 + 256, None) == ck.CK_ERR_INVALID_ARG  # scales overlap packed
+    assert f(P, -1, 256, 256, 64, 0, P2, 128, P3, None) == ck.CK_ERR_INVALID_ARG
+    assert f(None, 0, 256, 256, 64, 0, None, 128, None, None) == ck.CK_OK
+
+
 def test_test_hooks_reject():
     assert lib.ck_test_rotate_f32(P, 4, 256, 256, 64, P2 + 4, 256, None) == ck.CK_ERR_INVALID_ARG
     assert lib.ck_test_gemm_i32(P, 256, 4, 256, P3, 128, 64, P3, 64, None) == ck.CK_ERR_INVALID_ARG
-    f = lib.ck_test_rotate_quant4_packed
+    f = lib.ck_rotate_quant_packed4
     assert f(P, 4, 256, 256, 64, P2, 112, P3, None) == ck.CK_ERR_INVALID_ARG   # ldq < K/2
     assert f(P, 4, 256, 256, 64, P2, 136, P3, None) == ck.CK_ERR_INVALID_ARG   # ldq % 16
     assert f(P, 4, 256, 256, 64, P2 + 8, 128, P3, None) == ck.CK_ERR_INVALID_ARG

@@ -152,7 +152,7 @@ def test_packed_w4a4_codes_equal_byte_codes(G, M, K):
     """The packed store of rotate-quant holds exactly the bits=4 codes and scales."""
     x = workloads.activations(M, K, seed=G + M, outliers=max(1, K // 100), zero_rows=(0,))
     xd = bf16_dev(x)
-    codes4, s4 = ck.rotate_quant4_packed(xd, G)
+    codes4, s4 = ck.rotate_quant_packed4(xd, G)
     codes, s = ck.rotate_quant(xd, G, 4)
     assert np.array_equal(_unpack_nibbles(host(codes4)), host(codes))
     assert np.array_equal(host(s4), host(s))
@@ -164,7 +164,7 @@ def test_packed_w4a4_codes_strided_input():
     M, K, ld = 9, 1024, 1152  # padding columns hold NaN
     x = workloads.activations(M, K, seed=6, outliers=10, ld=ld)
     xd = bf16_dev(x)[:, :K]
-    c1, s1 = ck.rotate_quant4_packed(xd, 64)
+    c1, s1 = ck.rotate_quant_packed4(xd, 64)
     c2, s2 = ck.rotate_quant(bf16_dev(np.ascontiguousarray(x[:, :K])), 64, 4)
     assert np.array_equal(_unpack_nibbles(host(c1)), host(c2)) and np.array_equal(host(s1), host(s2))
 
@@ -192,6 +192,36 @@ def test_accumulators_a4_extremes():
     ref = oracle.int_gemm(codes, oracle.unpack(packed))
     assert np.array_equal(acc.astype(np.int64), ref)
     assert np.abs(ref).max() == 7 * 8 * K
+
+
+@pytest.mark.parametrize("per_group", [True, False])
+@pytest.mark.parametrize("M", [1, 7, 64, 257])
+def test_gemm_packed4_matches_oracle(M, per_group):
+    """ck_w4a4_gemm_packed at every M (the tiled GEMM on packed codes) against the
+    oracle epilogue on the same codes and scales."""
+    K, N = 1280, 272
+    inp = workloads.linear_inputs(M, K, N, seed=M + 17, outliers=13, scale="group" if per_group else "channel",
+                                  zero_rows=(M - 1,) if M > 2 else (), with_bias=(M % 2 == 1))
+    codes4, rs = ck.rotate_quant_packed4(bf16_dev(inp["x"]), 64)
+    bias = None if inp["bias"] is None else bf16_dev(inp["bias"])
+    out = host(ck.gemm_packed4(codes4, rs, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), per_group, bias=bias))
+    ref = oracle.gemm_q(_unpack_nibbles(host(codes4)), host(rs), inp["packed"], inp["w_scales"], per_group,
+                        bias=inp["bias"])
+    assert_output_close(out, ref)
+
+
+def test_activation_cache_reuses_packed_codes():
+    """One packed rotate-quant serves several linears on the same input (Q, K, V-like
+    weights of different widths): each result is bit-identical to its own whole linear."""
+    M, K, G = 300, 2304, 256
+    x = bf16_dev(workloads.activations(M, K, seed=4, outliers=23))
+    codes4, rs = ck.rotate_quant_packed4(x, G)
+    for i, N in enumerate((384, 128, 128)):
+        w = workloads.linear_inputs(1, K, N, seed=40 + i, outliers=1, scale="channel")
+        wd, sd = u8_dev(w["packed"]), bf16_dev(w["w_scales"])
+        cached = ck.gemm_packed4(codes4, rs, wd, sd, False)
+        whole = ck.linear(x, G, 4, wd, sd, False)
+        assert torch.equal(cached.view(torch.int16), whole.view(torch.int16))
 
 
 @pytest.mark.parametrize("per_group", [True, False])
@@ -404,3 +434,84 @@ def test_awq_gemv_matches_oracle(M, K, N):
                         bias=None if d["bias"] is None else bf16_dev(d["bias"]))
     ref = oracle.awq_gemv(d["x"], d["packed"], d["scales"], d["zeros"], bias=d["bias"])
     assert_output_close(host(out), ref)
+
+
+# ------------------------------------------------------ weight producer
+
+
+def _weights_bf16(N, K, seed, zero_rows=()):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((N, K)) * rng.uniform(0.005, 0.05, size=(N, 1))
+    w[:, rng.choice(K, max(1, K // 100), replace=False)] *= 8.0   # a few heavy input channels
+    for r in zero_rows:
+        w[r] = 0.0
+    return workloads.to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+@pytest.mark.parametrize("G", [16, 64, 256])
+def test_quantize_weights_bit_exact_given_rotation(G, per_group):
+    """Packed codes and bf16 scales equal the oracle's quantiser applied to the
+    kernel's own rotated values (ck_test_rotate_f32 runs the same rotation)."""
+    N, K = 272, 3840
+    w = _weights_bf16(N, K, seed=G + per_group, zero_rows=(5,))
+    wd = bf16_dev(w)
+    packed, scales = ck.quantize_weights(wd, G, per_group)
+    wr = host(ck.rotated_f32(wd, G))
+    ref_p, ref_s = oracle.quantize_weights(wr, per_group)
+    assert np.array_equal(host(packed), ref_p)
+    assert np.array_equal(host(scales.view(torch.int16)).view(np.uint16), ref_s)
+    assert (host(packed)[5] == 0x88).all()
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+@pytest.mark.parametrize("G", [16, 64, 256])
+def test_quantize_weights_matches_oracle(G, per_group):
+    """Against the oracle's exact rotation: codes agree to the rotation-codes bar, scales
+    within one bf16 step (the absmax can differ by an fp32 rounding)."""
+    N, K = 300, 2304
+    w = _weights_bf16(N, K, seed=3 * G + per_group)
+    packed, scales = ck.quantize_weights(bf16_dev(w), G, per_group)
+    ref_p, ref_s = oracle.rotate_quantize_weights(w, G, per_group)
+    assert_codes_close(oracle.unpack(host(packed)), oracle.unpack(ref_p))
+    s = host(scales.view(torch.int16)).view(np.uint16).astype(np.int32)
+    assert np.abs(s - ref_s.astype(np.int32)).max() <= 1
+    assert (s == ref_s).mean() >= 0.99
+
+
+def test_quantize_weights_strided_input_and_small_shapes():
+    K, ld = 256, 320                       # padding columns hold NaN
+    w = np.full((17, ld), 0x7FC0, dtype=np.uint16)
+    w[:, :K] = _weights_bf16(17, K, seed=1)
+    wd = bf16_dev(w)[:, :K]
+    for G in (16, 64, 256):
+        for pg in (False, True):
+            p1, s1 = ck.quantize_weights(wd, G, pg)
+            p2, s2 = ck.quantize_weights(bf16_dev(np.ascontiguousarray(w[:, :K])), G, pg)
+            assert torch.equal(p1, p2) and torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+    p, s = ck.quantize_weights(bf16_dev(_weights_bf16(3, 64, seed=2)), 16, True)
+    assert tuple(p.shape) == (3, 32) and tuple(s.shape) == (1, 3)
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+def test_produced_weights_run_the_linear(per_group):
+    """Weights from the producer feed the linear unchanged: the GPU linear matches the
+    oracle epilogue on them, and approximates the unquantised x . W^T."""
+    M, N, K, G = 96, 400, 1536, 64
+    w = _weights_bf16(N, K, seed=9)
+    x = workloads.activations(M, K, seed=9, outliers=15)
+    packed, scales = ck.quantize_weights(bf16_dev(w), G, per_group)
+    xd = bf16_dev(x)
+    out = host(ck.linear(xd, G, 8, packed, scales, per_group))
+    codes, rs = ck.rotate_quant(xd, G, 8)
+    ref = oracle.gemm_q(host(codes), host(rs), host(packed), host(scales.view(torch.int16)).view(np.uint16),
+                        per_group)
+    assert_output_close(out, ref)
+    # quantisation error of the whole path: as small as with the oracle's own weights
+    exact = workloads.bf16_bits_to_f32(x).astype(np.float64) @ workloads.bf16_bits_to_f32(w).astype(np.float64).T
+    ref_p, ref_s = oracle.rotate_quantize_weights(w, G, per_group)
+    oracle_out, _, _ = oracle.linear(x, G, 8, ref_p, ref_s, per_group)
+    err_gpu = np.linalg.norm(out - exact)
+    err_oracle = np.linalg.norm(oracle_out - exact)
+    assert err_oracle / np.linalg.norm(exact) < 0.3
+    assert err_gpu <= 1.05 * err_oracle

@@ -298,3 +298,93 @@ def test_awq_matches_numpy_brute_force():
     ref = _f32(d["x"]).astype(np.float64) @ W.T + _f32(d["bias"])
     np.testing.assert_allclose(oracle.awq_gemv(d["x"], d["packed"], d["scales"], d["zeros"], bias=d["bias"]),
                                ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------- weight quantiser
+
+
+def _impulse_rows(d):
+    w = np.zeros((len(d["impulses"]), d["K"]), dtype=np.float64)
+    for r, c, v in d["impulses"]:
+        w[r, c] = v
+    return _bf16(w)
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+def test_weight_quant_golden(per_group):
+    d = _golden("weight_quant.json")
+    packed, scales = oracle.rotate_quantize_weights(_impulse_rows(d), d["G"], per_group)
+    want = np.array([list(bytes.fromhex(h)) for h in d["packed_rows_hex"]], dtype=np.uint8)
+    assert np.array_equal(packed, want)
+    ref = d["scales_per_group"] if per_group else d["scales_per_channel"]
+    assert np.array_equal(scales, np.array([[int(v, 16) for v in r] for r in ref] if per_group
+                                           else [int(v, 16) for v in ref], dtype=np.uint16))
+
+
+def _unpacked(packed):
+    return oracle.unpack(packed).astype(np.int64)
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+def test_weight_quant_exact_round_trip(per_group):
+    """Rotated weights that are exactly code * s (s a bf16 value, every group holding a
+    +-7) come back as those codes and that scale."""
+    rng = np.random.default_rng(5)
+    N, K, Gw = 7, 256, 64
+    ng = K // Gw if per_group else 1
+    glen = Gw if per_group else K
+    codes = rng.integers(-7, 8, size=(N, K))
+    codes[:, ::glen] = np.where(rng.random((N, K // glen)) < 0.5, -7, 7)  # the absmax in every group
+    s_bits = _bf16(rng.uniform(1e-3, 3.0, size=(N, ng)))
+    s = _f32(s_bits).astype(np.float64)
+    wr = (codes * np.repeat(s, glen, axis=1)).astype(np.float32)
+    assert np.array_equal(wr.astype(np.float64), codes * np.repeat(s, glen, axis=1))  # exact in fp32
+    packed, scales = oracle.quantize_weights(wr, per_group, Gw)
+    assert np.array_equal(_unpacked(packed), codes)
+    assert np.array_equal(scales, s_bits.T if per_group else s_bits[:, 0])
+
+
+@pytest.mark.parametrize("per_group", [False, True])
+def test_weight_quant_error_bound_and_range(per_group):
+    """Every value lands within half a step of code * s; the group absmax maps to +-7;
+    stored codes are 1..15 (never 0); an all-zero group gets scale 0 and code 0."""
+    rng = np.random.default_rng(11)
+    N, K, Gw = 9, 512, 64
+    wr = (rng.standard_normal((N, K)) * rng.uniform(0.01, 10.0, size=(N, 1))).astype(np.float32)
+    wr[3] = 0.0
+    wr[4, :Gw] = 0.0
+    packed, scales = oracle.quantize_weights(wr, per_group, Gw)
+    q = oracle.unpack(packed).astype(np.int64) + 8
+    assert q.min() >= 1 and q.max() <= 15
+    glen = Gw if per_group else K
+    s = _f32(scales.T if per_group else scales[:, None]).astype(np.float64)
+    s_full = np.repeat(s, glen, axis=1)
+    codes = q - 8
+    err = np.abs(wr.astype(np.float64) - codes * s_full)
+    assert (err <= 0.5 * s_full * (1 + 1e-6) + 1e-30).all()
+    a = np.abs(wr).reshape(N, K // glen, glen).max(-1)
+    c = np.abs(codes).reshape(N, K // glen, glen).max(-1)
+    assert (c[a > 0] == 7).all() and (c[a == 0] == 0).all()
+    assert (s[a == 0] == 0).all() and (s[a > 0] > 0).all()
+    # scale is the bf16 rounding of a / 7: within half a bf16 step
+    assert (np.abs(s[a > 0] - a[a > 0] / 7.0) <= 2.0 ** -8 * a[a > 0] / 7.0 * 1.0001).all()
+
+
+@pytest.mark.parametrize("G", [16, 64, 256])
+@pytest.mark.parametrize("per_group", [False, True])
+def test_weight_producer_gives_the_linear_of_w(G, per_group):
+    """Rotating both sides by the same H_G leaves x . W^T unchanged, so the linear with
+    produced weights approximates the unquantised product; pairing weights rotated
+    with one G and activations rotated with another does not."""
+    rng = np.random.default_rng(G)
+    M, N, K = 6, 48, 512
+    x = _bf16(rng.standard_normal((M, K)))
+    W = _bf16(rng.standard_normal((N, K)) * 0.05)
+    ref = _f32(x).astype(np.float64) @ _f32(W).astype(np.float64).T
+    packed, scales = oracle.rotate_quantize_weights(W, G, per_group)
+    out, _, _ = oracle.linear(x, G, 8, packed, scales, per_group)
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 0.15, rel
+    other = 16 if G != 16 else 64
+    bad, _, _ = oracle.linear(x, other, 8, packed, scales, per_group)
+    assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 0.5
