@@ -230,6 +230,26 @@ int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   uint16_t *out, int64_t ldo, void *stream);
 
 /*
+ * ck_w4a16_gemm  [AWQ]
+ * AWQ W4A16 product for any number of rows (prefill), on the page's
+ * dequantise path (dequantize(), used when no quantised kernel runs): the
+ * weight is rebuilt in bf16 one tensor operation at a time,
+ *   W[n,k]   = bf16( bf16((q[n,k] - 8) * scales[k/Gw, n]) + zeros[k/Gw, n] ),
+ *   out[m,n] = sum_k x[m,k] * W[n,k]  (+ bias[n]), fp32 accumulation, bf16 out.
+ * The rebuilt weight lives only in registers.  It differs from ck_w4a16_gemv
+ * (which keeps W exact) by W's bf16 rounding.
+ *   x       bf16 [M, ldx], ldx <= 2^22, any M >= 0
+ *   packed  uint8 [N, ldw] as in ck_w4_gemm_q; N % 16 == 0
+ *   scales, zeros  bf16 [K/Gw, N], Gw = 64, 2-byte aligned
+ *   bias    bf16 [N] or NULL;  out bf16 [M, ldo] (16-byte aligned rows)
+ */
+int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                  const uint8_t *packed, int64_t ldw, const uint16_t *scales,
+                  const uint16_t *zeros, int32_t Gw, int64_t N, const uint16_t *bias,
+                  uint16_t *out, int64_t ldo, void *stream);
+
+/*
+ * ck_quantize_weights/*
  * ck_quantize_weights  [SD] [AWQ]
  * Offline producer of the packed weights the matmuls consume, for a bf16
  * weight W [N, K] (row n = output column n):

@@ -58,6 +58,8 @@ def _load():
             "oracle_epilogue": [p, i64, i64, i64, p, p, i32, p, p],
             "oracle_awq_gemv": [p, i64, i64, i64, p, i64, p, p, i64, i64, p, p],
             "oracle_quantize_weights": [p, i64, i64, i64, i32, p, i64, p],
+            "oracle_awq_dequantize": [p, i64, i64, i64, p, p, i64, p],
+            "oracle_bf16_matmul": [p, i64, i64, i64, p, i64, i64, p, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -203,3 +205,36 @@ def awq_gemv(x, packed, scales, zeros, Gw: int = 64, bias=None, K: int | None = 
     _check(_load().oracle_awq_gemv(_ptr(x), M, K, ldx, _ptr(packed), ldw, _ptr(s), _ptr(z), Gw, N,
                                    _ptr(b), _ptr(out)), "awq_gemv")
     return out
+
+
+def awq_dequantize(packed, scales, zeros, Gw: int = 64, K: int | None = None) -> np.ndarray:
+    """bf16 bits [N, K]: the AWQ weight rebuilt as the page's dequantize() does (each
+    tensor operation rounded to bf16)."""
+    packed = np.ascontiguousarray(np.asarray(packed).view(np.uint8))
+    N, ldw = packed.shape
+    K = 2 * ldw if K is None else K
+    s = _u16(scales)
+    z = _u16(zeros)
+    w = np.empty((N, K), dtype=np.uint16)
+    _check(_load().oracle_awq_dequantize(_ptr(packed), N, K, ldw, _ptr(s), _ptr(z), Gw, _ptr(w)),
+           "awq_dequantize")
+    return w
+
+
+def bf16_matmul(x, w, bias=None) -> np.ndarray:
+    """fp64 [M, N] = x . w^T (+ bias) for bf16 x [M, K] and w [N, K]."""
+    x = _u16(x)
+    w = _u16(w)
+    M, K = x.shape
+    N = w.shape[0]
+    b = None if bias is None else _u16(bias)
+    out = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_bf16_matmul(_ptr(x), M, K, K, _ptr(w), N, w.shape[1], _ptr(b), _ptr(out)),
+           "bf16_matmul")
+    return out
+
+
+def awq_gemm(x, packed, scales, zeros, Gw: int = 64, bias=None) -> np.ndarray:
+    """fp64 [M, N] AWQ product on the dequantised bf16 weight (the prefill path)."""
+    x = _u16(x)
+    return bf16_matmul(x, awq_dequantize(packed, scales, zeros, Gw, x.shape[1]), bias)

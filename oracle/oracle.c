@@ -321,3 +321,50 @@ int oracle_awq_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
     }
     return OK;
 }
+
+/*
+ * The dequantise path of "comfy_kitchen/tensor/awq_w4a16.py", dequantize():
+ * the weight is rebuilt in the bf16 compute dtype, one tensor operation at a
+ * time, so each product and each sum is rounded to bf16 (nearest even):
+ *   W[n, k] = bf16( bf16((q - 8) * s[k/Gw, n]) + z[k/Gw, n] )
+ * (each operation computed in fp32 first, as a bf16 tensor operation does;
+ * (q - 8) * s is exact in fp32).  W is written as bf16 bits [N, K].
+ */
+int oracle_awq_dequantize(const uint8_t *packed, int64_t N, int64_t K, int64_t ldw,
+                          const uint16_t *scales, const uint16_t *zeros, int64_t Gw,
+                          uint16_t *w)
+{
+    if (!packed || !scales || !zeros || !w || N < 0 || K < 0 || K % 2 != 0 ||
+        ldw < K / 2 || Gw <= 0 || K % Gw != 0)
+        return BAD_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t b = packed[n * ldw + k / 2];
+            const int q = (k % 2 == 0) ? (b & 0x0F) : (b >> 4);
+            const float sc = (float)bf16_value(scales[(k / Gw) * N + n]);
+            const float zp = (float)bf16_value(zeros[(k / Gw) * N + n]);
+            const float prod = (float)(q - 8) * sc;
+            const float sum = (float)bf16_value(bf16_round(prod)) + zp;
+            w[n * K + k] = bf16_round(sum);
+        }
+    return OK;
+}
+
+/* out[m, n] = sum_k x[m, k] * w[n, k] (+ bias[n]) in fp64, x and w bf16. */
+int oracle_bf16_matmul(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                       const uint16_t *w, int64_t N, int64_t ldw, const uint16_t *bias,
+                       double *out)
+{
+    if (!x || !w || !out || M < 0 || N < 0 || K < 0 || ldx < K || ldw < K)
+        return BAD_ARG;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double t = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                t += bf16_value(x[m * ldx + k]) * bf16_value(w[n * ldw + k]);
+            if (bias)
+                t += bf16_value(bias[n]);
+            out[m * N + n] = t;
+        }
+    return OK;
+}

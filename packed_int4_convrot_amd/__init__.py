@@ -43,6 +43,8 @@ SIGNATURES = {
                         _i64, _p, _sz, _p], ctypes.c_int),
     "ck_w4a16_gemv": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _i64, _p, _p, _i64, _p],
                       ctypes.c_int),
+    "ck_w4a16_gemm": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _i64, _p, _p, _i64, _p],
+                      ctypes.c_int),
     "ck_quantize_weights": ([_p, _i64, _i64, _i64, _i32, _i32, _p, _i64, _p, _p], ctypes.c_int),
     "ck_test_rotate_f32": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p], ctypes.c_int),
     "ck_test_gemm_i32": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
@@ -261,6 +263,24 @@ def w4a8_linear(x, G, packed, w_scales, per_group, **kw):
 
 def w4a4_linear(x, G, packed, w_scales, per_group, **kw):
     return linear(x, G, 4, packed, w_scales, per_group, **kw)
+
+
+def w4a16_gemm(x, packed, scales, zeros, bias=None, out=None):
+    """AWQ W4A16 product for any M on the dequantise path (W rebuilt in bf16), bf16 [M, N]."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    N = _weights(packed, scales, True, K)
+    _dense(zeros, "zeros", torch.bfloat16, (K // 64, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    _out(out, "out", torch.bfloat16, M, N)
+    _same_device(x, ("packed", packed), ("scales", scales), ("zeros", zeros), ("bias", bias),
+                 ("out", out))
+    _check(lib.ck_w4a16_gemm(_ptr(x), M, K, _ld(x), _ptr(packed), _ld(packed), _ptr(scales),
+                             _ptr(zeros), 64, N, _ptr(bias), _ptr(out), _ld(out), _stream(x)))
+    return out
 
 
 def w4a16_gemv(x, packed, scales, zeros, bias=None, out=None):

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libck.so")
 
-HIP_SOURCES = ["rotate_quant.hip", "w4_gemv.hip", "w4_skinny.hip", "w4_gemm.hip", "w4a16_gemv.hip"]
+HIP_SOURCES = ["rotate_quant.hip", "w4_gemv.hip", "w4_skinny.hip", "w4_gemm.hip", "w4a16_gemv.hip",
+               "awq_gemm.hip"]
 CXX_SOURCES = ["ck_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,317 @@
+// AWQ W4A16 prefill GEMM (many activation rows) on bf16 MFMA.
+//
+// Computes out = x . W^T (+ bias) with the weight rebuilt as the dequantise
+// path of "comfy_kitchen/tensor/awq_w4a16.py" (dequantize()) does it, in the
+// bf16 compute dtype, one tensor operation at a time:
+//   W[n, k] = bf16( bf16((q - 8) * s[k/64, n]) + z[k/64, n] )
+// then a bf16 x bf16 product with fp32 accumulation and a bf16 store.  The
+// rebuilt weight is never written to memory: each wave dequantises the
+// fragments it multiplies, in VGPRs, once per K step.
+//
+// Tiling: 4 waves (one per SIMD), block tile 256 x 256, each wave 256 rows x
+// 64 weight rows = 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (accumulators in
+// AGPRs).  Weights are the MFMA A operand, so a lane holds one output row and
+// four consecutive output columns per register group.  K step = 64 (one
+// scale group) in a ring of three stages filled by buffer_load ... lds, one
+// barrier per K step; the activation fragments of sub-step u + 1 are read,
+// and its weight fragments dequantised, while sub-step u multiplies.
+// MFMA operand layout: lane l holds 8 consecutive k of row l % 32, k = 8 (l /
+// 32) + e within a 16-wide sub-step; both operands use the same assignment,
+// with sub-step u of a K step covering k = 16 u .. 16 u + 15.
+#include "ck_device.h"
+#include "launch.h"
+
+namespace ck {
+namespace {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bfv __attribute__((ext_vector_type(8)));
+
+constexpr int kNst = 3;                       // ring stages (K steps)
+constexpr int kXRow = 128;                    // x bytes per row and K step (64 bf16)
+constexpr int kWRow = 32;                     // packed weight bytes per row and K step
+constexpr int kWaves = 4;                     // waves per block (WGN)
+
+// Block shape: kWaves waves side by side over the weight rows, each wave
+// WM x WN 32x32 tiles.
+template <int WM, int WN>
+struct Shape {
+    static constexpr int BM = WM * 32;
+    static constexpr int BN = kWaves * WN * 32;
+    static constexpr int XBytes = BM * kXRow;
+    static constexpr int Stage = XBytes + BN * kWRow;
+    static constexpr int XLanes = XBytes / kWaves >= 1024 ? kWave : XBytes / kWaves / 16;
+    static constexpr int XLd = XBytes / kWaves >= 1024 ? XBytes / kWaves / 1024 : 1;
+    static constexpr int WLanes = BN * kWRow / kWaves >= 1024 ? kWave : BN * kWRow / kWaves / 16;
+    static constexpr int WLd = BN * kWRow / kWaves >= 1024 ? BN * kWRow / kWaves / 1024 : 1;
+    static constexpr int L = XLd + WLd;        // DMA instructions per wave and stage
+    static constexpr int TW = WN * 32;         // output columns per wave
+    static constexpr int Pitch = TW * 2 + 16;  // staged epilogue row, bytes
+    static constexpr int Smem = kWaves * BM * Pitch > kNst * Stage ? kWaves * BM * Pitch : kNst * Stage;
+    static_assert(XLd * kWaves * XLanes * 16 == XBytes && WLd * kWaves * WLanes * 16 == BN * kWRow, "DMA split");
+    static_assert(Smem <= 160 * 1024, "LDS");
+};
+
+// Slot swizzles measured conflict-free for 32 consecutive rows reading one
+// 16-byte slot (lane half in bit 0): 128-byte rows (r >> 1) & 7, 32-byte rows
+// ((r >> 2) ^ (r >> 3)) & 1.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Eight packed codes (one dword, byte j = column 2j | column 2j+1 << 4) to
+// eight bf16 weights in column order, each rounded as the bf16 tensor
+// operations round: bf16(bf16((q - 8) s) + z).  (q - 8) s is exact in fp32.
+__device__ __forceinline__ v8bfv dequant8(uint32_t d, float s, float m8s, float z)
+{
+    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float q0 = (float)((lo >> (8 * i)) & 0xffu);
+        const float q1 = (float)((hi >> (8 * i)) & 0xffu);
+        const uint32_t p = pack_bf16x2(__builtin_fmaf(q0, s, m8s), __builtin_fmaf(q1, s, m8s));
+        r[i] = pack_bf16x2(__uint_as_float(p << 16) + z, __uint_as_float(p & 0xffff0000u) + z);
+    }
+    return __builtin_bit_cast(v8bfv, r);
+}
+
+template <int WM, int WN>
+__global__ __launch_bounds__(kWaves * kWave) void awq_gemm_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, int M, int K, const uint8_t *__restrict__ packed,
+    int64_t ldw, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros, int N,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int64_t ldo)
+{
+    using S = Shape<WM, WN>;
+    constexpr int kBM = S::BM, kBN = S::BN, kXBytes = S::XBytes, kStage = S::Stage, kTW = S::TW;
+    constexpr int kPitch = S::Pitch, kL = S::L;
+    constexpr int kWM = WM, kWN = WN;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
+    lds_u8 *smem = (lds_u8 *)smem_generic;
+
+    const int tiles_m = (M + kBM - 1) / kBM;
+    const int tiles_n = (N + kBN - 1) / kBN;
+    const int tile = xcd_block(blockIdx.x, tiles_m * tiles_n);
+    const int m0 = (tile / tiles_n) * kBM;
+    const int n0 = (tile % tiles_n) * kBN;
+
+    const int t = threadIdx.x;
+    const int wave = t / kWave, lane = t % kWave;
+    const int l32 = lane % 32, h = lane / 32;
+    const int ksteps = K / 64;
+
+    // Buffer resources spanning exactly the block's rows: rows past M / N read
+    // as zero and their results are never stored.
+    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + (int64_t)m0 * ldx), (short)0,
+        (int)((int64_t)(min(M - m0, kBM) - 1) * ldx * 2 + (int64_t)K * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(packed + (int64_t)n0 * ldw), (short)0,
+        (int)((int64_t)(min(N - n0, kBN) - 1) * ldw + K / 2), 0x00020000);
+
+    auto issue_stage = [&](int kt) {
+        lds_u8 *sa = smem + (kt % kNst) * kStage;
+#pragma unroll
+        for (int j = 0; j < S::XLd; ++j) {
+            const int q = (wave * S::XLd + j) * S::XLanes + lane;
+            if (S::XLanes == kWave || lane < S::XLanes) {
+                const int r = q / 8, c = (q % 8) ^ swz8(q / 8);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    x_rsrc, (__attribute__((address_space(3))) void *)(sa + (wave * S::XLd + j) * S::XLanes * 16),
+                    16, (int)(r * ldx * 2) + kt * kXRow + 16 * c, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < S::WLd; ++j) {
+            const int q = (wave * S::WLd + j) * S::WLanes + lane;
+            if (S::WLanes == kWave || lane < S::WLanes) {
+                const int n = q / 2, c = (q % 2) ^ swz2(q / 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    w_rsrc,
+                    (__attribute__((address_space(3))) void *)(sa + kXBytes + (wave * S::WLd + j) * S::WLanes * 16),
+                    16, (int)(n * ldw) + kt * kWRow + 16 * c, 0, 0, 0);
+            }
+        }
+    };
+
+    // Scale and zero point of this lane's two weight rows for K step kt.
+    uint32_t sz_raw[kWN][2];
+    auto load_sz = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < kWN; ++j) {
+            const int n = min(n0 + wave * kTW + j * 32 + l32, N - 1);
+            sz_raw[j][0] = scales[(int64_t)kt * N + n];
+            sz_raw[j][1] = zeros[(int64_t)kt * N + n];
+        }
+    };
+
+    const int sw8 = swz8(l32);
+    const int x_base = l32 * kXRow;                                    // + i * 32 rows
+    const int w_row = wave * kTW + l32;                                // + j * 32 rows
+    const int w_base = kXBytes + w_row * kWRow;
+    const int w_swz = swz2(w_row);
+
+    v16f acc[kWM][kWN];
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+#pragma unroll
+        for (int j = 0; j < kWN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    // Ring invariant: DMA(kt), then the scale loads of kt, then DMA(kt + 1).
+    issue_stage(0);
+    load_sz(0);
+    if (ksteps > 1)
+        issue_stage(1);
+
+    for (int kt = 0; kt < ksteps; ++kt) {
+        // This wave's DMA for step kt has landed once at most the scale loads
+        // of kt and the DMA of kt + 1 are outstanding; the barrier extends
+        // that to all waves and retires every read of the slot refilled below.
+        if (kt + 1 < ksteps)
+            wait_vmcnt<kWN * 2 + kL>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        float sc[kWN], m8s[kWN], zp[kWN];
+#pragma unroll
+        for (int j = 0; j < kWN; ++j) {
+            sc[j] = bf16_to_f32(sz_raw[j][0]);
+            m8s[j] = -8.f * sc[j];
+            zp[j] = bf16_to_f32(sz_raw[j][1]);
+        }
+        if (kt + 1 < ksteps)
+            load_sz(kt + 1);
+        if (kt + 2 < ksteps)
+            issue_stage(kt + 2);
+
+        const lds_u8 *sa = smem + (kt % kNst) * kStage;
+        // Packed codes of the step: sub-step u, half h is dword 2u + h of the
+        // row's 32 bytes, in 16-byte slot u / 2.
+        uint32_t pk[kWN][4];
+#pragma unroll
+        for (int j = 0; j < kWN; ++j)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                pk[j][u] = *(lds_u32 *)(sa + w_base + j * 32 * kWRow + 16 * ((u >> 1) ^ w_swz) +
+                                        4 * ((2 * u + h) & 3));
+        u32x4 xf[2][kWM];
+#pragma unroll
+        for (int i = 0; i < kWM; ++i)
+            xf[0][i] = *(lds_u32x4 *)(sa + x_base + i * 32 * kXRow + 16 * ((0 + h) ^ sw8));
+        v8bfv wf[2][kWN];
+#pragma unroll
+        for (int j = 0; j < kWN; ++j)
+            wf[0][j] = dequant8(pk[j][0], sc[j], m8s[j], zp[j]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // One scheduling region per sub-step: the reads and the
+            // dequantisation of sub-step u + 1 interleave with the MFMAs of u.
+            __builtin_amdgcn_sched_barrier(0);
+            if (u + 1 < 4) {
+#pragma unroll
+                for (int i = 0; i < kWM; ++i)
+                    xf[(u + 1) & 1][i] =
+                        *(lds_u32x4 *)(sa + x_base + i * 32 * kXRow + 16 * ((2 * (u + 1) + h) ^ sw8));
+#pragma unroll
+                for (int j = 0; j < kWN; ++j)
+                    wf[(u + 1) & 1][j] = dequant8(pk[j][u + 1], sc[j], m8s[j], zp[j]);
+            }
+#pragma unroll
+            for (int i = 0; i < kWM; ++i) {
+                const v8bfv xb = __builtin_bit_cast(v8bfv, xf[u & 1][i]);
+#pragma unroll
+                for (int j = 0; j < kWN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[u & 1][j], xb, acc[i][j], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue: lane l holds rows m = m0 + 32 i + l32 and, in register group
+    // q, columns n = n0w + 32 j + 8 q + 4 h + (0..3).  Each wave stages its
+    // 256 x 64 bf16 tile in LDS and writes 128-byte row pieces.
+    const int n0w = n0 + wave * kTW;
+    __builtin_amdgcn_s_barrier();  // every wave is done with the operand stages
+    lds_u8 *wt = smem + wave * (kBM * kPitch);
+#pragma unroll
+    for (int j = 0; j < kWN; ++j) {
+        float bc[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bc[q][e] = bias ? bf16_to_f32(bias[min(n0w + j * 32 + 8 * q + 4 * h + e, N - 1)]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < kWM; ++i) {
+            const int ml = i * 32 + l32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 pkd = {pack_bf16x2(acc[i][j][4 * q] + bc[q][0], acc[i][j][4 * q + 1] + bc[q][1]),
+                                   pack_bf16x2(acc[i][j][4 * q + 2] + bc[q][2], acc[i][j][4 * q + 3] + bc[q][3])};
+                *(__attribute__((address_space(3))) u32x2 *)(wt + ml * kPitch + (j * 32 + 8 * q + 4 * h) * 2) = pkd;
+            }
+        }
+    }
+    constexpr int kChunks = kTW * 2 / 16;  // 16-byte chunks per staged row
+    constexpr int kRows = kWave / kChunks;
+#pragma unroll 4
+    for (int it = 0; it < kBM / kRows; ++it) {
+        const int ml = it * kRows + lane / kChunks;
+        const int c = lane % kChunks;
+        const u32x4 v = *(lds_u32x4 *)(wt + ml * kPitch + 16 * c);
+        const int m = m0 + ml, n = n0w + 8 * c;
+        if (m < M && n < N)
+            *reinterpret_cast<u32x4 *>(out + (int64_t)m * ldo + n) = v;
+    }
+}
+
+
+template <int WM, int WN>
+hipError_t launch_shape(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed, int64_t ldw,
+                        const uint16_t *scales, const uint16_t *zeros, int N, const uint16_t *bias,
+                        uint16_t *out, int64_t ldo, hipStream_t s)
+{
+    using S = Shape<WM, WN>;
+    auto kern = awq_gemm_kernel<WM, WN>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::Smem);
+    if (attr != hipSuccess)
+        return attr;
+    const int tiles = ((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(kWaves * kWave), S::Smem, s, x, ldx, M, K, packed, ldw, scales,
+                       zeros, N, bias, out, ldo);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_awq_gemm(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed, int64_t ldw,
+                    const uint16_t *scales, const uint16_t *zeros, int N, const uint16_t *bias,
+                    uint16_t *out, int64_t ldo, void *stream)
+{
+    if (M <= 0)
+        return 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // 256 x 256 tiles (one wave per SIMD, each dequantised weight fragment
+    // reused for 8 row tiles) when they fill the chip; 128 x 128 tiles for
+    // fewer rows, where the larger tiles leave most CUs idle.
+    constexpr int kCus = 256;
+    const int big = ((M + 255) / 256) * ((N + 255) / 256);
+    if (big >= kCus)
+        return (int)launch_shape<8, 2>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
+    return (int)launch_shape<4, 1>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
+}
+
+}  // namespace ck

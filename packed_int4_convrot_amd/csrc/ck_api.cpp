@@ -541,6 +541,37 @@ int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const ui
     return hip_status(e, fn);
 }
 
+int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
+                  int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int32_t Gw, int64_t N,
+                  const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    const char *fn = "ck_w4a16_gemm";
+    CK_TRY(check_m(fn, M));
+    CK_TRY(check_k(fn, K));
+    const Weights w{packed, ldw, scales, CK_WS_PER_GROUP, Gw, N};
+    CK_TRY(check_weights(fn, w, K, true));
+    if (!zeros || !aligned(zeros, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: zeros must be a non-NULL 2-byte aligned pointer", fn);
+    if (M == 0)
+        return ok();
+    CK_TRY(check_x(fn, x, K, ldx));
+    if (ldx > kMaxLd / 2)
+        return fail(CK_ERR_UNSUPPORTED, "%s: ldx (%lld) must be at most %lld elements", fn, (long long)ldx,
+                    (long long)(kMaxLd / 2));
+    if (bias && !aligned(bias, 2))
+        return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
+    CK_TRY(check_out(fn, out, N, ldo, 2));
+    CK_TRY(check_tiles(fn, M, N));
+    const Range ro = span(out, M, N, ldo, 2);
+    if (overlap(ro, span(x, M, K, ldx, 2)) || overlap(ro, span(packed, N, K / 2, ldw, 1)) ||
+        overlap(ro, span(scales, K / 64, N, N, 2)) || overlap(ro, span(zeros, K / 64, N, N, 2)) ||
+        overlap(ro, span(bias, 1, N, N, 2)))
+        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    const int e = ck::launch_awq_gemm(x, (int)M, (int)K, ldx, packed, ldw, scales, zeros, (int)N, bias, out,
+                                      ldo, stream);
+    return hip_status(e, fn);
+}
+
 int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, const uint8_t *packed,
                      int64_t ldw, int64_t N, int32_t *acc, int64_t lda, void *stream)
 {

@@ -11,6 +11,12 @@ int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
                         bool packed4, void *stream);
 
+// AWQ W4A16 prefill GEMM: out = x . W^T (+ bias), W rebuilt in bf16 as the
+// page's dequantize() does; Gw = 64 scales and zero points [K/64, N].
+int launch_awq_gemm(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed, int64_t ldw,
+                    const uint16_t *scales, const uint16_t *zeros, int N, const uint16_t *bias,
+                    uint16_t *out, int64_t ldo, void *stream);
+
 // Offline weight producer: rotate N bf16 weight rows of K columns by H_G,
 // quantise to codes in [-7, 7] with bf16 scales per row (per_group false) or
 // per 64-column group ([K/64, N]), and pack q = code + 8 two per byte.

@@ -154,6 +154,24 @@ def test_awq_rejects():
     assert f(P, 1, 256, 256, P3, 128, P4, P2 + 8, 64, 64, None, P5, 64, None) == ck.CK_ERR_INVALID_ARG
 
 
+def test_awq_gemm_rejects():
+    f = lib.ck_w4a16_gemm
+    args = [P, 300, 256, 256, P3, 128, P4, P2, 64, 64, None, P5, 64, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a7=None) == ck.CK_ERR_INVALID_ARG          # zeros
+    assert call(a8=32) == ck.CK_ERR_UNSUPPORTED             # Gw
+    assert call(a9=40) == ck.CK_ERR_UNSUPPORTED             # N % 16
+    assert call(a3=200) == ck.CK_ERR_INVALID_ARG            # ldx < K
+    assert call(a3=(1 << 22) + 8) == ck.CK_ERR_UNSUPPORTED   # ldx beyond the buffer offsets
+    assert call(a11=P + 64) == ck.CK_ERR_INVALID_ARG        # output overlaps x
+    assert call(a12=68) == ck.CK_ERR_INVALID_ARG            # ldo % 8
+    assert call(a1=0, a0=None, a11=None) == ck.CK_OK
+
+
 def test_gemm_packed4_rejects():
     f = lib.ck_w4a4_gemm_packed
     ok = dict(c=P, ldq=128, rs=P2, M=4, K=256, w=P3, ldw=128, s=P4, kind=0, Gw=64, N=64, b=None, o=P5, ldo=64)

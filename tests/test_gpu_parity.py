@@ -515,3 +515,54 @@ def test_produced_weights_run_the_linear(per_group):
     err_oracle = np.linalg.norm(oracle_out - exact)
     assert err_oracle / np.linalg.norm(exact) < 0.3
     assert err_gpu <= 1.05 * err_oracle
+
+
+# ------------------------------------------------------- AWQ prefill GEMM
+
+
+def _awq_inputs(M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    x = workloads.to_bf16_bits(rng.standard_normal((M, K)))
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = workloads.to_bf16_bits(rng.uniform(0.002, 0.02, size=(K // 64, N)))
+    z = workloads.to_bf16_bits(rng.normal(0, 0.01, size=(K // 64, N)))
+    bias = workloads.to_bf16_bits(rng.standard_normal(N))
+    return x, packed, s, z, bias
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (9, 64, 16), (64, 256, 272), (300, 1152, 400), (513, 3072, 256), (257, 128, 528), (1, 640, 48),
+])
+def test_awq_gemm_matches_oracle(M, K, N):
+    x, packed, s, z, bias = _awq_inputs(M, K, N, seed=M + K + N)
+    out = host(ck.w4a16_gemm(bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z), bias=bf16_dev(bias)))
+    ref = oracle.awq_gemm(x, packed, s, z, bias=bias)
+    assert_output_close(out, ref)
+
+
+def test_awq_gemm_without_bias_strided_and_near_the_gemv():
+    """No bias, a strided input with NaN padding, and agreement with the exact-weight
+    GEMV within W's bf16 rounding at a size both accept."""
+    M, K, N, ld = 8, 3072, 512, 3200
+    x, packed, s, z, _ = _awq_inputs(M, K, N, seed=3)
+    xp = np.full((M, ld), 0x7FC0, dtype=np.uint16)
+    xp[:, :K] = x
+    xd = bf16_dev(xp)[:, :K]
+    g = host(ck.w4a16_gemm(xd, u8_dev(packed), bf16_dev(s), bf16_dev(z)))
+    assert np.isfinite(g).all()
+    assert_output_close(g, oracle.awq_gemm(x, packed, s, z))
+    v = host(ck.w4a16_gemv(xd, u8_dev(packed), bf16_dev(s), bf16_dev(z)))
+    wmax = np.abs(workloads.bf16_bits_to_f32(oracle.awq_dequantize(packed, s, z))).max()
+    bound = 2 * 2.0 ** -8 * np.abs(workloads.bf16_bits_to_f32(x)).sum(1, keepdims=True) * wmax
+    assert (np.abs(g - v) <= bound + 2.0 ** -7 * np.abs(v)).all()
+
+
+@pytest.mark.parametrize("M,K,N", [(4096, 512, 4096), (4100, 320, 4112)])
+def test_awq_gemm_large_tiles_sampled_rows(M, K, N):
+    """Shapes that fill the chip with 256 x 256 tiles (the prefill configuration),
+    ragged in M and N, checked on sampled rows that include the last tile's."""
+    x, packed, s, z, bias = _awq_inputs(M, K, N, seed=M + N)
+    out = host(ck.w4a16_gemm(bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z), bias=bf16_dev(bias)))
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), np.arange(M - 8, M), [255, 256]]))
+    ref = oracle.awq_gemm(x[rows], packed, s, z, bias=bias)
+    assert_output_close(out[rows], ref)

@@ -388,3 +388,59 @@ def test_weight_producer_gives_the_linear_of_w(G, per_group):
     other = 16 if G != 16 else 64
     bad, _, _ = oracle.linear(x, other, 8, packed, scales, per_group)
     assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 0.5
+
+
+# ------------------------------------------------ AWQ dequantise (prefill)
+
+
+def _hexes(rows):
+    return np.array([[int(v, 16) for v in r] for r in rows], dtype=np.uint16)
+
+
+def test_awq_dequantize_golden():
+    d = _golden("awq_dequantize.json")
+    w = oracle.awq_dequantize(np.array(d["packed"], dtype=np.uint8), _hexes(d["scales"]), _hexes(d["zeros"]),
+                              d["Gw"])
+    assert np.array_equal(w, _hexes(d["W"]))
+    y = oracle.awq_gemm(_bf16([d["x"]]), np.array(d["packed"], dtype=np.uint8), _hexes(d["scales"]),
+                        _hexes(d["zeros"]), d["Gw"])
+    assert np.array_equal(y[0], np.array(d["y"]))
+
+
+def test_awq_dequantize_is_the_rounded_exact_weight():
+    """Every dequantised weight is within one bf16 rounding of each step of the exact
+    (q - 8) s + z, and equals it whenever the exact value is a bf16 number."""
+    rng = np.random.default_rng(21)
+    N, K, Gw = 16, 256, 64
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = _bf16(rng.uniform(0.002, 0.02, size=(K // Gw, N)))
+    z = _bf16(rng.normal(0, 0.01, size=(K // Gw, N)))
+    w = _f32(oracle.awq_dequantize(packed, s, z, Gw)).astype(np.float64)
+    q = oracle.unpack(packed).astype(np.float64)
+    S = np.repeat(_f32(s).astype(np.float64).T, Gw, axis=1)
+    Z = np.repeat(_f32(z).astype(np.float64).T, Gw, axis=1)
+    exact = q * S + Z
+    # two roundings of at most half a bf16 step each (relative 2^-8 of the value rounded)
+    bound = 2.0 ** -8 * (np.abs(q * S) + np.abs(exact)) * 1.0001 + 1e-30
+    assert (np.abs(w - exact) <= bound).all()
+    # zero scale and zero point -> exact products
+    z0 = np.zeros_like(z)
+    s1 = _bf16(np.full((K // Gw, N), 0.25))
+    assert np.array_equal(_f32(oracle.awq_dequantize(packed, s1, z0, Gw)).astype(np.float64), q * 0.25)
+
+
+def test_awq_gemm_brute_force_and_near_the_exact_product():
+    rng = np.random.default_rng(22)
+    M, N, K, Gw = 5, 12, 128, 64
+    x = _bf16(rng.standard_normal((M, K)))
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = _bf16(rng.uniform(0.002, 0.02, size=(K // Gw, N)))
+    z = _bf16(rng.normal(0, 0.01, size=(K // Gw, N)))
+    bias = _bf16(rng.standard_normal(N))
+    y = oracle.awq_gemm(x, packed, s, z, Gw, bias=bias)
+    w = _f32(oracle.awq_dequantize(packed, s, z, Gw)).astype(np.float64)
+    ref = _f32(x).astype(np.float64) @ w.T + _f32(bias).astype(np.float64)
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+    exact = oracle.awq_gemv(x, packed, s, z, Gw, bias=bias)
+    wmax = np.abs(w).max()
+    assert np.abs(y - exact).max() <= 2 * 2.0 ** -8 * np.abs(_f32(x)).sum(1).max() * wmax
