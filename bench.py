@@ -37,6 +37,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_decode_gemv_m1_k3840_n10240_traffic.txt")
 GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv.hip", "packed_int4_convrot_amd/csrc/ck_device.h"]
@@ -435,7 +436,22 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
     total = pb + 2 * 2 * (w["K"] // 64) * w["N"] + w["K"] * 2 + w["N"] * 2
     res[name] = {"us": round(us, 3), "packed_GBps": round(pb / us / 1e3, 1),
                  "total_GBps": round(total / us / 1e3, 1), "frac_hbm": round(total / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del packs
     log("bench: awq done")
+
+    # AWQ prefill GEMM on the same layer at 4096 rows (bf16 MFMA, weights rebuilt in registers)
+    M, K, N = 4096, w["K"], w["N"]
+    rng = torch.Generator(device=dev).manual_seed(1)
+    xs = (torch.randn((M, K), generator=rng, device=dev)).to(torch.bfloat16)
+    pk = u8(d["packed"])
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = _time(lambda i: ck.w4a16_gemm(xs, pk, s, z, out=out), stream, 10)
+    fl = 2.0 * M * N * K
+    res["awq_w4a16_gemm_m%d_k%d_n%d" % (M, K, N)] = {
+        "us": round(us, 1), "bf16_TFLOPS": round(fl / us / 1e6, 1),
+        "frac_bf16_peak": round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    del xs, pk, out
+    log("bench: awq prefill done")
     return res
 
 

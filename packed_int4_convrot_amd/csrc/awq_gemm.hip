@@ -33,12 +33,11 @@ typedef __bf16 v8bfv __attribute__((ext_vector_type(8)));
 constexpr int kNst = 3;                       // ring stages (K steps)
 constexpr int kXRow = 128;                    // x bytes per row and K step (64 bf16)
 constexpr int kWRow = 32;                     // packed weight bytes per row and K step
-constexpr int kWaves = 4;                     // waves per block (WGN)
-
-// Block shape: kWaves waves side by side over the weight rows, each wave
-// WM x WN 32x32 tiles.
-template <int WM, int WN>
+// Block shape: NW waves side by side over the weight rows, each wave WM x WN
+// 32x32 tiles.
+template <int WM, int WN, int NW>
 struct Shape {
+    static constexpr int kWaves = NW;
     static constexpr int BM = WM * 32;
     static constexpr int BN = kWaves * WN * 32;
     static constexpr int XBytes = BM * kXRow;
@@ -85,13 +84,14 @@ __device__ __forceinline__ v8bfv dequant8(uint32_t d, float s, float m8s, float 
     return __builtin_bit_cast(v8bfv, r);
 }
 
-template <int WM, int WN>
-__global__ __launch_bounds__(kWaves * kWave) void awq_gemm_kernel(
+template <int WM, int WN, int NW>
+__global__ __launch_bounds__(NW * kWave) void awq_gemm_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int M, int K, const uint8_t *__restrict__ packed,
     int64_t ldw, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros, int N,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int64_t ldo)
 {
-    using S = Shape<WM, WN>;
+    using S = Shape<WM, WN, NW>;
+    constexpr int kWaves = NW;
     constexpr int kBM = S::BM, kBN = S::BN, kXBytes = S::XBytes, kStage = S::Stage, kTW = S::TW;
     constexpr int kPitch = S::Pitch, kL = S::L;
     constexpr int kWM = WM, kWN = WN;
@@ -278,19 +278,19 @@ __global__ __launch_bounds__(kWaves * kWave) void awq_gemm_kernel(
 }
 
 
-template <int WM, int WN>
+template <int WM, int WN, int NW>
 hipError_t launch_shape(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed, int64_t ldw,
                         const uint16_t *scales, const uint16_t *zeros, int N, const uint16_t *bias,
                         uint16_t *out, int64_t ldo, hipStream_t s)
 {
-    using S = Shape<WM, WN>;
-    auto kern = awq_gemm_kernel<WM, WN>;
+    using S = Shape<WM, WN, NW>;
+    auto kern = awq_gemm_kernel<WM, WN, NW>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::Smem);
     if (attr != hipSuccess)
         return attr;
     const int tiles = ((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(kWaves * kWave), S::Smem, s, x, ldx, M, K, packed, ldw, scales,
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(NW * kWave), S::Smem, s, x, ldx, M, K, packed, ldw, scales,
                        zeros, N, bias, out, ldo);
     return hipGetLastError();
 }
@@ -310,8 +310,8 @@ int launch_awq_gemm(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t 
     constexpr int kCus = 256;
     const int big = ((M + 255) / 256) * ((N + 255) / 256);
     if (big >= kCus)
-        return (int)launch_shape<8, 2>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
-    return (int)launch_shape<4, 1>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
+        return (int)launch_shape<8, 2, 4>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
+    return (int)launch_shape<4, 1, 4>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
 }
 
 }  // namespace ck
