@@ -351,6 +351,55 @@ def test_graph_replay_matches_eager(M):
         ck.rotate_quant(xd, 256, 4)  # unrelated eager work between replays
 
 
+def _graph_replays_equal_eager(fn, out):
+    """Capture fn (writing into out) in a HIP graph; every replay equals the eager result."""
+    eager = fn().clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        torch.mm(torch.ones(64, 64, device=DEV), torch.ones(64, 64, device=DEV))  # unrelated eager work
+
+
+def test_graph_replay_packed_w4a4_and_awq_gemm():
+    """The packed W4A4 path (M > 64), the weight producer and the AWQ prefill GEMM
+    replay from a HIP graph bit-identically."""
+    M, K, N = 300, 1024, 272
+    inp = workloads.linear_inputs(M, K, N, seed=8, outliers=5, scale="channel", with_bias=True)
+    xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    _graph_replays_equal_eager(lambda: ck.linear(xd, 256, 4, wd, sd, False, bias=bd, out=out, workspace=ws),
+                               out)
+    x, packed, s, z, bias = _awq_inputs(M, K, N, seed=9)
+    args = (bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z))
+    bias_d = bf16_dev(bias)
+    out2 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    _graph_replays_equal_eager(lambda: ck.w4a16_gemm(*args, bias=bias_d, out=out2), out2)
+    w = bf16_dev(_weights_bf16(N, K, seed=10))
+    pk = torch.empty((N, K // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((K // 64, N), dtype=torch.bfloat16, device=DEV)
+    _graph_replays_equal_eager(lambda: ck.quantize_weights(w, 64, True, pk, sc)[0], pk)
+
+
+def test_awq_gemm_deterministic():
+    x, packed, s, z, bias = _awq_inputs(1000, 768, 528, seed=12)
+    args = (bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z))
+    a = [ck.w4a16_gemm(*args, bias=bf16_dev(bias)) for _ in range(2)]
+    assert torch.equal(a[0].view(torch.int16), a[1].view(torch.int16))
+
+
 def test_linear_x_scale_power_of_two_is_exact():
     inp = workloads.linear_inputs(20, 512, 64, seed=2, outliers=4, scale="channel")
     xd, wd, sd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"])
