@@ -76,9 +76,10 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // order by act_perm16().
 __device__ __forceinline__ void w4_decode_x16(uint32_t d, uint32_t &lo, uint32_t &hi)
 {
-    const uint32_t e = d ^ 0x88888888u;
-    lo = (e << 4) & 0xf0f0f0f0u;
-    hi = e & 0xf0f0f0f0u;
+    // Only bit 3 of each nibble is flipped where it survives the mask, so the
+    // flip and the mask fold into one v_bitop3 per dword half.
+    lo = ((d << 4) ^ 0x80808080u) & 0xf0f0f0f0u;
+    hi = (d ^ 0x80808080u) & 0xf0f0f0f0u;
 }
 
 // Reorder 16 consecutive int8 values k = 0..15 (four dwords) into the order
