@@ -615,3 +615,45 @@ def test_awq_gemm_large_tiles_sampled_rows(M, K, N):
     rows = np.unique(np.concatenate([np.arange(0, M, 97), np.arange(M - 8, M), [255, 256]]))
     ref = oracle.awq_gemm(x[rows], packed, s, z, bias=bias)
     assert_output_close(out[rows], ref)
+
+
+# ------------------------------------------------------------ edge shapes
+
+
+@pytest.mark.parametrize("M,K,N,G", [
+    (65, 64, 16, 16),        # first tiled M, a single K step (stage tail of one step)
+    (129, 320, 48, 64),      # five K steps: one full stage of four, then a partial one
+    (300, 448, 32, 64),      # seven K steps
+    (70, 32768, 32, 256),    # longest K
+])
+def test_w4a4_packed_path_edge_shapes(M, K, N, G):
+    """The packed W4A4 tiled path at K tails that do not fill a 4-step stage and at the
+    longest K, against the oracle epilogue on the GPU's own codes."""
+    inp = workloads.linear_inputs(M, K, N, seed=M + K, outliers=3, scale="channel", with_bias=True)
+    xd = bf16_dev(inp["x"])
+    out = host(ck.linear(xd, G, 4, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), False,
+                         bias=bf16_dev(inp["bias"])))
+    codes, scales = ck.rotate_quant(xd, G, 4)
+    ref = oracle.gemm_q(host(codes), host(scales), inp["packed"], inp["w_scales"], False, bias=inp["bias"])
+    assert_output_close(out, ref)
+    codes4, rs = ck.rotate_quant_packed4(xd, G)
+    acc = host(ck.accumulators_i32_a4(codes4, K, u8_dev(inp["packed"])))
+    assert np.array_equal(acc.astype(np.int64), oracle.int_gemm(host(codes), oracle.unpack(inp["packed"])))
+
+
+@pytest.mark.parametrize("M,K,N", [(33, 64, 16), (20, 32768, 16), (300, 192, 784)])
+def test_awq_gemm_edge_shapes(M, K, N):
+    x, packed, s, z, bias = _awq_inputs(M, K, N, seed=K + N)
+    out = host(ck.w4a16_gemm(bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z), bias=bf16_dev(bias)))
+    assert_output_close(out, oracle.awq_gemm(x, packed, s, z, bias=bias))
+
+
+def test_quantize_weights_longest_rows():
+    w = _weights_bf16(5, 32768, seed=13, zero_rows=(2,))
+    wd = bf16_dev(w)
+    for G in (16, 256):
+        for pg in (False, True):
+            packed, scales = ck.quantize_weights(wd, G, pg)
+            ref_p, ref_s = oracle.quantize_weights(host(ck.rotated_f32(wd, G)), pg)
+            assert np.array_equal(host(packed), ref_p)
+            assert np.array_equal(host(scales.view(torch.int16)).view(np.uint16), ref_s)
