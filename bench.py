@@ -59,6 +59,10 @@ def parse():
                     help="only run a plain elementwise copy of CALIB_BYTES (counter calibration)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                     help="write the traffic record from rocprofv3 counter_collection CSVs and exit")
+    ap.add_argument("--profile-workload", choices=sorted(PROFILE_WORKLOADS),
+                    help="only run one kernel of the extras a few times (for rocprofv3 counter passes)")
+    ap.add_argument("--write-counters", nargs="+", metavar="ARG",
+                    help="WORKLOAD CSV...: write profiles/WORKLOAD_counters.txt from the counter passes")
     return ap.parse_args()
 
 
@@ -134,6 +138,145 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, alg_bytes)
     print(text)
 
 
+# Kernels of the extras that the counter summaries under profiles/ cover: the
+# kernel-name substring, the MFMA op counter, and the algorithmic bytes per launch.
+PROFILE_WORKLOADS = {
+    "w4a4_gemm_m8192_k3840_n3840": dict(
+        kernel="w4_gemm_kernel", M=8192, K=3840, N=3840, mops="SQ_INSTS_VALU_MFMA_MOPS_I8",
+        alg_bytes=8192 * 3840 // 2 + 8192 * 4 + 3840 * 3840 // 2 + 3840 * 2 + 8192 * 3840 * 2),
+    "w4a4_gemm_m8192_k10240_n3840": dict(
+        kernel="w4_gemm_kernel", M=8192, K=10240, N=3840, mops="SQ_INSTS_VALU_MFMA_MOPS_I8",
+        alg_bytes=8192 * 10240 // 2 + 8192 * 4 + 3840 * 10240 // 2 + 3840 * 2 + 8192 * 3840 * 2),
+    "awq_w4a16_gemm_m4096_k3072_n18432": dict(
+        kernel="awq_gemm_kernel", M=4096, K=3072, N=18432, mops="SQ_INSTS_VALU_MFMA_MOPS_BF16",
+        alg_bytes=4096 * 3072 * 2 + 18432 * 3072 // 2 + 2 * 2 * 48 * 18432 + 4096 * 18432 * 2),
+    "rotate_quant_m8192_k10240_ld10752_g64": dict(
+        kernel="rotate_quant_kernel", M=8192, K=10240, N=0, mops=None,
+        alg_bytes=8192 * 10240 * 2 + 8192 * 10240 + 8192 * 4),
+}
+KERNEL_SOURCES = {
+    "w4_gemm_kernel": ["packed_int4_convrot_amd/csrc/w4_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
+    "awq_gemm_kernel": ["packed_int4_convrot_amd/csrc/awq_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
+    "rotate_quant_kernel": ["packed_int4_convrot_amd/csrc/rotate_quant.hip",
+                            "packed_int4_convrot_amd/csrc/ck_device.h"],
+}
+
+
+def counter_passes(name):
+    """The --pmc argument of each counter pass (within one pass's hardware limits)."""
+    w = PROFILE_WORKLOADS[name]
+    if w["mops"] is None:
+        return ["FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU SQ_INSTS_LDS SQ_WAVES"]
+    return [w["mops"] + " SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVES",
+            "FETCH_SIZE", "WRITE_SIZE"]
+
+
+def profile_workload(name, reps=5):
+    """Run one kernel of the extras reps + 1 times, synchronising after each call, so that
+    counter passes see whole dispatches of it alone."""
+    import torch
+    import packed_int4_convrot_amd as ck
+    import workloads
+    dev = torch.device("cuda:0")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if name.startswith("w4a4_gemm"):
+        wl = "w4a4_linear_m8192_k3840_n3840_g64" if "k3840" in name else "w4a4_linear_m8192_k10240_n3840_g256"
+        inp = workloads.workload_inputs(wl)
+        x = bf16(inp["x"])
+        packed = torch.from_numpy(inp["packed"]).to(dev)
+        scl = bf16(inp["w_scales"])
+        codes4, rs = ck.rotate_quant_packed4(x, workloads.WORKLOADS[wl]["G"])
+        out = torch.empty((x.shape[0], packed.shape[0]), dtype=torch.bfloat16, device=dev)
+
+        def fn():
+            ck.gemm_packed4(codes4, rs, packed, scl, False, out=out)
+    elif name.startswith("awq"):
+        d = workloads.workload_inputs("awq_w4a16_gemv_m1_k3072_n18432")
+        rng = torch.Generator(device=dev).manual_seed(1)
+        xs = torch.randn((4096, 3072), generator=rng, device=dev).to(torch.bfloat16)
+        pk = torch.from_numpy(d["packed"]).to(dev)
+        s, z = bf16(d["scales"]), bf16(d["zeros"])
+        out = torch.empty((4096, 18432), dtype=torch.bfloat16, device=dev)
+
+        def fn():
+            ck.w4a16_gemm(xs, pk, s, z, out=out)
+    else:
+        wl = "rotate_quant_m8192_k10240_ld10752"
+        x = bf16(workloads.workload_inputs(wl)["x"])
+        K = workloads.WORKLOADS[wl]["K"]
+        codes = torch.empty((x.shape[0], K), dtype=torch.int8, device=dev)
+        rs = torch.empty((x.shape[0],), dtype=torch.float32, device=dev)
+
+        def fn():
+            ck.rotate_quant(x[:, :K], 64, 8, codes, rs)
+    for _ in range(reps + 1):
+        fn()
+        torch.cuda.synchronize()
+    print(json.dumps({"profile_workload": name, "dispatches": reps + 1}), flush=True)
+
+
+def write_counters(name, csvs, out_dir=None):
+    """Summarise the counter passes of one profile workload: each counter's mean per
+    dispatch of the workload's kernel, and what follows from them."""
+    import csv
+    w = PROFILE_WORKLOADS[name]
+    per = {}        # counter -> {(file, dispatch): value}
+    for path in csvs:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if w["kernel"] in row["Kernel_Name"]:
+                    key = (path, row["Dispatch_Id"])
+                    per.setdefault(row["Counter_Name"], {})[key] = float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no dispatches of %r in the given files" % w["kernel"])
+    mean = {c: sum(v.values()) / len(v) for c, v in per.items()}
+    rec = {"workload": name, "kernel": w["kernel"], "sources_sha": sources_sha(KERNEL_SOURCES[w["kernel"]]),
+           "dispatches_per_pass": min(len(v) for v in per.values()),
+           "counters_mean_per_dispatch": {c: round(v, 1) for c, v in sorted(mean.items())},
+           "algorithmic_bytes_per_launch": w["alg_bytes"]}
+    lines = []
+    try:
+        with open(TRAFFIC_FILE) as f:
+            cal = json.loads(f.read().split("JSON:", 1)[1])
+        fs, ws = cal["fetch_scale"], cal["write_scale"]
+    except (OSError, IndexError, ValueError, KeyError):
+        fs = ws = None
+    if fs is not None and "FETCH_SIZE" in mean and "WRITE_SIZE" in mean:
+        hbm = mean["FETCH_SIZE"] * 1024.0 * fs + mean["WRITE_SIZE"] * 1024.0 * ws
+        rec["fabric_bytes_per_launch"] = int(round(hbm))
+        rec["fabric_over_algorithmic"] = round(hbm / w["alg_bytes"], 4)
+        lines.append("Bytes between the L2s and the fabric per launch: FETCH_SIZE x %.4f + WRITE_SIZE x %.4f "
+                     "(the calibration factors of the headline traffic record) = %.1f MB, %.3f x the algorithmic "
+                     "%.1f MB.  FETCH_SIZE counts L2 misses, which the Infinity Cache serves in part: operands "
+                     "that several XCDs read each come from there, not from HBM, once per XCD."
+                     % (fs, ws, hbm / 1e6, hbm / w["alg_bytes"], w["alg_bytes"] / 1e6))
+    if w["mops"] and w["mops"] in mean:
+        ops = mean[w["mops"]] * 512.0
+        alg_ops = 2.0 * w["M"] * w["N"] * w["K"]
+        rec["mfma_ops_per_launch"] = ops
+        rec["mfma_ops_over_2MNK"] = round(ops / alg_ops, 4)
+        lines.append("MFMA ops per launch: %s x 512 = %.4g, %.4f x 2*M*N*K" % (w["mops"], ops, ops / alg_ops))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            per_simd = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0
+            rec["mfma_busy_cycles_per_simd"] = round(per_simd, 1)
+            lines.append("MFMA busy cycles per SIMD (1024 SIMDs): %.0f" % per_simd)
+    text = ("rocprofv3 counters of %s (kernel %s), mean per dispatch over the counter passes.\n\n"
+            "Commands (repository root, TMPDIR=/tmp; one pass per line):\n" % (name, w["kernel"]))
+    for i, pmc in enumerate(counter_passes(name)):
+        text += ("  rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s_%d -o run -- "
+                 "python3 bench.py --profile-workload %s\n" % (pmc, name, i, name))
+    text += "  python3 bench.py --write-counters %s <the run_counter_collection.csv files>\n\n" % name
+    text += "".join("%s\n" % line for line in lines)
+    text += "\nJSON: %s\n" % json.dumps(rec)
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "%s_counters.txt" % name)
+    with open(path, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def headline_alg_bytes(M, K, N):
     """Bytes the fused M = 1 step must move: packed weights, group scales, the bf16
     activation row and the bf16 output row."""
@@ -158,6 +301,11 @@ def main():
     if args.write_traffic:
         write_traffic(*args.write_traffic, alg_bytes=headline_alg_bytes(1, 3840, 10240))
         return
+    if args.write_counters:
+        if len(args.write_counters) < 2 or args.write_counters[0] not in PROFILE_WORKLOADS:
+            raise SystemExit("--write-counters WORKLOAD CSV...; workloads: %s" % ", ".join(sorted(PROFILE_WORKLOADS)))
+        write_counters(args.write_counters[0], args.write_counters[1:])
+        return
     if args.gpus != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path, run with --gpus 1",
               file=sys.stderr)
@@ -167,6 +315,9 @@ def main():
 
     if args.calibration_copy:
         calibration_copy()
+        return
+    if args.profile_workload:
+        profile_workload(args.profile_workload)
         return
 
     import packed_int4_convrot_amd as ck
