@@ -12,12 +12,15 @@
 // 64 weight rows = 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 (accumulators in
 // AGPRs).  Weights are the MFMA A operand, so a lane holds one output row and
 // four consecutive output columns per register group.  K step = 64 (one
-// scale group) in a ring of three stages filled by buffer_load ... lds, one
-// barrier per K step; the activation fragments of sub-step u + 1 are read,
-// and its weight fragments dequantised, while sub-step u multiplies.
+// scale group); a stage holds two K steps of both operands (256-byte x rows,
+// 64-byte weight rows), double-buffered and filled by buffer_load ... lds,
+// one barrier per stage.  The activation fragments of sub-step v + 1 are
+// read, and its weight fragments dequantised, while sub-step v multiplies.
 // MFMA operand layout: lane l holds 8 consecutive k of row l % 32, k = 8 (l /
 // 32) + e within a 16-wide sub-step; both operands use the same assignment,
 // with sub-step u of a K step covering k = 16 u .. 16 u + 15.
+#include <type_traits>
+
 #include "ck_device.h"
 #include "launch.h"
 
@@ -30,9 +33,10 @@ typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bfv __attribute__((ext_vector_type(8)));
 
-constexpr int kNst = 3;                       // ring stages (K steps)
-constexpr int kXRow = 128;                    // x bytes per row and K step (64 bf16)
-constexpr int kWRow = 32;                     // packed weight bytes per row and K step
+constexpr int kNst = 2;                       // stage buffers
+constexpr int kKS = 2;                        // K steps (64 wide) per stage
+constexpr int kXRow = 128 * kKS;              // x bytes per row and stage (bf16)
+constexpr int kWRow = 32 * kKS;               // packed weight bytes per row and stage
 // Block shape: NW waves side by side over the weight rows, each wave WM x WN
 // 32x32 tiles.
 template <int WM, int WN, int NW>
@@ -46,7 +50,6 @@ struct Shape {
     static constexpr int XLd = XBytes / kWaves >= 1024 ? XBytes / kWaves / 1024 : 1;
     static constexpr int WLanes = BN * kWRow / kWaves >= 1024 ? kWave : BN * kWRow / kWaves / 16;
     static constexpr int WLd = BN * kWRow / kWaves >= 1024 ? BN * kWRow / kWaves / 1024 : 1;
-    static constexpr int L = XLd + WLd;        // DMA instructions per wave and stage
     static constexpr int TW = WN * 32;         // output columns per wave
     static constexpr int Pitch = TW * 2 + 16;  // staged epilogue row, bytes
     static constexpr int Smem = kWaves * BM * Pitch > kNst * Stage ? kWaves * BM * Pitch : kNst * Stage;
@@ -54,11 +57,12 @@ struct Shape {
     static_assert(Smem <= 160 * 1024, "LDS");
 };
 
-// Slot swizzles measured conflict-free for 32 consecutive rows reading one
-// 16-byte slot (lane half in bit 0): 128-byte rows (r >> 1) & 7, 32-byte rows
-// ((r >> 2) ^ (r >> 3)) & 1.
-__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+// Slot swizzles for 32 consecutive rows reading one 16-byte slot each (lane
+// half in bit 0 of the slot): a 256-byte x row spans all 64 banks, so the
+// 16 rows of a quarter-wave take 16 distinct slots (r & 15); 64-byte weight
+// rows use (r >> 2) & 3, measured conflict-free for this pattern.
+__device__ __forceinline__ int swz16(int r) { return r & 15; }
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -72,13 +76,18 @@ __device__ __forceinline__ void wait_vmcnt()
 // operations round: bf16(bf16((q - 8) s) + z).  (q - 8) s is exact in fp32.
 __device__ __forceinline__ v8bfv dequant8(uint32_t d, float s, float m8s, float z)
 {
-    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
+    uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
+    // Opaque to the compiler, so that each code converts straight from its
+    // byte (v_cvt_f32_ubyte0..3) and each pair rounds to bf16 with one
+    // v_cvt_pk_bf16_f32, instead of the per-element forms it would choose.
+    asm("" : "+v"(lo), "+v"(hi));
     u32x4 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float q0 = (float)((lo >> (8 * i)) & 0xffu);
         const float q1 = (float)((hi >> (8 * i)) & 0xffu);
-        const uint32_t p = pack_bf16x2(__builtin_fmaf(q0, s, m8s), __builtin_fmaf(q1, s, m8s));
+        uint32_t p = pack_bf16x2(__builtin_fmaf(q0, s, m8s), __builtin_fmaf(q1, s, m8s));
+        asm("" : "+v"(p));
         r[i] = pack_bf16x2(__uint_as_float(p << 16) + z, __uint_as_float(p & 0xffff0000u) + z);
     }
     return __builtin_bit_cast(v8bfv, r);
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(NW * kWave) void awq_gemm_kernel(
     using S = Shape<WM, WN, NW>;
     constexpr int kWaves = NW;
     constexpr int kBM = S::BM, kBN = S::BN, kXBytes = S::XBytes, kStage = S::Stage, kTW = S::TW;
-    constexpr int kPitch = S::Pitch, kL = S::L;
+    constexpr int kPitch = S::Pitch;
     constexpr int kWM = WM, kWN = WN;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8 *smem = (lds_u8 *)smem_generic;
@@ -118,47 +127,53 @@ __global__ __launch_bounds__(NW * kWave) void awq_gemm_kernel(
         (void *)(packed + (int64_t)n0 * ldw), (short)0,
         (int)((int64_t)(min(N - n0, kBN) - 1) * ldw + K / 2), 0x00020000);
 
-    auto issue_stage = [&](int kt) {
-        lds_u8 *sa = smem + (kt % kNst) * kStage;
+    // Global -> LDS for stage st (K steps kKS st ..) into buffer st % kNst.
+    auto issue_stage = [&](int st) {
+        lds_u8 *sa = smem + (st % kNst) * kStage;
 #pragma unroll
         for (int j = 0; j < S::XLd; ++j) {
             const int q = (wave * S::XLd + j) * S::XLanes + lane;
             if (S::XLanes == kWave || lane < S::XLanes) {
-                const int r = q / 8, c = (q % 8) ^ swz8(q / 8);
+                const int r = q / 16, c = (q % 16) ^ swz16(q / 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     x_rsrc, (__attribute__((address_space(3))) void *)(sa + (wave * S::XLd + j) * S::XLanes * 16),
-                    16, (int)(r * ldx * 2) + kt * kXRow + 16 * c, 0, 0, 0);
+                    16, (int)(r * ldx * 2) + st * kXRow + 16 * c, 0, 0, 0);
             }
         }
 #pragma unroll
         for (int j = 0; j < S::WLd; ++j) {
             const int q = (wave * S::WLd + j) * S::WLanes + lane;
             if (S::WLanes == kWave || lane < S::WLanes) {
-                const int n = q / 2, c = (q % 2) ^ swz2(q / 2);
+                const int n = q / 4, c = (q % 4) ^ swz4(q / 4);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     w_rsrc,
                     (__attribute__((address_space(3))) void *)(sa + kXBytes + (wave * S::WLd + j) * S::WLanes * 16),
-                    16, (int)(n * ldw) + kt * kWRow + 16 * c, 0, 0, 0);
+                    16, (int)(n * ldw) + st * kWRow + 16 * c, 0, 0, 0);
             }
         }
     };
 
-    // Scale and zero point of this lane's two weight rows for K step kt.
-    uint32_t sz_raw[kWN][2];
-    auto load_sz = [&](int kt) {
+    // Scales and zero points of this lane's weight rows for the K steps of
+    // stage st (steps past the end repeat the last one; they are not used).
+    uint32_t sz_raw[kKS][kWN][2];
+    auto load_sz = [&](int st) {
 #pragma unroll
-        for (int j = 0; j < kWN; ++j) {
-            const int n = min(n0 + wave * kTW + j * 32 + l32, N - 1);
-            sz_raw[j][0] = scales[(int64_t)kt * N + n];
-            sz_raw[j][1] = zeros[(int64_t)kt * N + n];
+        for (int s = 0; s < kKS; ++s) {
+            const int kt = min(st * kKS + s, ksteps - 1);
+#pragma unroll
+            for (int j = 0; j < kWN; ++j) {
+                const int n = min(n0 + wave * kTW + j * 32 + l32, N - 1);
+                sz_raw[s][j][0] = scales[(int64_t)kt * N + n];
+                sz_raw[s][j][1] = zeros[(int64_t)kt * N + n];
+            }
         }
     };
 
-    const int sw8 = swz8(l32);
     const int x_base = l32 * kXRow;                                    // + i * 32 rows
+    const int x_swz = swz16(l32);
     const int w_row = wave * kTW + l32;                                // + j * 32 rows
     const int w_base = kXBytes + w_row * kWRow;
-    const int w_swz = swz2(w_row);
+    const int w_swz = swz4(w_row);
 
     v16f acc[kWM][kWN];
 #pragma unroll
@@ -169,75 +184,84 @@ __global__ __launch_bounds__(NW * kWave) void awq_gemm_kernel(
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.f;
 
-    // Ring invariant: DMA(kt), then the scale loads of kt, then DMA(kt + 1).
-    issue_stage(0);
-    load_sz(0);
-    if (ksteps > 1)
-        issue_stage(1);
-
-    for (int kt = 0; kt < ksteps; ++kt) {
-        // This wave's DMA for step kt has landed once at most the scale loads
-        // of kt and the DMA of kt + 1 are outstanding; the barrier extends
-        // that to all waves and retires every read of the slot refilled below.
-        if (kt + 1 < ksteps)
-            wait_vmcnt<kWN * 2 + kL>();
-        else
-            wait_vmcnt<0>();
+    // Sub-step v of a stage: K step v / 4, 16-wide slice v % 4 of it.  Lane
+    // half h holds k = 8 h .. 8 h + 7 of the slice: x slot 8 (v / 4) + 2 (v % 4)
+    // + h of its row, and dword 2 (v % 4) + h of the step's 32 packed bytes.
+    const int nstages = (ksteps + kKS - 1) / kKS;
+    // One stage of NSUB sub-steps (a full stage, or the single K step of a
+    // last stage that K leaves short), as straight-line code.
+    auto run_stage = [&](int st, auto nsub_c) {
+        constexpr int nsub = decltype(nsub_c)::value;
+        // This stage's DMA and scales have landed once each wave has waited
+        // for its own; the barrier extends that to the block and retires every
+        // read of the other buffer (stage st - 1), which is refilled below.
+        wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        float sc[kWN], m8s[kWN], zp[kWN];
+        float sc[kKS][kWN], m8s[kKS][kWN], zp[kKS][kWN];
 #pragma unroll
-        for (int j = 0; j < kWN; ++j) {
-            sc[j] = bf16_to_f32(sz_raw[j][0]);
-            m8s[j] = -8.f * sc[j];
-            zp[j] = bf16_to_f32(sz_raw[j][1]);
+        for (int s = 0; s < kKS; ++s)
+#pragma unroll
+            for (int j = 0; j < kWN; ++j) {
+                sc[s][j] = bf16_to_f32(sz_raw[s][j][0]);
+                m8s[s][j] = -8.f * sc[s][j];
+                zp[s][j] = bf16_to_f32(sz_raw[s][j][1]);
+            }
+        if (st + 1 < nstages) {
+            load_sz(st + 1);
+            issue_stage(st + 1);
         }
-        if (kt + 1 < ksteps)
-            load_sz(kt + 1);
-        if (kt + 2 < ksteps)
-            issue_stage(kt + 2);
-
-        const lds_u8 *sa = smem + (kt % kNst) * kStage;
-        // Packed codes of the step: sub-step u, half h is dword 2u + h of the
-        // row's 32 bytes, in 16-byte slot u / 2.
-        uint32_t pk[kWN][4];
+        const lds_u8 *sa = smem + (st % kNst) * kStage;
+        uint32_t pk[kKS][kWN][4];
 #pragma unroll
-        for (int j = 0; j < kWN; ++j)
+        for (int s = 0; s < nsub / 4; ++s)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                pk[j][u] = *(lds_u32 *)(sa + w_base + j * 32 * kWRow + 16 * ((u >> 1) ^ w_swz) +
-                                        4 * ((2 * u + h) & 3));
+            for (int j = 0; j < kWN; ++j)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    pk[s][j][u] = *(lds_u32 *)(sa + w_base + j * 32 * kWRow + 16 * ((2 * s + (u >> 1)) ^ w_swz) +
+                                               4 * ((2 * u + h) & 3));
         u32x4 xf[2][kWM];
+        auto read_x = [&](u32x4 (&f)[kWM], int v) {
+            const int slot = (8 * (v / 4) + 2 * (v % 4) + h) ^ x_swz;
 #pragma unroll
-        for (int i = 0; i < kWM; ++i)
-            xf[0][i] = *(lds_u32x4 *)(sa + x_base + i * 32 * kXRow + 16 * ((0 + h) ^ sw8));
+            for (int i = 0; i < kWM; ++i)
+                f[i] = *(lds_u32x4 *)(sa + x_base + i * 32 * kXRow + 16 * slot);
+        };
         v8bfv wf[2][kWN];
+        auto dequant = [&](v8bfv (&f)[kWN], int v) {
 #pragma unroll
-        for (int j = 0; j < kWN; ++j)
-            wf[0][j] = dequant8(pk[j][0], sc[j], m8s[j], zp[j]);
+            for (int j = 0; j < kWN; ++j)
+                f[j] = dequant8(pk[v / 4][j][v % 4], sc[v / 4][j], m8s[v / 4][j], zp[v / 4][j]);
+        };
+        read_x(xf[0], 0);
+        dequant(wf[0], 0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int v = 0; v < nsub; ++v) {
             // One scheduling region per sub-step: the reads and the
-            // dequantisation of sub-step u + 1 interleave with the MFMAs of u.
+            // dequantisation of sub-step v + 1 interleave with the MFMAs of v.
             __builtin_amdgcn_sched_barrier(0);
-            if (u + 1 < 4) {
-#pragma unroll
-                for (int i = 0; i < kWM; ++i)
-                    xf[(u + 1) & 1][i] =
-                        *(lds_u32x4 *)(sa + x_base + i * 32 * kXRow + 16 * ((2 * (u + 1) + h) ^ sw8));
-#pragma unroll
-                for (int j = 0; j < kWN; ++j)
-                    wf[(u + 1) & 1][j] = dequant8(pk[j][u + 1], sc[j], m8s[j], zp[j]);
+            if (v + 1 < nsub) {
+                read_x(xf[(v + 1) & 1], v + 1);
+                dequant(wf[(v + 1) & 1], v + 1);
             }
 #pragma unroll
             for (int i = 0; i < kWM; ++i) {
-                const v8bfv xb = __builtin_bit_cast(v8bfv, xf[u & 1][i]);
+                const v8bfv xb = __builtin_bit_cast(v8bfv, xf[v & 1][i]);
 #pragma unroll
                 for (int j = 0; j < kWN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[u & 1][j], xb, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[v & 1][j], xb, acc[i][j], 0, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    static_assert(kKS == 2, "a short last stage holds one K step");
+    issue_stage(0);
+    load_sz(0);
+    const int nfull = ksteps / kKS;
+    for (int st = 0; st < nfull; ++st)
+        run_stage(st, std::integral_constant<int, 4 * kKS>{});
+    if (nfull < nstages)
+        run_stage(nfull, std::integral_constant<int, 4>{});
 
     // Epilogue: lane l holds rows m = m0 + 32 i + l32 and, in register group
     // q, columns n = n0w + 32 j + 8 q + 4 h + (0..3).  Each wave stages its
