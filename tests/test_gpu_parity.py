@@ -641,7 +641,12 @@ def test_w4a4_packed_path_edge_shapes(M, K, N, G):
     assert np.array_equal(acc.astype(np.int64), oracle.int_gemm(host(codes), oracle.unpack(inp["packed"])))
 
 
-@pytest.mark.parametrize("M,K,N", [(33, 64, 16), (20, 32768, 16), (300, 192, 784)])
+@pytest.mark.parametrize("M,K,N", [
+    (33, 64, 16),            # a single K step: only the short last stage
+    (20, 32768, 16),         # longest K
+    (300, 192, 784),         # one two-step stage, then a short one
+    (200, 448, 96),          # three two-step stages, then a short one
+])
 def test_awq_gemm_edge_shapes(M, K, N):
     x, packed, s, z, bias = _awq_inputs(M, K, N, seed=K + N)
     out = host(ck.w4a16_gemm(bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z), bias=bf16_dev(bias)))
