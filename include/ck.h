@@ -249,7 +249,6 @@ int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   uint16_t *out, int64_t ldo, void *stream);
 
 /*
- * ck_quantize_weights/*
  * ck_quantize_weights  [SD] [AWQ]
  * Offline producer of the packed weights the matmuls consume, for a bf16
  * weight W [N, K] (row n = output column n):
