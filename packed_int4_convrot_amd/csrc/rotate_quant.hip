@@ -14,8 +14,8 @@
 //     wave (groups never straddle a wave or a chunk round);
 //   * the first three butterfly stages (strides 1, 2, 4) run inside the
 //     thread's 8 registers, the remaining log2(G/8) stages across lanes
-//     (DPP quad permutes for lane distance 1 and 2, ds_swizzle for 4..16, and
-//     ds_swizzle for every distance at G = 256, where the VALU is the limit);
+//     (DPP quad permute at G = 16, ds_swizzle from G = 64 on, which keeps the
+//     exchange off the VALU);
 //   * the fp32 values stay in registers until the row absmax is known
 //     (wave reduction, then LDS across waves); then every thread quantises and
 //     stores its own 8 codes with one 8-byte store.
@@ -77,10 +77,14 @@ __device__ __forceinline__ void fht(float (&v)[CPT][8], int lane)
                     v[i][r + h] = a - b;
                 }
     }
-    // At G = 256 the five cross-lane stages make the kernel VALU-bound
-    // (about 17 VALU instructions per element); exchanging through the LDS
-    // pipe instead of DPP measured 6-8% faster there, and slower at G <= 64.
-    constexpr bool SWZ = G >= 256;
+    // From G = 64 on, the kernel issues about as many VALU cycles as its HBM
+    // traffic takes, so it turns VALU-bound wherever the clock drops.  A DPP
+    // exchange costs a VALU move besides the fma; ds_swizzle runs on the LDS
+    // pipe, which has room here.  At G = 64 that takes the kernel from 14.8
+    // to 12.8 VALU instructions per element (591 -> 511 per thread at
+    // K = 10240), with the same time where HBM is the limit; at G = 256 it
+    // measured 6-8% faster.
+    constexpr bool SWZ = G >= 64;
     if constexpr (G >= 16) lane_stage<1, CPT, SWZ>(v, (lane & 1) ? -1.f : 1.f);
     if constexpr (G >= 32) lane_stage<2, CPT, SWZ>(v, (lane & 2) ? -1.f : 1.f);
     if constexpr (G >= 64) lane_stage<4, CPT, SWZ>(v, (lane & 4) ? -1.f : 1.f);
