@@ -139,7 +139,10 @@ __device__ __forceinline__ WeightScale weight_scale(float am)
     return WeightScale{sf > 0.f ? (1.0f / sf) * kInvSqrtG : 0.f, sb};
 }
 
-template <int G, int BLOCK, int CPT, int MODE>
+// FULL: every thread's CPT chunks lie inside the row (K = 8 * BLOCK * CPT),
+// so the loads and stores need no bounds test (the test and the zero fill
+// cost 5-6% of the kernel's VALU instructions).
+template <int G, int BLOCK, int CPT, int MODE, bool FULL>
 __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int K, float qmax, int8_t *__restrict__ codes,
     int64_t ldq, float *__restrict__ row_scales, float *__restrict__ xr, int64_t ldr,
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int c = t + i * BLOCK;
-        raw[i] = c < nchunk ? load_nt16(xrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        raw[i] = FULL || c < nchunk ? load_nt16(xrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
     }
     float v[CPT][8];
 #pragma unroll
@@ -206,14 +209,14 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
                 gm = fmaxf(gm, lane_xor<2>(gm));
                 gm = fmaxf(gm, lane_xor<4>(gm));
                 ws = weight_scale<G>(gm);
-                if (c < nchunk && (c & 7) == 0)
+                if ((FULL || c < nchunk) && (c & 7) == 0)
                     wscales[(int64_t)(c >> 3) * ldsc + m] = ws.bits;
             }
             uint32_t b[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 b[r] = rne_byte(fminf(fmaxf(v[i][r] * ws.inv_y, -7.f), 7.f));
-            if (c < nchunk) {
+            if (FULL || c < nchunk) {
                 const uint32_t ev = pack4(b[0], b[2], b[4], b[6]);
                 const uint32_t od = pack4(b[1], b[3], b[5], b[7]);
                 // two's-complement nibble ^ 8 = value + 8
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = t + i * BLOCK;
-            if (c < nchunk) {
+            if (FULL || c < nchunk) {
                 float4 *o = reinterpret_cast<float4 *>(orow + 8 * c);
                 o[0] = make_float4(v[i][0] * kInvSqrtG, v[i][1] * kInvSqrtG, v[i][2] * kInvSqrtG,
                                    v[i][3] * kInvSqrtG);
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 b[r] = rne_byte(v[i][r] * inv);
-            if (c < nchunk) {
+            if (FULL || c < nchunk) {
                 if constexpr (MODE == kPacked4) {
                     // byte j = nibble of column 2j | nibble of column 2j + 1 << 4
                     const uint32_t ev = pack4(b[0], b[2], b[4], b[6]);
@@ -277,11 +280,19 @@ hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_
     constexpr int kMaxCpt = BLOCK >= 1024 ? 4 : 8;
     if (cpt < 1 || cpt > kMaxCpt)
         return hipErrorInvalidValue;
-#define CK_RQ_CASE(C)                                                                         \
-    case C:                                                                                   \
-        if constexpr (C <= kMaxCpt)                                                           \
-            hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE>), grid, dim3(BLOCK), 0, \
-                               s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);       \
+    const bool full = K == 8 * BLOCK * cpt;
+#define CK_RQ_CASE(C)                                                                           \
+    case C:                                                                                     \
+        if constexpr (C <= kMaxCpt) {                                                           \
+            if (full)                                                                           \
+                hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE, true>), grid,        \
+                                   dim3(BLOCK), 0, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr,  \
+                                   wsc, ldsc);                                                  \
+            else                                                                                \
+                hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE, false>), grid,       \
+                                   dim3(BLOCK), 0, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, \
+                                   wsc, ldsc);                                                  \
+        }                                                                                       \
         break;
     switch (cpt) {
         CK_RQ_CASE(1)
