@@ -14,8 +14,8 @@
 //     wave (groups never straddle a wave or a chunk round);
 //   * the first three butterfly stages (strides 1, 2, 4) run inside the
 //     thread's 8 registers, the remaining log2(G/8) stages across lanes
-//     (DPP quad permute at G = 16, ds_swizzle from G = 64 on, which keeps the
-//     exchange off the VALU);
+//     (ds_swizzle from G = 64 on, which keeps the exchange off the VALU,
+//     except the lane-distance-1 stage at G = 16 and 256: DPP quad permute);
 //   * the fp32 values stay in registers until the row absmax is known
 //     (wave reduction, then LDS across waves); then every thread quantises and
 //     stores its own 8 codes with one 8-byte store.
@@ -80,12 +80,14 @@ __device__ __forceinline__ void fht(float (&v)[CPT][8], int lane)
     // From G = 64 on, the kernel issues about as many VALU cycles as its HBM
     // traffic takes, so it turns VALU-bound wherever the clock drops.  A DPP
     // exchange costs a VALU move besides the fma; ds_swizzle runs on the LDS
-    // pipe, which has room here.  At G = 64 that takes the kernel from 14.8
-    // to 12.8 VALU instructions per element (591 -> 511 per thread at
-    // K = 10240), with the same time where HBM is the limit; at G = 256 it
-    // measured 6-8% faster.
+    // pipe instead.  At G = 64 all three exchanges use it (12.8 rather than
+    // 14.8 VALU instructions per element).  At G = 256 five swizzles per
+    // element overload the LDS pipe (wave-cycles waiting to issue LDS
+    // instructions: 11.5 M per launch, against 1.6 M at G = 64), so the
+    // distance-1 stage goes through DPP: 4 swizzles and about 15 VALU
+    // instructions per element, measured 6% faster than all-swizzle.
     constexpr bool SWZ = G >= 64;
-    if constexpr (G >= 16) lane_stage<1, CPT, SWZ>(v, (lane & 1) ? -1.f : 1.f);
+    if constexpr (G >= 16) lane_stage<1, CPT, SWZ && G < 256>(v, (lane & 1) ? -1.f : 1.f);
     if constexpr (G >= 32) lane_stage<2, CPT, SWZ>(v, (lane & 2) ? -1.f : 1.f);
     if constexpr (G >= 64) lane_stage<4, CPT, SWZ>(v, (lane & 4) ? -1.f : 1.f);
     if constexpr (G >= 128) lane_stage<8, CPT, SWZ>(v, (lane & 8) ? -1.f : 1.f);
