@@ -373,6 +373,18 @@ def main():
     alg_bytes = headline_alg_bytes(M, K, N)
     achieved = alg_bytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(alg_bytes)
+    # Spread: the same graph replayed again, each replay's mean step time.
+    reps = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g_steps.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        reps.append(a.elapsed_time(b) / args.steps * 1e3)
+    reps.sort()
+    spread = {"replays": len(reps), "steps_each": args.steps, "p10_us": round(reps[1], 3),
+              "median_us": round((reps[9] + reps[10]) / 2, 3), "p90_us": round(reps[17], 3)}
     eager_us = _time_eager(torch, step, stream, min(args.steps, 100)) * 1.0
     log("bench: step %.3f us (wall %.2f us), %.0f GB/s packed, eager %.2f us/step" %
         (ms_step * 1e3, wall / args.steps * 1e6, value, eager_us))
@@ -400,6 +412,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(ms_step * 1e3, 3)},
         "eager_us_per_step": round(eager_us, 3),
+        "us_per_step_over_replays": spread,
+        "gfx_clock_mhz": gfx_clock_mhz(torch, g_steps),
     }
 
     # ------------------------------------------------------------ extras
@@ -413,6 +427,42 @@ def main():
         result["cpu_baseline"] = cpu_baseline(workloads, inp, G, packed_bytes)
 
     print(json.dumps(result), flush=True)
+
+
+def gfx_clock_mhz(torch, graph, seconds=1.5):
+    """GFX clock (MHz, mean over the XCDs) read with amd-smi while `graph` is replayed
+    back to back for about `seconds`; the median of the readings, or None where amd-smi
+    is missing or prints something else."""
+    import subprocess
+    import threading
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                d = json.loads(r.stdout)
+                d = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                vals = [v["clk"]["value"] for k, v in d["clock"].items() if k.startswith("gfx")]
+                if vals:
+                    samples.append(sum(vals) / len(vals))
+            except Exception:
+                return
+
+    t = threading.Thread(target=poll, daemon=True)
+    t0 = time.time()
+    graph.replay()
+    t.start()
+    while time.time() - t0 < seconds:
+        graph.replay()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join(timeout=15)
+    if not samples:
+        return None
+    samples.sort()
+    return round(samples[len(samples) // 2], 1)
 
 
 def capture(torch, fn, n):
@@ -532,7 +582,9 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
         gm8 = _time(lambda i: ck.gemm_q(codes, rs8, packed, scl, False, out=out), stream, 20)
         ops = 2.0 * M * N * K
         rq_bytes = M * K * 2 + M * K // 2 + M * 4
+        clk = gfx_clock_mhz(torch, capture(torch, lambda i: ck.gemm_packed4(codes4, rs, packed, scl, False, out=out), 40))
         res[name] = {"linear_us": round(lin, 2), "rotate_quant_us": round(rq, 2), "gemm_us": round(gm, 2),
+                     "gemm_gfx_clock_mhz": clk,
                      "gemm_int8_TOPS": round(ops / gm / 1e6, 1),
                      "gemm_frac_int8_peak": round(ops / gm / 1e6 / INT8_PEAK_TOPS, 4),
                      "linear_int8_TOPS": round(ops / lin / 1e6, 1),
@@ -553,9 +605,11 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
     rq_bytes = M * K * 2 + M * K + M * 4
     for G in w["Gs"]:
         us = _time(lambda i: ck.rotate_quant(xs[i % 2][:, :K], G, 8, codes, rs), stream, 20)
+        clk = gfx_clock_mhz(torch, capture(torch, lambda i: ck.rotate_quant(xs[i % 2][:, :K], G, 8, codes, rs), 40),
+                            seconds=1.0)
         res["rotate_quant_m8192_k10240_ld10752_g%d" % G] = {
             "us": round(us, 2), "GBps": round(rq_bytes / us / 1e3, 1),
-            "frac_hbm": round(rq_bytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+            "frac_hbm": round(rq_bytes / us / 1e3 / HBM_PEAK_GBS, 4), "gfx_clock_mhz": clk}
     del xs
     log("bench: rotate-quant done")
 
