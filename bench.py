@@ -51,10 +51,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # 1000 warm-up steps are about 7 ms: enough for the clocks to leave their idle state
-    # before the timed replay (20 steps left the first timed replay ~4% slow).
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--no-extras", action="store_true", help="skip the secondary measurements")
+    # 30000 warm-up steps are about 0.2 s of the headline step: the clocks of a chip
+    # coming out of idle keep rising for tens of milliseconds under load.
+    ap.add_argument("--warmup", type=int, default=30000)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary measurements and the clock readings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=32, help="weight copies cycled through (cold cache)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -308,6 +309,8 @@ def main():
             raise SystemExit("--write-counters WORKLOAD CSV...; workloads: %s" % ", ".join(sorted(PROFILE_WORKLOADS)))
         write_counters(args.write_counters[0], args.write_counters[1:])
         return
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     if args.gpus != 1:
         print("bench.py measures one MI355X: this build has no multi-GPU path, run with --gpus 1",
               file=sys.stderr)
@@ -355,9 +358,15 @@ def main():
     def step(i):
         ck.linear(x, G, 8, packs[i % args.copies], scls[i % args.copies], True, out=out, workspace=ws)
 
-    g_warm = capture(torch, step, args.warmup)
+    # W warm-up steps: W mod K steps from a graph of their own, then W // K replays
+    # of the timed graph itself, so that the timed replay is not that graph's first
+    # (a graph's first replay measured ~3-5% slower than the next ones).
     g_steps = capture(torch, step, args.steps)
-    g_warm.replay()
+    rest = args.warmup % args.steps
+    if rest:
+        capture(torch, step, rest).replay()
+    for _ in range(args.warmup // args.steps):
+        g_steps.replay()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -415,7 +424,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(ms_step * 1e3, 3)},
         "eager_us_per_step": round(eager_us, 3),
         "us_per_step_over_replays": spread,
-        "gfx_clock_mhz": gfx_clock_mhz(torch, capture(torch, step, 2000)),
+        "gfx_clock_mhz": None if args.no_extras else gfx_clock_mhz(torch, capture(torch, step, 2000)),
     }
 
     # ------------------------------------------------------------ extras
@@ -512,13 +521,25 @@ def _time_eager(torch, fn, stream, iters, warmup=3):
     return a.elapsed_time(b) / iters * 1e3  # us
 
 
-def _time(fn, stream, iters, warmup=3):
-    """Microseconds per call, from a HIP graph of `iters` calls replayed once."""
+WARM_S = 0.2   # seconds of the same work before each secondary measurement
+
+
+def _time(fn, stream, iters, warmup=3, warm_s=None):
+    """Microseconds per call, from a HIP graph of `iters` calls replayed once, after a
+    graph of `warmup` calls has been replayed for at least `warm_s` seconds (WARM_S by
+    default).  Under sustained load the chip's clocks keep rising for tens of
+    milliseconds: the M = 8192 GEMM at K = 3840 times 116 us per call after 3 warm-up
+    calls, 107 us after 100 and 97 us from 300 on, so each measurement first runs
+    long enough to reach that steady state."""
     import torch
     g_w = capture(torch, fn, warmup)
     g = capture(torch, fn, iters)
-    g_w.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        g_w.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= (WARM_S if warm_s is None else warm_s):
+            break
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     g.replay()
@@ -669,9 +690,7 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
     xs = (torch.randn((M, K), generator=rng, device=dev)).to(torch.bfloat16)
     pk = u8(d["packed"])
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    # The first tens of launches on fresh buffers run up to 20% slower than
-    # the steady state, so this one warms up for 30 launches before timing 20.
-    us = _time(lambda i: ck.w4a16_gemm(xs, pk, s, z, out=out), stream, 20, warmup=30)
+    us = _time(lambda i: ck.w4a16_gemm(xs, pk, s, z, out=out), stream, 20)
     fl = 2.0 * M * N * K
     res["awq_w4a16_gemm_m%d_k%d_n%d" % (M, K, N)] = {
         "us": round(us, 1), "bf16_TFLOPS": round(fl / us / 1e6, 1),
