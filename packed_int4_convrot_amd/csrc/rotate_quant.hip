@@ -31,8 +31,7 @@ namespace {
 
 // Value held by the lane whose index differs in bit log2(MASK).  DPP moves
 // are VALU instructions, ds_swizzle runs on the LDS pipe; SWZ selects the
-// swizzle for every distance, which moves VALU work off the butterflies when
-// they are the bottleneck (G = 256).
+// swizzle for every distance (see fht() for where each is used).
 template <int MASK, bool SWZ = false>
 __device__ __forceinline__ float lane_xor(float v)
 {
