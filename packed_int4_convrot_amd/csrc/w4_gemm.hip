@@ -24,6 +24,11 @@
 //     right after that barrier, so LDS latency is never waited on between
 //     MFMAs; the DMA of stage t + 2 is issued at the same barrier into the
 //     buffer that stage t has just finished reading;
+//   * the per-channel and int32 tiles run each K step in a fixed order: the
+//     nibble decodes sit between the MFMA pairs, and the operands of the next
+//     step's first MFMAs are decoded under this step's last ones, so the
+//     matrix core never waits for a run of decode instructions (4-5% faster
+//     at M = 8192 than the compiler's own order);
 //   * LDS rows are unpadded; the 16-byte slots inside a row are XOR-swizzled
 //     by row (swizzles measured conflict-free with SQ_LDS_BANK_CONFLICT for
 //     these read patterns); the DMA writes lanes contiguously, so each lane
@@ -220,6 +225,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                     y[i][j][r] = 0.f;
             }
 
+    // MFMA operands of K half s: weight tile j and activation tile i.
+    auto w_operand = [](const Frag &f, int s, int j) { return w4_operand_x16(f.b[j][2 * s], f.b[j][2 * s + 1]); };
+    auto a_operand = [](const Frag &f, int s, int i) {
+        if constexpr (A4)
+            return a4_operand_x16(f.a[0][i][2 * s], f.a[0][i][2 * s + 1]);
+        else
+            return act_perm16(f.a[s][i][0], f.a[s][i][1], f.a[s][i][2], f.a[s][i][3]);
+    };
+
     // One K step on fragments f; kt is the global K step (per-group scale row).
     auto compute = [&](const Frag &f, int kt) {
         uint16_t sc[PER_GROUP ? WN : 1];
@@ -233,14 +247,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
             v4i bf[WN];
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-                bf[j] = w4_operand_x16(f.b[j][2 * s], f.b[j][2 * s + 1]);
+                bf[j] = w_operand(f, s, j);
 #pragma unroll
             for (int i = 0; i < WM; ++i) {
-                v4i af;
-                if constexpr (A4)
-                    af = a4_operand_x16(f.a[0][i][2 * s], f.a[0][i][2 * s + 1]);
-                else
-                    af = act_perm16(f.a[s][i][0], f.a[s][i][1], f.a[s][i][2], f.a[s][i][3]);
+                const v4i af = a_operand(f, s, i);
 #pragma unroll
                 for (int j = 0; j < WN; ++j) {
                     if constexpr (TRANS)  // D^T[n][m]: lane = row m, registers = columns n
@@ -264,8 +274,80 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
         }
     };
 
-    constexpr int L = A_LD + B_LD;  // DMA instructions per wave and stage
+    // The same K step for the transposed 4 x 2 wave tile, in a fixed order.
+    // The step's 16 MFMAs run as 8 pairs (one activation tile, both weight
+    // tiles); the decodes each pair needs are placed between earlier pairs,
+    // and the operands of the next K step's first pair (its head: both weight
+    // tiles and activation tile 0 of K half 0) are decoded under this step's
+    // last pairs.  Left to itself the compiler decoded a whole K half in one
+    // run ahead of its MFMAs, and a step's head could not start before the
+    // step: with two waves per SIMD the matrix core then sat idle.  The fences
+    // keep every pair's decodes (6 VALU ops per tile) inside the previous
+    // pair's 64 MFMA cycles.  fn holds the next step's fragments; the last
+    // stage runs the plain form (its K steps may end early).
+    constexpr bool ILV = TRANS && WM == 4 && WN == 2;
+    struct Head {
+        v4i b[WN];
+        v4i a;
+    };
+    auto decode_head = [&](Head &hd, const Frag &f) {
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+            hd.b[j] = w_operand(f, 0, j);
+        hd.a = a_operand(f, 0, 0);
+    };
+    auto compute_ilv = [&](const Frag &f, const Head &hd, const Frag &fn, Head &hn) {
+        if constexpr (ILV) {
+            v4i b1[WN], a0[WM], a1[WM];
+            auto pair = [&](int i, const v4i(&bf)[WN], const v4i &af) {
+#pragma unroll
+                for (int j = 0; j < WN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af, acc[i][j], 0, 0, 0);
+            };
+            __builtin_amdgcn_sched_barrier(0);
+            pair(0, hd.b, hd.a);
+            a0[1] = a_operand(f, 0, 1);
+            b1[0] = w_operand(f, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(1, hd.b, a0[1]);
+            a0[2] = a_operand(f, 0, 2);
+            b1[1] = w_operand(f, 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(2, hd.b, a0[2]);
+            a0[3] = a_operand(f, 0, 3);
+            a1[0] = a_operand(f, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(3, hd.b, a0[3]);
+            a1[1] = a_operand(f, 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(0, b1, a1[0]);
+            a1[2] = a_operand(f, 1, 2);
+            hn.b[0] = w_operand(fn, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(1, b1, a1[1]);
+            a1[3] = a_operand(f, 1, 3);
+            hn.b[1] = w_operand(fn, 0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(2, b1, a1[2]);
+            hn.a = a_operand(fn, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            pair(3, b1, a1[3]);
+        }
+    };
+    // K step u (not a stage's last) of stage buffer b, with step u + 1 read ahead.
     Frag fr[2];
+    Head hd[2];
+    auto step = [&](int b, int u, int kt) {
+        read_frag(fr[(u + 1) & 1], b, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ILV)
+            compute_ilv(fr[u & 1], hd[u & 1], fr[(u + 1) & 1], hd[(u + 1) & 1]);
+        else
+            compute(fr[u & 1], kt);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    constexpr int L = A_LD + B_LD;  // DMA instructions per wave and stage
     issue_stage(0, 0);
     if (nstages > 1) {
         issue_stage(1, 1);
@@ -281,20 +363,16 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     read_frag(fr[0], 0, 0);
+    if constexpr (ILV)
+        decode_head(hd[0], fr[0]);
 
     // Stages that have a successor: straight-line K steps.
     int st = 0;
     for (; st + 1 < nstages; ++st) {
         const int b = st & 1;
 #pragma unroll
-        for (int u = 0; u + 1 < KSUB; ++u) {
-            // The fences keep the reads of step u + 1 ahead of the MFMAs of
-            // step u, so that those MFMAs wait only for their own fragments.
-            read_frag(fr[(u + 1) & 1], b, u + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(fr[u & 1], st * KSUB + u);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int u = 0; u + 1 < KSUB; ++u)
+            step(b, u, st * KSUB + u);
         // Every read of this buffer has returned once each wave has waited
         // for its own, and the next stage has landed once each wave has
         // waited for its own DMA; the barrier extends both to the block, so
@@ -307,7 +385,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
             issue_stage(st + 2, b);
         read_frag(fr[0], b ^ 1, 0);
         __builtin_amdgcn_sched_barrier(0);
-        compute(fr[(KSUB - 1) & 1], st * KSUB + KSUB - 1);
+        if constexpr (ILV)
+            compute_ilv(fr[(KSUB - 1) & 1], hd[(KSUB - 1) & 1], fr[0], hd[0]);
+        else
+            compute(fr[(KSUB - 1) & 1], st * KSUB + KSUB - 1);
         __builtin_amdgcn_sched_barrier(0);
     }
     // The last stage, possibly partial.
