@@ -6,19 +6,20 @@
 // the dynamic per-row quantisation happen in one pass over x, so the rotated
 // tensor is never written out.
 //
-// Work layout (one workgroup per row, 128 threads up to K = 8192, 256 up to
-// 16384, 1024 beyond):
-//   * thread t owns chunks c = t, t + BLOCK, ... of 8 consecutive bf16 (16 B),
-//     loaded with one coalesced 16-byte load each;
-//   * a group of G columns is G/8 chunks held by G/8 neighbouring lanes of one
-//     wave (groups never straddle a wave or a chunk round);
-//   * the first three butterfly stages (strides 1, 2, 4) run inside the
-//     thread's 8 registers, the remaining log2(G/8) stages across lanes
+// Work layout (one workgroup per row of 128, 256 or 1024 threads, by K):
+//   * thread t owns chunks c = t, t + BLOCK, ... of CW consecutive bf16
+//     (CW = 8: one coalesced 16-byte load; CW = 16, used for activation codes
+//     from G = 64 on: two);
+//   * a group of G columns is G/CW chunks held by G/CW neighbouring lanes of
+//     one wave (groups never straddle a wave or a chunk round);
+//   * the first log2(CW) butterfly stages (strides 1 .. CW/2) run inside the
+//     thread's registers, the remaining log2(G/CW) stages across lanes
 //     (ds_swizzle from G = 64 on, which keeps the exchange off the VALU,
-//     except the lane-distance-1 stage at G = 16 and 256: DPP quad permute);
+//     except the lane-distance-1 stage of 8-column chunks at G = 16 and 256:
+//     DPP quad permute);
 //   * the fp32 values stay in registers until the row absmax is known
 //     (wave reduction, then LDS across waves); then every thread quantises and
-//     stores its own 8 codes with one 8-byte store.
+//     stores its own CW codes with one store.
 // The transform is kept unnormalised (y = sqrt(G) * xr).  Because sqrt(G) is a
 // power of two, fp32(qmax / max|y|) * y equals fp32(qmax / max|xr|) * xr
 // exactly, so the codes match the normalised definition bit for bit; the row
@@ -49,27 +50,27 @@ __device__ __forceinline__ float lane_xor(float v)
 
 // One cross-lane butterfly stage: the lower lane of each pair keeps u + v,
 // the upper lane v' = u - v (written as fma(v, -1, u), same rounding).
-template <int MASK, int CPT, bool SWZ>
-__device__ __forceinline__ void lane_stage(float (&v)[CPT][8], float sgn)
+template <int MASK, int CPT, int CW, bool SWZ>
+__device__ __forceinline__ void lane_stage(float (&v)[CPT][CW], float sgn)
 {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
+        for (int r = 0; r < CW; ++r) {
             const float p = lane_xor<MASK, SWZ>(v[i][r]);
             v[i][r] = __builtin_fmaf(v[i][r], sgn, p);
         }
 }
 
-template <int G, int CPT>
-__device__ __forceinline__ void fht(float (&v)[CPT][8], int lane)
+template <int G, int CPT, int CW>
+__device__ __forceinline__ void fht(float (&v)[CPT][CW], int lane)
 {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
 #pragma unroll
-        for (int h = 1; h < 8; h <<= 1)
+        for (int h = 1; h < CW && h < G; h <<= 1)
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
+            for (int r = 0; r < CW; ++r)
                 if ((r & h) == 0) {
                     const float a = v[i][r], b = v[i][r + h];
                     v[i][r] = a + b;
@@ -84,13 +85,18 @@ __device__ __forceinline__ void fht(float (&v)[CPT][8], int lane)
     // element overload the LDS pipe (wave-cycles waiting to issue LDS
     // instructions: 11.5 M per launch, against 1.6 M at G = 64), so the
     // distance-1 stage goes through DPP: 4 swizzles and about 15 VALU
-    // instructions per element, measured 6% faster than all-swizzle.
-    constexpr bool SWZ = G >= 64;
-    if constexpr (G >= 16) lane_stage<1, CPT, SWZ && G < 256>(v, (lane & 1) ? -1.f : 1.f);
-    if constexpr (G >= 32) lane_stage<2, CPT, SWZ>(v, (lane & 2) ? -1.f : 1.f);
-    if constexpr (G >= 64) lane_stage<4, CPT, SWZ>(v, (lane & 4) ? -1.f : 1.f);
-    if constexpr (G >= 128) lane_stage<8, CPT, SWZ>(v, (lane & 8) ? -1.f : 1.f);
-    if constexpr (G >= 256) lane_stage<16, CPT, SWZ>(v, (lane & 16) ? -1.f : 1.f);
+    // instructions per element, measured 6% faster than all-swizzle (these
+    // figures are for 8-column chunks).  With 16-column chunks the stride-8
+    // stage is in registers and every remaining exchange goes through
+    // ds_swizzle (at most 4 per element at G = 256).
+    constexpr int L = G / CW;  // lanes per group
+    constexpr bool SWZ = G >= 64 || CW == 16;
+    constexpr bool SWZ1 = CW == 16 || (G >= 64 && G < 256);
+    if constexpr (L >= 2) lane_stage<1, CPT, CW, SWZ1>(v, (lane & 1) ? -1.f : 1.f);
+    if constexpr (L >= 4) lane_stage<2, CPT, CW, SWZ>(v, (lane & 2) ? -1.f : 1.f);
+    if constexpr (L >= 8) lane_stage<4, CPT, CW, SWZ>(v, (lane & 4) ? -1.f : 1.f);
+    if constexpr (L >= 16) lane_stage<8, CPT, CW, SWZ>(v, (lane & 8) ? -1.f : 1.f);
+    if constexpr (L >= 32) lane_stage<16, CPT, CW, SWZ>(v, (lane & 16) ? -1.f : 1.f);
 }
 
 __device__ __forceinline__ float wave_max(float v)
@@ -143,7 +149,7 @@ __device__ __forceinline__ WeightScale weight_scale(float am)
 // FULL: every thread's CPT chunks lie inside the row (K = 8 * BLOCK * CPT),
 // so the loads and stores need no bounds test (the test and the zero fill
 // cost 5-6% of the kernel's VALU instructions).
-template <int G, int BLOCK, int CPT, int MODE, bool FULL>
+template <int G, int BLOCK, int CPT, int MODE, bool FULL, int CW>
 __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int K, float qmax, int8_t *__restrict__ codes,
     int64_t ldq, float *__restrict__ row_scales, float *__restrict__ xr, int64_t ldr,
@@ -151,38 +157,42 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 {
     constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
     static_assert(G == 16 || G == 64 || G == 256, "G");
+    static_assert(CW == 8 || (CW == 16 && (MODE == kCodes8 || MODE == kPacked4)), "chunk width");
     __shared__ float wmax[BLOCK / kWave];
 
     const int64_t m = blockIdx.x;
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
-    const int nchunk = K >> 3;
+    const int nchunk = K / CW;
     const uint16_t *xrow = x + m * ldx;
 
-    u32x4 raw[CPT];
+    constexpr int LD = CW / 8;  // 16-byte loads per chunk
+    u32x4 raw[CPT][LD];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int c = t + i * BLOCK;
-        raw[i] = FULL || c < nchunk ? load_nt16(xrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
-    float v[CPT][8];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const uint32_t w[4] = {raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[i][2 * j] = __uint_as_float(w[j] << 16);
-            v[i][2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-        }
+        for (int q = 0; q < LD; ++q)
+            raw[i][q] = FULL || c < nchunk ? load_nt16(xrow + CW * c + 8 * q) : u32x4{0u, 0u, 0u, 0u};
     }
+    float v[CPT][CW];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int q = 0; q < LD; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[i][8 * q + 2 * j] = __uint_as_float(raw[i][q][j] << 16);
+                v[i][8 * q + 2 * j + 1] = __uint_as_float(raw[i][q][j] & 0xffff0000u);
+            }
 
-    fht<G, CPT>(v, lane);
+    fht<G, CPT, CW>(v, lane);
 
     float am = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+        for (int r = 0; r < CW; ++r)
             am = fmaxf(am, fabsf(v[i][r]));
     am = wave_max(am);
     if (lane == 0)
@@ -248,22 +258,33 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = t + i * BLOCK;
-            uint32_t b[8];
+            uint32_t b[CW];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
+            for (int r = 0; r < CW; ++r)
                 b[r] = rne_byte(v[i][r] * inv);
-            if (FULL || c < nchunk) {
+            // Per 8 columns: one dword of packed nibbles (byte j = nibble of
+            // column 2j | nibble of column 2j + 1 << 4) or two dwords of bytes.
+            uint32_t o[MODE == kPacked4 ? CW / 8 : CW / 4];
+#pragma unroll
+            for (int q = 0; q < CW / 8; ++q) {
+                const uint32_t *bq = b + 8 * q;
                 if constexpr (MODE == kPacked4) {
-                    // byte j = nibble of column 2j | nibble of column 2j + 1 << 4
-                    const uint32_t ev = pack4(b[0], b[2], b[4], b[6]);
-                    const uint32_t od = pack4(b[1], b[3], b[5], b[7]);
-                    reinterpret_cast<uint32_t *>(crow)[c] = (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
+                    const uint32_t ev = pack4(bq[0], bq[2], bq[4], bq[6]);
+                    const uint32_t od = pack4(bq[1], bq[3], bq[5], bq[7]);
+                    o[q] = (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
                 } else {
-                    uint2 o;
-                    o.x = pack4(b[0], b[1], b[2], b[3]);
-                    o.y = pack4(b[4], b[5], b[6], b[7]);
-                    reinterpret_cast<uint2 *>(crow)[c] = o;
+                    o[2 * q] = pack4(bq[0], bq[1], bq[2], bq[3]);
+                    o[2 * q + 1] = pack4(bq[4], bq[5], bq[6], bq[7]);
                 }
+            }
+            if (FULL || c < nchunk) {
+                constexpr int NO = sizeof(o) / sizeof(o[0]);
+                if constexpr (NO == 1)
+                    reinterpret_cast<uint32_t *>(crow)[c] = o[0];
+                else if constexpr (NO == 2)
+                    reinterpret_cast<uint2 *>(crow)[c] = uint2{o[0], o[1]};
+                else
+                    reinterpret_cast<uint4 *>(crow)[c] = uint4{o[0], o[1], o[2], o[3]};
             }
         }
         if (t == 0)
@@ -271,26 +292,27 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
     }
 }
 
-// BLOCK threads, CPT chunks of 8 columns per thread.  CPT is capped so that
-// the row stays in VGPRs without spilling: 8 at 256 threads, 4 at 1024.
-template <int G, int BLOCK, int MODE>
+// BLOCK threads, CPT chunks of CW columns per thread.  CPT is capped so that
+// the row stays in VGPRs without spilling: 64 columns per thread up to 256
+// threads (80 with 16-column chunks), 32 at 1024.
+template <int G, int BLOCK, int MODE, int CW>
 hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_t ldx, int K,
                     float qmax, int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr,
                     uint16_t *wsc, int64_t ldsc)
 {
-    constexpr int kMaxCpt = BLOCK >= 1024 ? 4 : 8;
+    constexpr int kMaxCpt = BLOCK >= 1024 ? 32 / CW : CW == 16 ? 5 : 8;
     if (cpt < 1 || cpt > kMaxCpt)
         return hipErrorInvalidValue;
-    const bool full = K == 8 * BLOCK * cpt;
+    const bool full = K == CW * BLOCK * cpt;
 #define CK_RQ_CASE(C)                                                                           \
     case C:                                                                                     \
         if constexpr (C <= kMaxCpt) {                                                           \
             if (full)                                                                           \
-                hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE, true>), grid,        \
+                hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE, true, CW>), grid,    \
                                    dim3(BLOCK), 0, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr,  \
                                    wsc, ldsc);                                                  \
             else                                                                                \
-                hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE, false>), grid,       \
+                hipLaunchKernelGGL((rotate_quant_kernel<G, BLOCK, C, MODE, false, CW>), grid,   \
                                    dim3(BLOCK), 0, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, \
                                    wsc, ldsc);                                                  \
         }                                                                                       \
@@ -316,21 +338,42 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
                      int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr,
                      uint16_t *wsc = nullptr, int64_t ldsc = 0)
 {
-    const int nchunk = K / 8;
     const dim3 grid((unsigned)M);
-    // Rows of up to 8192 columns: 128 threads with up to 8 chunks each, which
-    // measured 3-10% faster than 256 threads at K = 2048 and 3840 (more loads
-    // in flight per thread, more resident rows per CU).
-    if (nchunk <= 128 * 8) {
-        const int cpt = (nchunk + 127) / 128;
-        return launch_g<G, 128, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
+    if constexpr ((MODE == kCodes8 || MODE == kPacked4) && G >= 64) {
+        // Activation codes from G = 64 on: 16-column chunks (K is a multiple
+        // of G).  Up to 10240 columns 128 threads of up to 5 chunks, then 256,
+        // then 1024 threads of up to 2.  The in-register distance-8 stage and
+        // the longer rows per thread take 1-2 VALU instructions per element
+        // off (13.3 instead of 15.3 at G = 256, K = 10240), which is what
+        // sets the time here: 5-10% faster at G = 64 and 256.  At G = 16 the
+        // kernel is HBM-bound and the 8-column layout, whose loads fill whole
+        // cache lines per instruction (a 16-column chunk is two 16-byte loads
+        // 32 bytes apart), measured 8% faster.
+        const int nchunk = K / 16;
+        if (nchunk <= 128 * 5)
+            return launch_g<G, 128, MODE, 16>((nchunk + 127) / 128, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr,
+                                              ldr, wsc, ldsc);
+        if (nchunk <= 256 * 5)
+            return launch_g<G, 256, MODE, 16>((nchunk + 255) / 256, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr,
+                                              ldr, wsc, ldsc);
+        return launch_g<G, 1024, MODE, 16>((nchunk + 1023) / 1024, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr,
+                                           ldr, wsc, ldsc);
+    } else {
+        const int nchunk = K / 8;
+        // Rows of up to 8192 columns: 128 threads with up to 8 chunks each, which
+        // measured 3-10% faster than 256 threads at K = 2048 and 3840 (more loads
+        // in flight per thread, more resident rows per CU).
+        if (nchunk <= 128 * 8) {
+            const int cpt = (nchunk + 127) / 128;
+            return launch_g<G, 128, MODE, 8>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
+        }
+        if (nchunk <= 256 * 8) {
+            const int cpt = (nchunk + 255) / 256;
+            return launch_g<G, 256, MODE, 8>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
+        }
+        const int cpt = (nchunk + 1023) / 1024;
+        return launch_g<G, 1024, MODE, 8>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
     }
-    if (nchunk <= 256 * 8) {
-        const int cpt = (nchunk + 255) / 256;
-        return launch_g<G, 256, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
-    }
-    const int cpt = (nchunk + 1023) / 1024;
-    return launch_g<G, 1024, MODE>(cpt, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
 }
 
 }  // namespace

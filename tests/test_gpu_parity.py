@@ -66,6 +66,35 @@ def test_rotate_quant_matches_oracle(G, bits):
     assert s[7] == 1.0 and s[95] == 1.0 and not host(codes)[[7, 95]].any()
 
 
+# K is a multiple of 64 (the entry point's rule) and of G.
+_RQ_SHAPES = [(G, K) for G in (16, 64, 256)
+              for K in (max(G, 64), 3 * max(G, 64), 2304, 10240, 10496, 16384, 20480, 20736, 32768)]
+
+
+@pytest.mark.parametrize("G,K", _RQ_SHAPES)
+def test_rotate_quant_every_launch_shape(G, K):
+    """K across every workgroup size and chunk width the launcher picks (8- and
+    16-column chunks; 128, 256 and 1024 threads; rows that fill every thread's
+    chunks and rows that do not), in both code layouts, against the oracle."""
+    x = workloads.activations(3, K, seed=K + G, outliers=max(1, K // 400), zero_rows=(1,))
+    xd = bf16_dev(x)
+    ref_codes, ref_scales = oracle.rotate_quant(x, G, 4)
+    codes, scales = ck.rotate_quant(xd, G, 4)
+    assert_codes_close(host(codes), ref_codes, min_equal=1.0 - max(1.0, 1e-4 * codes.numel()) / codes.numel())
+    assert np.all(np.abs(host(scales) - ref_scales) <= 2.0 ** -20 * ref_scales)
+    c4, s4 = ck.rotate_quant_packed4(xd, G)
+    lo = (host(c4) & 0x0F).astype(np.int16)
+    hi = (host(c4) >> 4).astype(np.int16)
+    unpacked = np.empty((3, K), dtype=np.int16)
+    unpacked[:, 0::2] = lo - 16 * (lo >= 8)
+    unpacked[:, 1::2] = hi - 16 * (hi >= 8)
+    assert np.array_equal(unpacked.astype(np.int8), host(codes))
+    assert np.array_equal(host(s4), host(scales))
+    c8, _ = ck.rotate_quant(xd, G, 8)
+    assert_codes_close(host(c8), oracle.rotate_quant(x, G, 8)[0],
+                       min_equal=1.0 - max(1.0, 1e-4 * c8.numel()) / c8.numel())
+
+
 def test_rotate_quant_strided_input_ignores_padding():
     M, K, ld = 9, 1024, 1152  # padding columns hold NaN
     x = workloads.activations(M, K, seed=5, outliers=10, ld=ld)
