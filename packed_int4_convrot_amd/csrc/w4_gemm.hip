@@ -48,6 +48,8 @@
 // weights ([M][K/2] bytes, two's complement nibbles in [-7, 7]), so the
 // activation stage, its DMA and its LDS reads are half as large, and both
 // operands are decoded to 16 * value: the accumulator carries a factor 256.
+#include <type_traits>
+
 #include "ck_device.h"
 #include "launch.h"
 
@@ -160,10 +162,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(packed + (int64_t)n0 * ldw), (short)0,
         (int)((int64_t)(min(N - n0, BN) - 1) * ldw + K / 2), 0x00020000);
-    auto issue_stage = [&](int st, int b) {
+    // Part p of NP equal parts of stage st's DMA into buffer b (NP = 1: all of it).
+    auto issue_part = [&](int st, int b, int p, auto np_c) {
+        constexpr int NP = decltype(np_c)::value;
         lds_u8 *sa = smem + b * STAGE;
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j) {
+        for (int jj = 0; jj < A_LD / NP; ++jj) {
+            const int j = p * (A_LD / NP) + jj;
             const int q = (wave * A_LD + j) * A_LANES + lane;
             if (A_LANES == kWave || lane < A_LANES) {
                 const int r = q / A_SLOTS;
@@ -174,7 +179,8 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
             }
         }
 #pragma unroll
-        for (int j = 0; j < B_LD; ++j) {
+        for (int jj = 0; jj < B_LD / NP; ++jj) {
+            const int j = p * (B_LD / NP) + jj;
             const int q = (wave * B_LD + j) * B_LANES + lane;
             if (B_LANES == kWave || lane < B_LANES) {
                 const int n = q / B_SLOTS;
@@ -185,6 +191,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
             }
         }
     };
+    auto issue_stage = [&](int st, int b) { issue_part(st, b, 0, std::integral_constant<int, 1>{}); };
+    // The DMA of a four-step stage (packed codes, per-channel and int32
+    // tiles) is issued in four parts, one per K step: a burst of LDS writes
+    // then no longer meets every wave's first fragment reads of the stage at
+    // once (about 1% faster at M = 8192).
+    constexpr bool SPLIT = KSUB == 4 && TRANS && A_LD % KSUB == 0 && B_LD % KSUB == 0;
+    constexpr int NPART = SPLIT ? KSUB : 1;
 
     // Fragments of one K step: weight row pieces and activation row pieces.
     struct Frag {
@@ -334,11 +347,15 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
             pair(3, b1, a1[3]);
         }
     };
-    // K step u (not a stage's last) of stage buffer b, with step u + 1 read ahead.
+    // K step u (not a stage's last) of stage buffer b, with step u + 1 read
+    // ahead and, where dma, part u + 1 of the DMA of stage dst into buffer b ^ 1.
     Frag fr[2];
     Head hd[2];
-    auto step = [&](int b, int u, int kt) {
+    auto step = [&](int b, int u, int kt, bool dma, int dst) {
         read_frag(fr[(u + 1) & 1], b, u + 1);
+        if constexpr (SPLIT)
+            if (dma)
+                issue_part(dst, b ^ 1, u + 1, std::integral_constant<int, NPART>{});
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ILV)
             compute_ilv(fr[u & 1], hd[u & 1], fr[(u + 1) & 1], hd[(u + 1) & 1]);
@@ -370,9 +387,12 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     int st = 0;
     for (; st + 1 < nstages; ++st) {
         const int b = st & 1;
+        // Stage st + 1 was issued whole before the loop (st = 0), else in
+        // parts: part 0 at the last barrier, the others here.
+        const bool dma = st >= 1;
 #pragma unroll
         for (int u = 0; u + 1 < KSUB; ++u)
-            step(b, u, st * KSUB + u);
+            step(b, u, st * KSUB + u, dma, st + 1);
         // Every read of this buffer has returned once each wave has waited
         // for its own, and the next stage has landed once each wave has
         // waited for its own DMA; the barrier extends both to the block, so
@@ -381,9 +401,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
         wait_lgkm0();
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        if (st + 2 < nstages)
-            issue_stage(st + 2, b);
         read_frag(fr[0], b ^ 1, 0);
+        if (st + 2 < nstages)
+            issue_part(st + 2, b, 0, std::integral_constant<int, NPART>{});
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ILV)
             compute_ilv(fr[(KSUB - 1) & 1], hd[(KSUB - 1) & 1], fr[0], hd[0]);
