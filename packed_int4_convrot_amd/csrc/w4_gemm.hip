@@ -22,8 +22,10 @@
 //   * one barrier per stage.  Fragment reads run one K step ahead of the
 //     MFMAs (two register sets), and the first step of the next stage is read
 //     right after that barrier, so LDS latency is never waited on between
-//     MFMAs; the DMA of stage t + 2 is issued at the same barrier into the
-//     buffer that stage t has just finished reading;
+//     MFMAs; the DMA of stage t + 2 goes into the buffer that stage t has
+//     just finished reading: all of it at that barrier, or for four-step
+//     stages a quarter there and a quarter after each of the next stage's
+//     first three K steps;
 //   * the per-channel and int32 tiles run each K step in a fixed order: the
 //     nibble decodes sit between the MFMA pairs, and the operands of the next
 //     step's first MFMAs are decoded under this step's last ones, so the
@@ -387,8 +389,9 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     int st = 0;
     for (; st + 1 < nstages; ++st) {
         const int b = st & 1;
-        // Stage st + 1 was issued whole before the loop (st = 0), else in
-        // parts: part 0 at the last barrier, the others here.
+        // Stage st + 1 was issued whole before the loop (st = 0); otherwise
+        // its first part (or all of it, without SPLIT) went out at the last
+        // barrier and the remaining parts go out here.
         const bool dma = st >= 1;
 #pragma unroll
         for (int u = 0; u + 1 < KSUB; ++u)
