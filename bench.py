@@ -156,12 +156,17 @@ PROFILE_WORKLOADS = {
     "rotate_quant_m8192_k10240_ld10752_g64": dict(
         kernel="rotate_quant_kernel", M=8192, K=10240, N=0, mops=None,
         alg_bytes=8192 * 10240 * 2 + 8192 * 10240 + 8192 * 4),
+    "awq_w4a16_gemv_m1_k3072_n18432": dict(
+        kernel="w4a16_gemv_kernel", M=1, K=3072, N=18432, mops=None,
+        alg_bytes=18432 * 3072 // 2 + 2 * 2 * 48 * 18432 + 3072 * 2 + 18432 * 2),
 }
 KERNEL_SOURCES = {
     "w4_gemm_kernel": ["packed_int4_convrot_amd/csrc/w4_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
     "awq_gemm_kernel": ["packed_int4_convrot_amd/csrc/awq_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
     "rotate_quant_kernel": ["packed_int4_convrot_amd/csrc/rotate_quant.hip",
                             "packed_int4_convrot_amd/csrc/ck_device.h"],
+    "w4a16_gemv_kernel": ["packed_int4_convrot_amd/csrc/w4a16_gemv.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
+                          "packed_int4_convrot_amd/csrc/ck_device.h"],
 }
 
 
@@ -196,6 +201,15 @@ def profile_workload(name, reps=5):
 
         def fn():
             ck.gemm_packed4(codes4, rs, packed, scl, False, out=out)
+    elif name.startswith("awq_w4a16_gemv"):
+        d = workloads.workload_inputs("awq_w4a16_gemv_m1_k3072_n18432")
+        xv = bf16(d["x"])
+        pk = torch.from_numpy(d["packed"]).to(dev)
+        s, z = bf16(d["scales"]), bf16(d["zeros"])
+        out = torch.empty((xv.shape[0], pk.shape[0]), dtype=torch.bfloat16, device=dev)
+
+        def fn():
+            ck.w4a16_gemv(xv, pk, s, z, out=out)
     elif name.startswith("awq"):
         d = workloads.workload_inputs("awq_w4a16_gemv_m1_k3072_n18432")
         rng = torch.Generator(device=dev).manual_seed(1)
