@@ -50,7 +50,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    # 2000 headline steps are about 13 ms: long enough that a stall of a few hundred
+    # microseconds in one replay (seen once, at 1.3 ms per timed region, while the
+    # next 20 replays agreed to 1%) moves the result by a few percent at most.
+    ap.add_argument("--steps", type=int, default=2000)
     # 30000 warm-up steps are about 0.2 s of the headline step: the clocks of a chip
     # coming out of idle keep rising for tens of milliseconds under load.
     ap.add_argument("--warmup", type=int, default=30000)
