@@ -653,6 +653,9 @@ def test_awq_gemm_large_tiles_sampled_rows(M, K, N):
     (65, 64, 16, 16),        # first tiled M, a single K step (stage tail of one step)
     (129, 320, 48, 64),      # five K steps: one full stage of four, then a partial one
     (300, 448, 32, 64),      # seven K steps
+    (257, 512, 32, 16),      # two full stages: the second stage's DMA is issued whole up front
+    (96, 768, 64, 64),       # three stages: the third is issued in parts during the second
+    (200, 1088, 48, 64),     # four full stages and a one-step tail
     (70, 32768, 32, 256),    # longest K
 ])
 def test_w4a4_packed_path_edge_shapes(M, K, N, G):
