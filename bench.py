@@ -369,7 +369,7 @@ def main():
     packs = [packed0] + [packed0.clone() for _ in range(args.copies - 1)]
     scls = [scales0] + [scales0.clone() for _ in range(args.copies - 1)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -628,7 +628,7 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
         packed = u8(inp["packed"])
         scl = bf16(inp["w_scales"])
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        work = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=dev)  # held by the caller
+        work = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)  # held by the caller
         # the linear's own two launches: packed rotate-quant, then the GEMM on packed codes
         codes4, rs = ck.rotate_quant_packed4(x, G)
         lin = _time(lambda i: ck.linear(x, G, 4, packed, scl, False, out=out, workspace=work), stream, 20)

@@ -44,13 +44,15 @@
  *    thread-local description.  Faults inside a kernel surface at the
  *    caller's next synchronisation.
  *  - M == 0 is a valid no-op.
- *  - Shape limits (CK_ERR_UNSUPPORTED otherwise): G in {16, 64, 256};
- *    bits in {8, 4}; K % 64 == 0 and 64 <= K <= 32768 (K % G != 0 is
- *    CK_ERR_INVALID_ARG: a row must split into whole groups);
- *    N % 16 == 0; weight-scale group Gw == 64 for per-group scales;
- *    M, N <= 2^22 (one launch's grid), and for shapes that run the tiled
- *    GEMM ceil(M / 128) * ceil(N / 256) < 2^23; row strides of codes and
- *    packed weights ldq, ldw <= 2^23 bytes.
+ *  - Shape rules.  CK_ERR_INVALID_ARG: K <= 0, K % 64 != 0 or K % G != 0
+ *    (a row must split into whole 64-column weight-scale groups and whole
+ *    rotation groups).  CK_ERR_UNSUPPORTED (valid, outside what this build
+ *    serves): G not in {16, 64, 256}; bits not in {8, 4}; K > 32768;
+ *    N % 16 != 0; weight-scale group Gw != 64 for per-group scales;
+ *    M or N >= 2^22 (one launch's grid); for shapes that run the tiled
+ *    GEMM ceil(M / 128) * ceil(N / 256) >= 2^23; row strides of codes and
+ *    packed weights ldq, ldw > 2^23 bytes.
+ *  - Every entry point returns a ck_status (CK_OK on success).
  *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
  *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
  *    ldw % 16 == 0; AWQ scales and zero points 16-byte aligned; outputs
@@ -82,7 +84,7 @@ typedef enum {
 typedef enum { CK_WS_PER_CHANNEL = 0, CK_WS_PER_GROUP = 1 } ck_wscale_kind;
 
 /* Static string for a status code. */
-const char *ck_status_str(int status);
+const char *ck_status_str(ck_status status);
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char *ck_last_error_msg(void);
@@ -104,7 +106,7 @@ const char *ck_version(void);
  *   row_scales fp32 [M]
  * codes/row_scales must not overlap x.
  */
-int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+ck_status ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                     int32_t bits, int8_t *codes, int64_t ldq, float *row_scales,
                     void *stream);
 
@@ -128,7 +130,7 @@ int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_
  * stay in registers) runs the weight-streaming kernel of ck_w4_gemv; every
  * other shape runs the tiled MFMA GEMM.
  */
-int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
+ck_status ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
                  int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                  int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                  uint16_t *out, int64_t ldo, void *stream);
@@ -140,7 +142,7 @@ int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int6
  * streams the packed weights once (VALU dot products for M <= 5, MFMA for
  * 6 <= M <= 8 when K fits its range).
  */
-int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
+ck_status ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M,
                int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                uint16_t *out, int64_t ldo, void *stream);
@@ -157,7 +159,7 @@ int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_
  * reused by every ck_w4a4_gemm_packed that shares the input (the activation
  * cache of [SD], for inputs of scale 1).
  */
-int ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+ck_status ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                             uint8_t *codes4, int64_t ldq, float *row_scales, void *stream);
 
 /*
@@ -169,15 +171,16 @@ int ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
  * Weights, scales, bias and out as in ck_w4_gemm_q; codes4 uint8 [M, ldq],
  * ldq >= K/2.  This is the matmul half of ck_w4a4_linear for M > 64.
  */
-int ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t M,
+ck_status ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t M,
                         int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                         int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                         uint16_t *out, int64_t ldo, void *stream);
 
 /* Bytes of workspace ck_w4a8_linear / ck_w4a4_linear need for M rows of K
- * columns: the int8 codes [M, K] plus the fp32 row scales, each 256-byte
- * aligned inside the workspace. */
-size_t ck_linear_workspace_bytes(int64_t M, int64_t K);
+ * columns and N outputs: the int8 codes [M, K] plus the fp32 row scales, each
+ * 256-byte aligned inside the workspace (no part depends on N, which is taken
+ * so that a later matmul needing per-output scratch keeps this signature). */
+size_t ck_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
  * ck_w4a8_linear  [SD] [RQ] [GEMV]
@@ -191,7 +194,7 @@ size_t ck_linear_workspace_bytes(int64_t M, int64_t K);
  *             bytes, 256-byte aligned; CK_ERR_WORKSPACE if smaller or NULL
  *             (with M > 0).  Its contents are scratch.
  */
-int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+ck_status ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                    int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                    float x_scale, uint16_t *out, int64_t ldo, void *ws, size_t ws_bytes,
@@ -205,7 +208,7 @@ int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
  * the low nibble), as ck_rotate_quant_packed4 writes them; the result is
  * the same as with one code per byte.
  */
-int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                    int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                    float x_scale, uint16_t *out, int64_t ldo, void *ws, size_t ws_bytes,
@@ -224,7 +227,7 @@ int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
  *   bias    bf16 [N] or NULL;  out bf16 [M, ldo]
  * The weight is never materialised; it is decoded in registers.
  */
-int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+ck_status ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   const uint8_t *packed, int64_t ldw, const uint16_t *scales,
                   const uint16_t *zeros, int32_t Gw, int64_t N, const uint16_t *bias,
                   uint16_t *out, int64_t ldo, void *stream);
@@ -243,7 +246,7 @@ int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  *   scales, zeros  bf16 [K/Gw, N], Gw = 64, 2-byte aligned
  *   bias    bf16 [N] or NULL;  out bf16 [M, ldo] (16-byte aligned rows)
  */
-int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+ck_status ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   const uint8_t *packed, int64_t ldw, const uint16_t *scales,
                   const uint16_t *zeros, int32_t Gw, int64_t N, const uint16_t *bias,
                   uint16_t *out, int64_t ldo, void *stream);
@@ -268,7 +271,7 @@ int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  *   scales  bf16 [N] (per channel) or [K/64, N] (per group)
  * G and K as in ck_rotate_quant; N <= 2^22.  Runs on `stream`.
  */
-int ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
+ck_status ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
                         int32_t scale_kind, uint8_t *packed, int64_t ldp, uint16_t *scales,
                         void *stream);
 
@@ -277,20 +280,25 @@ int ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in,
  * can be compared exactly with the oracle. */
 
 /* The rotation of ck_rotate_quant as held in registers, divided by sqrt(G)
- * (exact, sqrt(G) is a power of two): xr fp32 [M, ldr]. */
-int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+ * (exact, sqrt(G) is a power of two): xr fp32 [M, ldr].  It runs the kernel
+ * instantiation that ck_rotate_quant and ck_rotate_quant_packed4 run for the
+ * same K and G (16-column chunks from G = 64 on, 8-column chunks at G = 16).
+ * The weight producer (ck_quantize_weights) always uses 8-column chunks; those
+ * apply the same butterfly stages to the same operands in the same order, so
+ * the values are identical, which its bit-exact test checks. */
+ck_status ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                        float *xr, int64_t ldr, void *stream);
 
 /* The integer accumulators of ck_w4_gemm_q (kernel chosen by M exactly as
  * there): acc int32 [M, lda], acc[m,n] = sum_k codes[m,k] * (q[n,k] - 8). */
-int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,
+ck_status ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,
                      const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,
                      int64_t lda, void *stream);
 
 /* The integer accumulators of the tiled GEMM on packed W4A4 codes (codes4 as
  * written by ck_rotate_quant_packed4), for any M >= 1:
  * acc[m,n] = sum_k code[m,k] * (q[n,k] - 8), acc int32 [M, lda]. */
-int ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
+ck_status ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
                         const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc,
                         int64_t lda, void *stream);
 

@@ -55,7 +55,7 @@ def _load():
             "oracle_quantize": [p, i64, i64, i64, i32, p, i64, p],
             "oracle_unpack": [p, i64, i64, i64, p],
             "oracle_int_gemm": [p, i64, i64, i64, p, i64, i64, p],
-            "oracle_epilogue": [p, i64, i64, i64, p, p, i32, p, p],
+            "oracle_epilogue": [p, i64, i64, i64, p, p, i32, p, ctypes.c_double, p],
             "oracle_awq_gemv": [p, i64, i64, i64, p, i64, p, p, i64, i64, p, p],
             "oracle_quantize_weights": [p, i64, i64, i64, i32, p, i64, p],
             "oracle_awq_dequantize": [p, i64, i64, i64, p, p, i64, p],
@@ -163,8 +163,11 @@ def int_gemm(codes: np.ndarray, w: np.ndarray, group: int | None = None) -> np.n
     return acc[:, :, 0] if group is None else acc
 
 
-def epilogue(acc: np.ndarray, row_scales, w_scales, per_group: bool, bias=None) -> np.ndarray:
-    """fp64 [M, N] output from exact accumulators and the activation / weight scales."""
+def epilogue(acc: np.ndarray, row_scales, w_scales, per_group: bool, bias=None,
+             x_scale: float = 1.0) -> np.ndarray:
+    """fp64 [M, N] output from exact accumulators and the activation / weight scales;
+    x_scale > 0 is the input scale (the linear of x_scale * x: the row scale times
+    x_scale, the bias unscaled)."""
     acc = np.ascontiguousarray(acc, dtype=np.int64)
     M, N = acc.shape[:2]
     ng = acc.shape[2] if acc.ndim == 3 else 1
@@ -173,22 +176,24 @@ def epilogue(acc: np.ndarray, row_scales, w_scales, per_group: bool, bias=None) 
     b = None if bias is None else _u16(bias)
     out = np.empty((M, N), dtype=np.float64)
     _check(_load().oracle_epilogue(_ptr(acc), M, N, ng, _ptr(rs), _ptr(ws), 1 if per_group else 0,
-                                   _ptr(b), _ptr(out)), "epilogue")
+                                   _ptr(b), float(x_scale), _ptr(out)), "epilogue")
     return out
 
 
-def gemm_q(codes, row_scales, packed, w_scales, per_group: bool, Gw: int = 64, bias=None):
+def gemm_q(codes, row_scales, packed, w_scales, per_group: bool, Gw: int = 64, bias=None,
+           x_scale: float = 1.0):
     """fp64 linear output from given activation codes and scales (the matmul half)."""
     w = unpack(packed, codes.shape[1])
     acc = int_gemm(codes, w, Gw if per_group else None)
-    return epilogue(acc, row_scales, w_scales, per_group, bias)
+    return epilogue(acc, row_scales, w_scales, per_group, bias, x_scale)
 
 
 def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, Gw: int = 64, bias=None,
-           K: int | None = None):
-    """Whole ConvRot linear: returns (out fp64 [M,N], codes, row scales)."""
+           K: int | None = None, x_scale: float = 1.0):
+    """Whole ConvRot linear of x_scale * x: returns (out fp64 [M,N], codes, row scales).
+    The codes and row scales returned are those of x itself."""
     codes, scales = rotate_quant(x, G, bits, K)
-    return gemm_q(codes, scales, packed, w_scales, per_group, Gw, bias), codes, scales
+    return gemm_q(codes, scales, packed, w_scales, per_group, Gw, bias, x_scale), codes, scales
 
 
 def awq_gemv(x, packed, scales, zeros, Gw: int = 64, bias=None, K: int | None = None) -> np.ndarray:

@@ -33,6 +33,8 @@
  *  - Codes are symmetric: qmax = 127 (int8) or 7 (int4); scale = absmax/qmax;
  *    code = round-half-even(fp32(xr * fp32(qmax/absmax))), clamped to
  *    [-qmax, qmax].  An all-zero row gets codes 0 and scale 1.0.
+ *  - The input scale a of the packed matmul is the linear of a * x: the
+ *    codes of x with the row scale multiplied by a (see oracle_epilogue).
  */
 #include <math.h>
 #include <stdint.h>
@@ -257,17 +259,28 @@ int oracle_int_gemm(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,
 
 /*
  * Scale epilogue in fp64.
- *   per channel (kind 0, ng == 1): out = s_x[m] * s_w[n] * acc[m,n]
- *   per group   (kind 1):          out = s_x[m] * sum_g s_w[g,n] * acc_g[m,n]
+ *   per channel (kind 0, ng == 1): out = a * s_x[m] * s_w[n] * acc[m,n]
+ *   per group   (kind 1):          out = a * s_x[m] * sum_g s_w[g,n] * acc_g[m,n]
  * plus bias[n] when bias is not NULL.  w_scales is bf16: [N] for kind 0,
  * [ng, N] (N contiguous) for kind 1.  out is [M, N] fp64.
+ *
+ * a is the input scale of "feat: support packed INT4 convrot models"
+ * (summary: the packed matmul takes an optional bias and input scale; the
+ * review text on its ConvRot notes says inputs of other scales are scaled
+ * and quantised inside the matmul).  Reading: the result is the linear of
+ * a * x.  In exact arithmetic the rotation and the absmax are both linear in
+ * x, so a * x has the codes of x and the row scale a * s_x; the oracle
+ * therefore multiplies the row scale by a (in fp64) and leaves the bias
+ * unscaled.  a = 1 is the plain linear; a must be positive and finite.
  */
 int oracle_epilogue(const int64_t *acc, int64_t M, int64_t N, int64_t ng,
                     const float *row_scales, const uint16_t *w_scales,
-                    int32_t kind, const uint16_t *bias, double *out)
+                    int32_t kind, const uint16_t *bias, double x_scale,
+                    double *out)
 {
     if (!acc || !row_scales || !w_scales || !out || M < 0 || N < 0 ||
-        ng <= 0 || (kind != 0 && kind != 1) || (kind == 0 && ng != 1))
+        ng <= 0 || (kind != 0 && kind != 1) || (kind == 0 && ng != 1) ||
+        !(x_scale > 0.0) || !isfinite(x_scale))
         return BAD_ARG;
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
@@ -279,7 +292,7 @@ int oracle_epilogue(const int64_t *acc, int64_t M, int64_t N, int64_t ng,
                     t += bf16_value(w_scales[g * N + n]) *
                          (double)acc[(m * N + n) * ng + g];
             }
-            t *= (double)row_scales[m];
+            t *= (double)row_scales[m] * x_scale;
             if (bias)
                 t += bf16_value(bias[n]);
             out[m * N + n] = t;

@@ -36,7 +36,7 @@ SIGNATURES = {
                      ctypes.c_int),
     "ck_w4_gemv": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i32, _i64, _p, _p, _i64, _p],
                    ctypes.c_int),
-    "ck_linear_workspace_bytes": ([_i64, _i64], _sz),
+    "ck_linear_workspace_bytes": ([_i64, _i64, _i64], _sz),
     "ck_w4a8_linear": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p, _f32, _p,
                         _i64, _p, _sz, _p], ctypes.c_int),
     "ck_w4a4_linear": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p, _f32, _p,
@@ -106,20 +106,32 @@ def _stream(t):
 
 
 def _matrix(t, name, dtypes):
+    """A 2-D GPU tensor of one of `dtypes` whose rows are disjoint runs of unit-stride
+    elements (the layout the C ABI describes with one row stride)."""
     if not isinstance(t, torch.Tensor) or t.dim() != 2:
         raise ValueError("%s must be a 2-D tensor" % name)
     if t.dtype not in dtypes:
         raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
-    if not t.is_cuda:
-        raise ValueError("%s must be a GPU tensor" % name)
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("%s must have unit column stride" % name)
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        # expanded (stride 0) or overlapping rows: the C ABI would take them as
+        # disjoint rows of stride >= K and touch memory past the tensor's storage
+        raise ValueError("%s has row stride %d below its row length %d (expanded or overlapping rows)"
+                         % (name, t.stride(0), t.shape[1]))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
     return t
 
 
 def _ld(t):
-    """Row stride in elements (a single row may report any stride; use at least its length)."""
-    return max(t.stride(0), t.shape[1])
+    """Row stride in elements.  A single row may report any stride, so it counts as its
+    own length; for more rows _matrix has checked that the stride covers a row."""
+    if t.shape[0] <= 1:
+        return max(t.stride(0), t.shape[1])
+    if t.stride(0) < t.shape[1]:
+        raise ValueError("row stride %d below the row length %d" % (t.stride(0), t.shape[1]))
+    return t.stride(0)
 
 
 def _same_device(ref, *named):
@@ -156,8 +168,9 @@ def _weights(packed, w_scales, per_group, K):
     return N
 
 
-def workspace_bytes(M: int, K: int) -> int:
-    return int(lib.ck_linear_workspace_bytes(M, K))
+def workspace_bytes(M: int, K: int, N: int) -> int:
+    """Workspace bytes of the whole-linear entry points for M rows, K columns, N outputs."""
+    return int(lib.ck_linear_workspace_bytes(M, K, N))
 
 
 def rotate_quant(x, G: int, bits: int, codes=None, row_scales=None):
@@ -239,7 +252,7 @@ def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
         raise ValueError("bits must be 8 or 4")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    need = workspace_bytes(M, K)
+    need = workspace_bytes(M, K, N)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     if bias is not None:

@@ -62,9 +62,10 @@ constexpr int64_t kMaxK = 32768;
 // Row strides of codes and packed weights, in bytes: the tiled GEMM addresses
 // a block's 256 rows with 32-bit buffer offsets.
 constexpr int64_t kMaxLd = int64_t(1) << 23;
-// A launch covers at most 2^32 - 1 work-items per grid dimension; one
-// workgroup of up to 1024 threads per activation row bounds the rows to 2^22.
-constexpr int64_t kMaxRows = int64_t(1) << 22;
+// A launch covers at most 2^32 - 1 work-items per grid dimension.  Rotate-quant
+// and the weight producer launch one workgroup of up to 1024 threads per row,
+// so the rows stay below 2^22: (2^22 - 1) * 1024 = 2^32 - 1024 work-items.
+constexpr int64_t kMaxRows = (int64_t(1) << 22) - 1;
 // The tiled GEMM launches one 512-thread workgroup per 256 x 256 (or
 // 128 x 256) output tile.
 constexpr int64_t kMaxGemmTiles = (int64_t(1) << 32) / 512 - 1;
@@ -73,9 +74,11 @@ int check_k(const char *fn, int64_t K)
 {
     if (K <= 0)
         return fail(CK_ERR_INVALID_ARG, "%s: K must be positive (got %lld)", fn, (long long)K);
-    if (K % 64 != 0 || K > kMaxK)
-        return fail(CK_ERR_UNSUPPORTED, "%s: K must be a multiple of 64 and at most %lld (got %lld)",
-                    fn, (long long)kMaxK, (long long)K);
+    if (K % 64 != 0)
+        return fail(CK_ERR_INVALID_ARG, "%s: K must be a multiple of 64 (got %lld)", fn, (long long)K);
+    if (K > kMaxK)
+        return fail(CK_ERR_UNSUPPORTED, "%s: K must be at most %lld (got %lld)", fn, (long long)kMaxK,
+                    (long long)K);
     return CK_OK;
 }
 
@@ -193,6 +196,14 @@ int check_out(const char *fn, const void *out, int64_t N, int64_t ldo, size_t es
 constexpr size_t kWsAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Whole-linear workspace: the int8 codes [M, K], then the fp32 row scales.
+size_t workspace_bytes(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0)
+        return 0;
+    return round_up((size_t)(M * K), kWsAlign) + round_up((size_t)M * sizeof(float), kWsAlign);
+}
+
 // Dispatch of the integer matmul + epilogue by M.
 enum class GemmPath { kGemv, kSkinny, kTiled };
 
@@ -286,7 +297,7 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
     if (bias && !aligned(bias, 2))
         return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
     CK_TRY(check_out(fn, out, w.N, ldo, 2));
-    const size_t need = ck_linear_workspace_bytes(M, K);
+    const size_t need = workspace_bytes(M, K);
     if (!ws || ws_bytes < need)
         return fail(CK_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, ws_bytes,
                     ws ? "" : ", NULL");
@@ -328,9 +339,9 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char *ck_status_str(int status)
+const char *status_str_impl(int status)
 {
     switch (status) {
     case CK_OK: return "CK_OK";
@@ -342,18 +353,7 @@ const char *ck_status_str(int status)
     }
 }
 
-const char *ck_last_error_msg(void) { return g_last_error.c_str(); }
-
-const char *ck_version(void) { return "ck 0.1 gfx950"; }
-
-size_t ck_linear_workspace_bytes(int64_t M, int64_t K)
-{
-    if (M <= 0 || K <= 0)
-        return 0;
-    return round_up((size_t)(M * K), kWsAlign) + round_up((size_t)M * sizeof(float), kWsAlign);
-}
-
-int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, int32_t bits,
+int ck_rotate_quant_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, int32_t bits,
                     int8_t *codes, int64_t ldq, float *row_scales, void *stream)
 {
     const char *fn = "ck_rotate_quant";
@@ -377,7 +377,7 @@ int ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_
     return hip_status(e, fn);
 }
 
-int ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
+int ck_quantize_weights_impl(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
                         int32_t scale_kind, uint8_t *packed, int64_t ldp, uint16_t *scales, void *stream)
 {
     const char *fn = "ck_quantize_weights";
@@ -408,7 +408,7 @@ int ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in,
     return hip_status(e, fn);
 }
 
-int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, float *xr,
+int ck_test_rotate_f32_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, float *xr,
                        int64_t ldr, void *stream)
 {
     const char *fn = "ck_test_rotate_f32";
@@ -427,7 +427,7 @@ int ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int
     return hip_status(e, fn);
 }
 
-int ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+int ck_rotate_quant_packed4_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                                  uint8_t *codes4, int64_t ldq, float *row_scales, void *stream)
 {
     const char *fn = "ck_rotate_quant_packed4";
@@ -449,7 +449,7 @@ int ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
     return hip_status(e, fn);
 }
 
-int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,
+int ck_w4_gemm_q_impl(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,
                  const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
                  int32_t Gw, int64_t N, const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
 {
@@ -457,7 +457,7 @@ int ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int6
     return gemm_q_common("ck_w4_gemm_q", false, codes, ldq, row_scales, M, K, w, bias, out, ldo, stream);
 }
 
-int ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t M,
+int ck_w4a4_gemm_packed_impl(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t M,
                         int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                         int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
                         uint16_t *out, int64_t ldo, void *stream)
@@ -483,7 +483,7 @@ int ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_sca
     return run_gemm(fn, codes4, ldq, row_scales, M, K, w, bias, 1.0f, out, ldo, nullptr, 0, true, stream);
 }
 
-int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,
+int ck_w4_gemv_impl(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t K,
                const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
                int32_t Gw, int64_t N, const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
 {
@@ -491,7 +491,7 @@ int ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_
     return gemm_q_common("ck_w4_gemv", true, codes, ldq, row_scales, M, K, w, bias, out, ldo, stream);
 }
 
-int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+int ck_w4a8_linear_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
                    int32_t Gw, int64_t N, const uint16_t *bias, float x_scale, uint16_t *out,
                    int64_t ldo, void *ws, size_t ws_bytes, void *stream)
@@ -501,7 +501,7 @@ int ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
                          ws_bytes, stream);
 }
 
-int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+int ck_w4a4_linear_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
                    int32_t Gw, int64_t N, const uint16_t *bias, float x_scale, uint16_t *out,
                    int64_t ldo, void *ws, size_t ws_bytes, void *stream)
@@ -511,7 +511,7 @@ int ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t
                          ws_bytes, stream);
 }
 
-int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
+int ck_w4a16_gemv_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
                   int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int32_t Gw, int64_t N,
                   const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
 {
@@ -541,7 +541,7 @@ int ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const ui
     return hip_status(e, fn);
 }
 
-int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
+int ck_w4a16_gemm_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
                   int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int32_t Gw, int64_t N,
                   const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
 {
@@ -572,7 +572,7 @@ int ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const ui
     return hip_status(e, fn);
 }
 
-int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, const uint8_t *packed,
+int ck_test_gemm_i32_impl(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, const uint8_t *packed,
                      int64_t ldw, int64_t N, int32_t *acc, int64_t lda, void *stream)
 {
     const char *fn = "ck_test_gemm_i32";
@@ -590,7 +590,7 @@ int ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, con
     return run_gemm(fn, codes, ldq, nullptr, M, K, w, nullptr, 1.0f, nullptr, 0, acc, lda, false, stream);
 }
 
-int ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
+int ck_test_gemm_i32_a4_impl(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K,
                         const uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc, int64_t lda,
                         void *stream)
 {
@@ -607,6 +607,126 @@ int ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K
     if (overlap(ra, span(codes4, M, K / 2, ldq, 1)) || overlap(ra, span(packed, N, K / 2, ldw, 1)))
         return fail(CK_ERR_INVALID_ARG, "%s: acc overlaps an input", fn);
     return run_gemm(fn, codes4, ldq, nullptr, M, K, w, nullptr, 1.0f, nullptr, 0, acc, lda, true, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ck_status_str(ck_status status) { return status_str_impl(status); }
+
+const char *ck_last_error_msg(void) { return g_last_error.c_str(); }
+
+const char *ck_version(void) { return "ck 0.2 gfx950"; }
+
+size_t ck_linear_workspace_bytes(int64_t M, int64_t K, int64_t N)
+{
+    (void)N;  // the codes and row scales do not depend on N
+    return workspace_bytes(M, K);
+}
+
+ck_status ck_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, int32_t
+                          bits, int8_t *codes, int64_t ldq, float *row_scales, void *stream)
+{
+    return static_cast<ck_status>(ck_rotate_quant_impl(x, M, K, ldx, G, bits, codes, ldq,
+            row_scales, stream));
+}
+
+ck_status ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t ldw_in, int32_t G,
+                              int32_t scale_kind, uint8_t *packed, int64_t ldp, uint16_t *scales,
+                              void *stream)
+{
+    return static_cast<ck_status>(ck_quantize_weights_impl(w, N, K, ldw_in, G, scale_kind, packed,
+            ldp, scales, stream));
+}
+
+ck_status ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, float
+                             *xr, int64_t ldr, void *stream)
+{
+    return static_cast<ck_status>(ck_test_rotate_f32_impl(x, M, K, ldx, G, xr, ldr, stream));
+}
+
+ck_status ck_rotate_quant_packed4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                                  uint8_t *codes4, int64_t ldq, float *row_scales, void *stream)
+{
+    return static_cast<ck_status>(ck_rotate_quant_packed4_impl(x, M, K, ldx, G, codes4, ldq,
+            row_scales, stream));
+}
+
+ck_status ck_w4_gemm_q(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t
+                       K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t
+                       scale_kind, int32_t Gw, int64_t N, const uint16_t *bias, uint16_t *out,
+                       int64_t ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_w4_gemm_q_impl(codes, ldq, row_scales, M, K, packed, ldw,
+            w_scales, scale_kind, Gw, N, bias, out, ldo, stream));
+}
+
+ck_status ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *row_scales, int64_t
+                              M, int64_t K, const uint8_t *packed, int64_t ldw, const uint16_t
+                              *w_scales, int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t
+                              *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_w4a4_gemm_packed_impl(codes4, ldq, row_scales, M, K, packed,
+            ldw, w_scales, scale_kind, Gw, N, bias, out, ldo, stream));
+}
+
+ck_status ck_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int64_t M, int64_t
+                     K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t
+                     scale_kind, int32_t Gw, int64_t N, const uint16_t *bias, uint16_t *out, int64_t
+                     ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_w4_gemv_impl(codes, ldq, row_scales, M, K, packed, ldw,
+            w_scales, scale_kind, Gw, N, bias, out, ldo, stream));
+}
+
+ck_status ck_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, const
+                         uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
+                         int32_t Gw, int64_t N, const uint16_t *bias, float x_scale, uint16_t *out,
+                         int64_t ldo, void *ws, size_t ws_bytes, void *stream)
+{
+    return static_cast<ck_status>(ck_w4a8_linear_impl(x, M, K, ldx, G, packed, ldw, w_scales,
+            scale_kind, Gw, N, bias, x_scale, out, ldo, ws, ws_bytes, stream));
+}
+
+ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, const
+                         uint8_t *packed, int64_t ldw, const uint16_t *w_scales, int32_t scale_kind,
+                         int32_t Gw, int64_t N, const uint16_t *bias, float x_scale, uint16_t *out,
+                         int64_t ldo, void *ws, size_t ws_bytes, void *stream)
+{
+    return static_cast<ck_status>(ck_w4a4_linear_impl(x, M, K, ldx, G, packed, ldw, w_scales,
+            scale_kind, Gw, N, bias, x_scale, out, ldo, ws, ws_bytes, stream));
+}
+
+ck_status ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
+                        int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int32_t Gw,
+                        int64_t N, const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_w4a16_gemv_impl(x, M, K, ldx, packed, ldw, scales, zeros, Gw,
+            N, bias, out, ldo, stream));
+}
+
+ck_status ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
+                        int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int32_t Gw,
+                        int64_t N, const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_w4a16_gemm_impl(x, M, K, ldx, packed, ldw, scales, zeros, Gw,
+            N, bias, out, ldo, stream));
+}
+
+ck_status ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K, const uint8_t
+                           *packed, int64_t ldw, int64_t N, int32_t *acc, int64_t lda, void *stream)
+{
+    return static_cast<ck_status>(ck_test_gemm_i32_impl(codes, ldq, M, K, packed, ldw, N, acc, lda,
+            stream));
+}
+
+ck_status ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int64_t K, const
+                              uint8_t *packed, int64_t ldw, int64_t N, int32_t *acc, int64_t lda,
+                              void *stream)
+{
+    return static_cast<ck_status>(ck_test_gemm_i32_a4_impl(codes4, ldq, M, K, packed, ldw, N, acc,
+            lda, stream));
 }
 
 }  // extern "C"

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 {
     constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
     static_assert(G == 16 || G == 64 || G == 256, "G");
-    static_assert(CW == 8 || (CW == 16 && (MODE == kCodes8 || MODE == kPacked4)), "chunk width");
+    static_assert(CW == 8 || (CW == 16 && (MODE == kCodes8 || MODE == kPacked4 || MODE == kF32)),
+                  "chunk width");
     __shared__ float wmax[BLOCK / kWave];
 
     const int64_t m = blockIdx.x;
@@ -244,11 +245,11 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
         for (int i = 0; i < CPT; ++i) {
             const int c = t + i * BLOCK;
             if (FULL || c < nchunk) {
-                float4 *o = reinterpret_cast<float4 *>(orow + 8 * c);
-                o[0] = make_float4(v[i][0] * kInvSqrtG, v[i][1] * kInvSqrtG, v[i][2] * kInvSqrtG,
-                                   v[i][3] * kInvSqrtG);
-                o[1] = make_float4(v[i][4] * kInvSqrtG, v[i][5] * kInvSqrtG, v[i][6] * kInvSqrtG,
-                                   v[i][7] * kInvSqrtG);
+                float4 *o = reinterpret_cast<float4 *>(orow + CW * c);
+#pragma unroll
+                for (int q = 0; q < CW / 4; ++q)
+                    o[q] = make_float4(v[i][4 * q] * kInvSqrtG, v[i][4 * q + 1] * kInvSqrtG,
+                                       v[i][4 * q + 2] * kInvSqrtG, v[i][4 * q + 3] * kInvSqrtG);
             }
         }
     } else {
@@ -339,9 +340,10 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
                      uint16_t *wsc = nullptr, int64_t ldsc = 0)
 {
     const dim3 grid((unsigned)M);
-    if constexpr ((MODE == kCodes8 || MODE == kPacked4) && G >= 64) {
+    if constexpr ((MODE == kCodes8 || MODE == kPacked4 || MODE == kF32) && G >= 64) {
         // Activation codes from G = 64 on: 16-column chunks (K is a multiple
-        // of G).  Up to 10240 columns 128 threads of up to 5 chunks, then 256,
+        // of G).  The fp32 test output takes the same instantiation, so the
+        // rotation it exposes is the one the activation codes are made from.  Up to 10240 columns 128 threads of up to 5 chunks, then 256,
         // then 1024 threads of up to 2.  The in-register distance-8 stage and
         // the longer rows per thread take 1-2 VALU instructions per element
         // off (13.3 instead of 15.3 at G = 256, K = 10240), which is what

@@ -44,10 +44,10 @@ def test_status_strings_and_version():
 
 
 def test_workspace_bytes():
-    assert lib.ck_linear_workspace_bytes(0, 3840) == 0
-    ws = lib.ck_linear_workspace_bytes(32, 3840)
+    assert lib.ck_linear_workspace_bytes(0, 3840, 3840) == 0
+    ws = lib.ck_linear_workspace_bytes(32, 3840, 3840)
     assert ws >= 32 * 3840 + 32 * 4 and ws % 256 == 0
-    assert lib.ck_linear_workspace_bytes(8192, 10240) == 8192 * 10240 + 32768
+    assert lib.ck_linear_workspace_bytes(8192, 10240, 3840) == 8192 * 10240 + 32768
 
 
 def rq(x=P, M=4, K=256, ldx=256, G=64, bits=8, codes=P2, ldq=256, rs=P3):
@@ -59,7 +59,7 @@ def rq(x=P, M=4, K=256, ldx=256, G=64, bits=8, codes=P2, ldq=256, rs=P3):
     (dict(G=128), ck.CK_ERR_UNSUPPORTED),
     (dict(bits=6), ck.CK_ERR_UNSUPPORTED),
     (dict(K=0), ck.CK_ERR_INVALID_ARG),
-    (dict(K=96, ldx=96, ldq=96), ck.CK_ERR_UNSUPPORTED),         # K % 64
+    (dict(K=96, ldx=96, ldq=96), ck.CK_ERR_INVALID_ARG),         # K % 64
     (dict(K=320, ldx=320, ldq=320, G=256), ck.CK_ERR_INVALID_ARG),  # K % G
     (dict(K=65536, ldx=65536, ldq=65536), ck.CK_ERR_UNSUPPORTED),
     (dict(M=-1), ck.CK_ERR_INVALID_ARG),
@@ -110,9 +110,13 @@ def test_gemm_q_rejects(kw, status):
 def test_launch_size_limits():
     # rows beyond one launch's grid, and a tiled GEMM whose tile grid would overflow
     assert rq(M=(1 << 22) + 1) == ck.CK_ERR_UNSUPPORTED
-    assert gq(M=(1 << 22), N=(1 << 22), ldo=(1 << 22)) == ck.CK_ERR_UNSUPPORTED
+    # 2^22 rows of 1024-thread workgroups (K above 16384) would be 2^32 work-items,
+    # one more than a grid dimension holds
+    assert rq(M=(1 << 22), K=16448, ldx=16448, ldq=16448) == ck.CK_ERR_UNSUPPORTED
+    assert lib.ck_quantize_weights(P, 1 << 22, 16448, 16448, 64, 0, P2, 8224, P3, None) == ck.CK_ERR_UNSUPPORTED
+    assert gq(M=(1 << 22) - 1, N=(1 << 22) - 16, ldo=(1 << 22) - 16) == ck.CK_ERR_UNSUPPORTED
     assert b"too large" in lib.ck_last_error_msg()
-    assert gq(N=(1 << 22) + 16) == ck.CK_ERR_UNSUPPORTED
+    assert gq(N=(1 << 22)) == ck.CK_ERR_UNSUPPORTED
     # row strides beyond 32-bit buffer offsets of a 256-row tile
     assert gq(ldq=(1 << 23) + 16) == ck.CK_ERR_UNSUPPORTED
     assert gq(ldw=(1 << 23) + 16) == ck.CK_ERR_UNSUPPORTED
@@ -229,6 +233,30 @@ def test_error_message_is_thread_local():
     t.join()
     assert msgs == [b""]
     assert b"G must be" in lib.ck_last_error_msg()
+
+
+def test_binding_rejects_expanded_and_overlapping_rows():
+    """Tensors whose rows overlap (an expanded row, a too-small row stride) are rejected
+    by the binding before any call: the C ABI describes a matrix by one row stride and
+    would read or write past the tensor's storage."""
+    import torch
+    M, K = 4, 256
+    expanded = torch.zeros((1, K), dtype=torch.bfloat16).expand(M, K)
+    assert expanded.stride(0) == 0
+    with pytest.raises(ValueError, match="row stride"):
+        ck.rotate_quant(expanded, 64, 8)
+    overlapping = torch.zeros(M * K, dtype=torch.bfloat16).as_strided((M, K), (K // 2, 1))
+    packed = torch.zeros((16, K // 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="row stride"):
+        ck.linear(overlapping, 64, 8, packed, torch.zeros(16, dtype=torch.bfloat16), False)
+    out = torch.zeros((1, 16), dtype=torch.bfloat16).expand(M, 16)
+    with pytest.raises(ValueError, match="row stride"):
+        ck._out(out, "out", torch.bfloat16, M, 16)
+    with pytest.raises(ValueError, match="row stride"):
+        ck._ld(expanded)
+    # a single row may report any stride; dense and padded rows keep theirs
+    assert ck._ld(torch.zeros((1, K)).as_strided((1, K), (0, 1))) == K
+    assert ck._ld(torch.zeros((M, K + 64))[:, :K]) == K + 64
 
 
 def test_binding_requires_gpu_tensors():

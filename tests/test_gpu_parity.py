@@ -95,6 +95,25 @@ def test_rotate_quant_every_launch_shape(G, K):
                        min_equal=1.0 - max(1.0, 1e-4 * c8.numel()) / c8.numel())
 
 
+def test_rotate_quant_small_arrays_pooled_rate():
+    """The >= 99.99% code-agreement bar is a rate.  An array of n < 10^4 codes cannot
+    show it (one flip is already 1/n > 10^-4), so the per-array checks above allow one
+    flip there; this test holds the rate itself on the pooled codes of all those
+    small arrays (every launch shape, both code widths, each G)."""
+    equal = total = 0
+    for G, K in _RQ_SHAPES:
+        x = workloads.activations(3, K, seed=K + G, outliers=max(1, K // 400), zero_rows=(1,))
+        xd = bf16_dev(x)
+        for bits in (4, 8):
+            d = np.abs(host(ck.rotate_quant(xd, G, bits)[0]).astype(np.int32)
+                       - oracle.rotate_quant(x, G, bits)[0].astype(np.int32))
+            assert d.max() <= 1
+            equal += int((d == 0).sum())
+            total += d.size
+    assert total > 10 ** 5
+    assert equal >= 0.9999 * total, "pooled agreement %.6f" % (equal / total)
+
+
 def test_rotate_quant_strided_input_ignores_padding():
     M, K, ld = 9, 1024, 1152  # padding columns hold NaN
     x = workloads.activations(M, K, seed=5, outliers=10, ld=ld)
@@ -359,7 +378,7 @@ def test_graph_replay_matches_eager(M):
     K, N = 1024, 272
     inp = workloads.linear_inputs(M, K, N, seed=M, outliers=5, scale="group", with_bias=True)
     xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
-    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
+    ws = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=DEV)
     eager = ck.linear(xd, 64, 8, wd, sd, True, bias=bd)
     out = torch.zeros_like(eager)
     s = torch.cuda.Stream()
@@ -407,7 +426,7 @@ def test_graph_replay_packed_w4a4_and_awq_gemm():
     M, K, N = 300, 1024, 272
     inp = workloads.linear_inputs(M, K, N, seed=8, outliers=5, scale="channel", with_bias=True)
     xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
-    ws = torch.empty((ck.workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
+    ws = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=DEV)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     _graph_replays_equal_eager(lambda: ck.linear(xd, 256, 4, wd, sd, False, bias=bd, out=out, workspace=ws),
                                out)
@@ -435,6 +454,27 @@ def test_linear_x_scale_power_of_two_is_exact():
     a = host(ck.linear(xd, 64, 8, wd, sd, False))
     b = host(ck.linear(xd, 64, 8, wd, sd, False, x_scale=4.0))
     assert np.array_equal(b, 4.0 * a)
+
+
+@pytest.mark.parametrize("alpha", [0.3, 3.0, 4.0])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M", [1, 4, 20, 300])
+def test_linear_x_scale_matches_oracle(M, bits, alpha):
+    """Input scale against the oracle's reading (the linear of alpha * x: codes of x,
+    row scale times alpha, bias unscaled), on every kernel path: the fused decode
+    launch, the VALU GEMV, the few-row MFMA kernel and the tiled GEMM."""
+    K, N = 1536, 272
+    for per_group in (True, False):
+        inp = workloads.linear_inputs(M, K, N, seed=M + bits, outliers=15, scale="group" if per_group else "channel",
+                                      with_bias=True)
+        xd = bf16_dev(inp["x"])
+        out = host(ck.linear(xd, 64, bits, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), per_group,
+                             bias=bf16_dev(inp["bias"]), x_scale=alpha))
+        codes, scales = ck.rotate_quant(xd, 64, bits)
+        a32 = float(np.float32(alpha))   # the C ABI takes the scale as fp32
+        ref = oracle.gemm_q(host(codes), host(scales), inp["packed"], inp["w_scales"], per_group,
+                            bias=inp["bias"], x_scale=a32)
+        assert_output_close(out, ref)
 
 
 def test_linear_int8_weight_tensor_and_strided_weights():

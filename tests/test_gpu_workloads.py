@@ -58,19 +58,29 @@ def test_w4a8_decode_gemv_k3840_n10240(M):
     _linear_case("w4a8_decode_gemv_k3840_n10240_g64", M=M, full=True)
 
 
-def test_w4a4_linear_m8192_k3840_n3840_g64_sampled():
-    inp, codes, rows = _linear_case("w4a4_linear_m8192_k3840_n3840_g64")
-    acc = host(ck.accumulators_i32(codes, u8_dev(inp["packed"])))
+def _accumulators_both_layouts(name, inp, codes, rows):
+    """int32 accumulators of the tiled GEMM on byte codes and on the packed codes that
+    ck_w4a4_linear actually multiplies at this size, exact on the sampled rows."""
+    w = workloads.WORKLOADS[name]
     ref = oracle.int_gemm(host(codes)[rows], oracle.unpack(inp["packed"]))
+    acc = host(ck.accumulators_i32(codes, u8_dev(inp["packed"])))
     assert np.array_equal(acc[rows].astype(np.int64), ref)
+    codes4, _ = ck.rotate_quant_packed4(bf16_dev(inp["x"]), w["G"])
+    acc4 = host(ck.accumulators_i32_a4(codes4, w["K"], u8_dev(inp["packed"])))
+    assert np.array_equal(acc4[rows].astype(np.int64), ref)
+
+
+def test_w4a4_linear_m8192_k3840_n3840_g64_sampled():
+    name = "w4a4_linear_m8192_k3840_n3840_g64"
+    inp, codes, rows = _linear_case(name)
+    _accumulators_both_layouts(name, inp, codes, rows)
 
 
 def test_w4a4_linear_m8192_k10240_n3840_g256_sampled():
-    inp, codes, rows = _linear_case("w4a4_linear_m8192_k10240_n3840_g256")
-    assert set(workloads.WORKLOADS["w4a4_linear_m8192_k10240_n3840_g256"]["zero_rows"]) <= set(rows.tolist())
-    acc = host(ck.accumulators_i32(codes, u8_dev(inp["packed"])))
-    ref = oracle.int_gemm(host(codes)[rows], oracle.unpack(inp["packed"]))
-    assert np.array_equal(acc[rows].astype(np.int64), ref)
+    name = "w4a4_linear_m8192_k10240_n3840_g256"
+    inp, codes, rows = _linear_case(name)
+    assert set(workloads.WORKLOADS[name]["zero_rows"]) <= set(rows.tolist())
+    _accumulators_both_layouts(name, inp, codes, rows)
 
 
 @pytest.mark.parametrize("G", [16, 64, 256])

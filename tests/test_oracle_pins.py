@@ -261,6 +261,72 @@ def test_epilogue_equals_dequantised_fp64_matmul(per_group):
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_x_scale_golden():
+    """Input scale (hand-worked, tests/golden/x_scale.json): the row scale is multiplied
+    by x_scale and the bias is added unscaled."""
+    g = _golden("x_scale.json")
+    x = np.zeros((1, g["K"]))
+    x[0, g["x_nonzero"]["index"]] = g["x_nonzero"]["value"]
+    x = _bf16(x)
+    packed = np.array([[b] * (g["K"] // 2) for b in g["packed_row_bytes"]], dtype=np.uint8)
+    sx_exact = sum(2.0 ** e for e in g["sx_f32_terms_pow2"])
+    ws, bias = _bf16(g["w_scales"]), _bf16(g["bias"])
+    for case in g["cases"]:
+        out, codes, sx = oracle.linear(x, g["G"], g["bits"], packed, ws, False, bias=bias,
+                                       x_scale=case["x_scale"])
+        assert (codes == 127).all() and float(sx[0]) == sx_exact
+        assert oracle.int_gemm(codes, oracle.unpack(packed))[0].tolist() == g["acc"]
+        if "out" in case:
+            np.testing.assert_allclose(out[0], case["out"], rtol=1e-15)
+        else:
+            assert out[0].tolist() == [4 * sx_exact * 4064 + 1, -4 * sx_exact * 1016 - 2]
+
+
+@pytest.mark.parametrize("alpha", [0.25, 4.0, 64.0])
+def test_x_scale_power_of_two_equals_linear_of_scaled_input(alpha):
+    """For a power-of-two input scale, alpha * x is exact in bf16 and the linear of it
+    (computed from that input, scale 1) is bit-identical to the linear of x at scale alpha."""
+    M, K, N = 5, 512, 24
+    for per_group in (False, True):
+        inp = workloads.linear_inputs(M, K, N, seed=11, outliers=3, scale="group" if per_group else "channel",
+                                      zero_rows=(2,), with_bias=True)
+        scaled = _bf16(_f32(inp["x"]).astype(np.float64) * alpha)
+        assert np.array_equal(_f32(scaled), _f32(inp["x"]) * np.float32(alpha))
+        for bits in (8, 4):
+            a = oracle.linear(inp["x"], 64, bits, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"],
+                              x_scale=alpha)
+            b = oracle.linear(scaled, 64, bits, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
+            assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
+
+
+@pytest.mark.parametrize("alpha", [0.3, 3.0, 1.7e-3])
+def test_x_scale_equals_dequantised_product_of_scaled_activations(alpha):
+    """Any positive scale: the output equals (alpha * s_x * codes) . (s_w * w)^T + bias by
+    a dequantise-then-matmul route in numpy, and approximates (alpha * x) . W^T."""
+    M, K, N = 7, 256, 10
+    inp = workloads.linear_inputs(M, K, N, seed=5, outliers=2, scale="group", with_bias=True)
+    out, codes, sx = oracle.linear(inp["x"], 64, 8, inp["packed"], inp["w_scales"], True, bias=inp["bias"],
+                                   x_scale=alpha)
+    w = oracle.unpack(inp["packed"]).astype(np.float64) * np.repeat(_f32(inp["w_scales"]).T, 64, axis=1)
+    a_deq = alpha * codes.astype(np.float64) * sx.astype(np.float64)[:, None]
+    np.testing.assert_allclose(out, a_deq @ w.T + _f32(inp["bias"]).astype(np.float64), rtol=1e-12, atol=1e-12)
+    # against the unquantised linear of the scaled input (rotation undone on the
+    # dequantised activations): the error is the activation quantisation error, scaled by alpha
+    H = scipy.linalg.hadamard(64) / 8.0
+    x_rot = _f32(inp["x"]).astype(np.float64).reshape(M, K // 64, 64) @ H
+    exact = alpha * x_rot.reshape(M, K) @ w.T + _f32(inp["bias"]).astype(np.float64)
+    bound = alpha * (sx.astype(np.float64)[:, None] / 2 * (1 + 2.0 ** -20)) @ np.abs(w).sum(1)[None, :]
+    bound += alpha * 2.0 ** -24 * np.abs(x_rot.reshape(M, K)) @ np.abs(w).T   # fp32 rounding of the rotation
+    assert (np.abs(out - exact) <= bound + 1e-12).all()
+
+
+def test_x_scale_rejects_non_positive():
+    inp = workloads.linear_inputs(1, 64, 2, seed=1, outliers=0, scale="channel")
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            oracle.linear(inp["x"], 64, 8, inp["packed"], inp["w_scales"], False, x_scale=bad)
+
+
 def test_linear_zero_rows_give_bias_only():
     inp = workloads.linear_inputs(4, 128, 16, seed=1, outliers=0, scale="group", zero_rows=(2,),
                                   with_bias=True)
