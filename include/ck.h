@@ -215,6 +215,34 @@ ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, i
                    void *stream);
 
 /*
+ * ck_w4a4_linear_noalloc
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ck_w4a4_linear
+ * with the codes and row scales held in a scratch array owned by the library
+ * instead of a caller workspace.  Same arguments minus ws / ws_bytes, same
+ * kernels, same results bit for bit.
+ *   - The scratch is a static device array of 64 MiB (67108864 bytes), one
+ *     copy on each GPU that loads the library, kept until the process ends.
+ *     A call needing more returns CK_ERR_UNSUPPORTED before anything is
+ *     enqueued: M * K / 2 bytes of packed codes (tiled path, M > 64) or M * K
+ *     bytes (fewer rows), each rounded up to 256, plus 4 * M bytes of row
+ *     scales rounded up to 256; M = 1 uses no scratch.  For example M = 8192
+ *     rows fit up to K = 16384.
+ *   - The call allocates nothing (no hipMalloc, no allocating library call).
+ *     Its scratch address on a device is looked up (hipGetSymbolAddress) on the
+ *     first call made with that device current; `stream` must belong to the
+ *     current device (CK_ERR_HIP otherwise).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents; each call writes all it reads.  Calls that can overlap
+ *     on one GPU (different streams, or threads without ordering) race on the
+ *     scratch: order them on one stream.
+ */
+ck_status ck_w4a4_linear_noalloc(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                                 const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                                 int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                                 float x_scale, uint16_t *out, int64_t ldo, void *stream);
+
+/*
  * ck_w4a16_gemv  [AWQ]
  * AWQ W4A16 product with fp activations (no activation quantisation):
  *   W[n,k]   = (q[n,k] - 8) * scales[k/Gw, n] + zeros[k/Gw, n]

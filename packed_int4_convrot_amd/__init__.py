@@ -41,6 +41,8 @@ SIGNATURES = {
                         _i64, _p, _sz, _p], ctypes.c_int),
     "ck_w4a4_linear": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p, _f32, _p,
                         _i64, _p, _sz, _p], ctypes.c_int),
+    "ck_w4a4_linear_noalloc": ([_p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p, _f32, _p,
+                                _i64, _p], ctypes.c_int),
     "ck_w4a16_gemv": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _i64, _p, _p, _i64, _p],
                       ctypes.c_int),
     "ck_w4a16_gemm": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _i64, _p, _p, _i64, _p],
@@ -267,6 +269,28 @@ def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
               CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N, _ptr(bias), x_scale,
               _ptr(out), _ld(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
               _stream(x)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's static scratch per GPU (include/ck.h)
+
+
+def w4a4_linear_noalloc(x, G: int, packed, w_scales, per_group: bool, bias=None,
+                        x_scale: float = 1.0, out=None):
+    """ck_w4a4_linear without a workspace: the codes live in the library's static
+    scratch (one per GPU, shared by every call on it; calls must not overlap)."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    N = _weights(packed, w_scales, per_group, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    _out(out, "out", torch.bfloat16, M, N)
+    _same_device(x, ("packed", packed), ("w_scales", w_scales), ("bias", bias), ("out", out))
+    _check(lib.ck_w4a4_linear_noalloc(_ptr(x), M, K, _ld(x), G, _ptr(packed), _ld(packed), _ptr(w_scales),
+                                      CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N, _ptr(bias),
+                                      x_scale, _ptr(out), _ld(out), _stream(x)))
     return out
 
 

@@ -281,9 +281,36 @@ int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, c
     return run_gemm(fn, codes, ldq, rs, M, K, w, bias, 1.0f, out, ldo, nullptr, 0, false, stream);
 }
 
+// How the whole linear runs for M rows: one fused launch (decode), or rotate-quant
+// into scratch followed by the matmul kernel that pick_path() chooses.  W4A4
+// codes bound for the tiled GEMM are stored two per byte, which halves the
+// codes traffic on both sides of the scratch.
+struct LinearPlan {
+    bool fused;
+    GemmPath path;
+    bool a4;
+    int64_t ldq;          // bytes per row of codes in the scratch
+    size_t scales_off;    // offset of the fp32 row scales
+    size_t used;          // scratch bytes the plan touches (0 when fused)
+};
+
+LinearPlan plan_linear(int bits, int64_t M, int64_t K)
+{
+    LinearPlan p{};
+    p.fused = ck::w4_gemv_fused_supports(M, K);
+    p.path = pick_path(M, K);
+    p.a4 = !p.fused && bits == 4 && p.path == GemmPath::kTiled;
+    p.ldq = p.a4 ? K / 2 : K;
+    p.scales_off = round_up((size_t)(M * p.ldq), kWsAlign);
+    p.used = p.fused ? 0 : p.scales_off + round_up((size_t)M * sizeof(float), kWsAlign);
+    return p;
+}
+
+// library_scratch: the scratch is the library's static device array
+// (ck_w4a4_linear_noalloc) instead of the caller's workspace ws.
 int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   int32_t G, const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out,
-                  int64_t ldo, void *ws, size_t ws_bytes, void *stream)
+                  int64_t ldo, void *ws, size_t ws_bytes, void *stream, bool library_scratch = false)
 {
     CK_TRY(check_m(fn, M));
     CK_TRY(check_k(fn, K));
@@ -297,44 +324,57 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
     if (bias && !aligned(bias, 2))
         return fail(CK_ERR_INVALID_ARG, "%s: bias must be 2-byte aligned", fn);
     CK_TRY(check_out(fn, out, w.N, ldo, 2));
-    const size_t need = workspace_bytes(M, K);
-    if (!ws || ws_bytes < need)
-        return fail(CK_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, ws_bytes,
-                    ws ? "" : ", NULL");
-    if (!aligned(ws, kWsAlign))
-        return fail(CK_ERR_WORKSPACE, "%s: workspace must be %zu-byte aligned", fn, kWsAlign);
     const Range ro = span(out, M, w.N, ldo, 2);
-    const Range rw = span(ws, 1, (int64_t)need, (int64_t)need, 1);
     const Range rx = span(x, M, K, ldx, 2);
     if (overlap(ro, rx) || overlap(ro, span(w.packed, w.N, K / 2, w.ldw, 1)) ||
-        overlap(ro, scales_span(w, K)) || overlap(ro, span(bias, 1, w.N, w.N, 2)) || overlap(ro, rw))
-        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input or the workspace", fn);
-    if (overlap(rw, rx) || overlap(rw, span(w.packed, w.N, K / 2, w.ldw, 1)) ||
-        overlap(rw, scales_span(w, K)) || overlap(rw, span(bias, 1, w.N, w.N, 2)))
-        return fail(CK_ERR_WORKSPACE, "%s: workspace overlaps an input", fn);
+        overlap(ro, scales_span(w, K)) || overlap(ro, span(bias, 1, w.N, w.N, 2)))
+        return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    const LinearPlan plan = plan_linear(bits, M, K);
+    if (!plan.fused && plan.path == GemmPath::kTiled)
+        CK_TRY(check_tiles(fn, M, w.N));
+    if (library_scratch) {
+        if (plan.used > ck::static_scratch_bytes())
+            return fail(CK_ERR_UNSUPPORTED, "%s: M = %lld, K = %lld needs %zu bytes of scratch; the "
+                        "library's static scratch holds %zu", fn, (long long)M, (long long)K, plan.used,
+                        ck::static_scratch_bytes());
+        ws = nullptr;
+        if (plan.used > 0) {
+            const int e = ck::static_scratch(stream, &ws);
+            if (e != 0)
+                return fail(CK_ERR_HIP, "%s: static scratch unavailable on this device or stream "
+                            "(hipError_t %d)", fn, e);
+        }
+    } else {
+        // The size asked of the caller does not depend on the path taken.
+        const size_t need = workspace_bytes(M, K);
+        if (!ws || ws_bytes < need)
+            return fail(CK_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, ws_bytes,
+                        ws ? "" : ", NULL");
+        if (!aligned(ws, kWsAlign))
+            return fail(CK_ERR_WORKSPACE, "%s: workspace must be %zu-byte aligned", fn, kWsAlign);
+        const Range rw = span(ws, 1, (int64_t)need, (int64_t)need, 1);
+        if (overlap(ro, rw))
+            return fail(CK_ERR_INVALID_ARG, "%s: output overlaps the workspace", fn);
+        if (overlap(rw, rx) || overlap(rw, span(w.packed, w.N, K / 2, w.ldw, 1)) ||
+            overlap(rw, scales_span(w, K)) || overlap(rw, span(bias, 1, w.N, w.N, 2)))
+            return fail(CK_ERR_WORKSPACE, "%s: workspace overlaps an input", fn);
+    }
 
     const int qmax = bits == 8 ? 127 : 7;
-    if (ck::w4_gemv_fused_supports(M, K)) {
+    if (plan.fused) {
         // Decode shapes: one launch that rotates, quantises and multiplies.
         const int e = ck::launch_w4_gemv(x, ldx, G, qmax, nullptr, 0, nullptr, (int)M, (int)K, w.packed,
                                          w.ldw, w.scales, w.kind == CK_WS_PER_GROUP, (int)w.N, bias,
                                          x_scale, out, ldo, nullptr, 0, stream);
         return hip_status(e, fn);
     }
-    // W4A4 codes bound for the tiled GEMM are stored two per byte, which
-    // halves the codes traffic on both sides of the workspace.
-    const GemmPath path = pick_path(M, K);
-    if (path == GemmPath::kTiled)
-        CK_TRY(check_tiles(fn, M, w.N));
-    const bool a4 = bits == 4 && path == GemmPath::kTiled;
-    const int64_t ldq = a4 ? K / 2 : K;
     int8_t *codes = static_cast<int8_t *>(ws);
-    float *rs = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round_up((size_t)(M * K), kWsAlign));
-    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, qmax, codes, ldq, rs, nullptr, 0, a4,
-                                          stream);
+    float *rs = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + plan.scales_off);
+    const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, qmax, codes, plan.ldq, rs, nullptr, 0,
+                                          plan.a4, stream);
     if (e != 0)
         return hip_status(e, fn);
-    return run_gemm(fn, codes, ldq, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, a4, stream);
+    return run_gemm(fn, codes, plan.ldq, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, plan.a4, stream);
 }
 
 }  // namespace
@@ -509,6 +549,16 @@ int ck_w4a4_linear_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, in
     const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
     return linear_common("ck_w4a4_linear", 4, x, M, K, ldx, G, w, bias, x_scale, out, ldo, ws,
                          ws_bytes, stream);
+}
+
+int ck_w4a4_linear_noalloc_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                                const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                                int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                                float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    return linear_common("ck_w4a4_linear_noalloc", 4, x, M, K, ldx, G, w, bias, x_scale, out, ldo,
+                         nullptr, 0, stream, true);
 }
 
 int ck_w4a16_gemv_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint8_t *packed,
@@ -727,6 +777,16 @@ ck_status ck_test_gemm_i32_a4(const uint8_t *codes4, int64_t ldq, int64_t M, int
 {
     return static_cast<ck_status>(ck_test_gemm_i32_a4_impl(codes4, ldq, M, K, packed, ldw, N, acc,
             lda, stream));
+}
+
+ck_status ck_w4a4_linear_noalloc(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
+                                 const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                                 int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                                 float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_w4a4_linear_noalloc_impl(x, M, K, ldx, G, packed, ldw, w_scales,
+                                                               scale_kind, Gw, N, bias, x_scale, out,
+                                                               ldo, stream));
 }
 
 }  // extern "C"

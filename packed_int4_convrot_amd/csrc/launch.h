@@ -53,4 +53,11 @@ int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_
                       const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream);
 bool w4a16_supports(int64_t K);
 
+// Library-owned device scratch of the allocation-free linear (static_scratch.hip):
+// its size in bytes, and its address on the current device, which must be the
+// device of `stream` (NULL: the null stream); looked up once per device.  Returns
+// 0 or a hipError_t.
+size_t static_scratch_bytes();
+int static_scratch(void *stream, void **ptr);
+
 }  // namespace ck

@@ -224,6 +224,26 @@ def test_test_hooks_reject():
     assert g(P, 128, (1 << 22), 256, P3, 128, (1 << 22), P5, (1 << 22), None) == ck.CK_ERR_UNSUPPORTED
 
 
+def test_noalloc_linear_rejects_before_any_hip_call():
+    """The allocation-free linear validates like ck_w4a4_linear and refuses sizes beyond
+    its 64 MiB static scratch with CK_ERR_UNSUPPORTED, all before any HIP call."""
+    f = lib.ck_w4a4_linear_noalloc
+
+    def call(M=4, K=256, ldx=256, G=64, N=16, scale_kind=0, x_scale=1.0, out=P4, ldo=16):
+        return f(P, M, K, ldx, G, P2, K // 2, P3, scale_kind, 64, N, None, x_scale, out, ldo, None)
+
+    assert call(M=0) == ck.CK_OK
+    assert call(G=32) == ck.CK_ERR_UNSUPPORTED
+    assert call(K=96, ldx=96) == ck.CK_ERR_INVALID_ARG
+    assert call(x_scale=0.0) == ck.CK_ERR_INVALID_ARG
+    assert call(out=P + 64) == ck.CK_ERR_INVALID_ARG          # output overlaps x
+    # packed codes of the tiled path: 8192 * 32768 / 2 = 128 MiB > 64 MiB
+    assert call(M=8192, K=32768, ldx=32768, N=16) == ck.CK_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.ck_last_error_msg()
+    # few-row path keeps one code per byte: 64 rows of 32768 fit, as do 8192 rows of 16384
+    # (those would launch, so they are not called here)
+
+
 def test_error_message_is_thread_local():
     import threading
     rq(G=32)
