@@ -55,7 +55,8 @@
  *  - Every entry point returns a ck_status (CK_OK on success).
  *  - Alignment (CK_ERR_INVALID_ARG otherwise): x and codes 16-byte aligned,
  *    ldx % 8 == 0, ldq % 16 == 0, packed weights 16-byte aligned with
- *    ldw % 16 == 0; AWQ scales and zero points 16-byte aligned; outputs
+ *    ldw % 16 == 0; per-group weight scales, AWQ scales and zero points
+ *    16-byte aligned (per-channel weight scales 2-byte aligned); outputs
  *    16-byte aligned with 16-byte aligned rows (bf16: ldo % 8 == 0; int32
  *    test outputs: lda % 4 == 0).
  */

@@ -159,8 +159,9 @@ int check_weights(const char *fn, const Weights &w, int64_t K, bool need_scales)
             return fail(CK_ERR_INVALID_ARG, "%s: unknown weight-scale kind %d", fn, w.kind);
         if (w.kind == CK_WS_PER_GROUP && w.Gw != 64)
             return fail(CK_ERR_UNSUPPORTED, "%s: per-group weight scales need Gw == 64 (got %d)", fn, w.Gw);
-        if (!aligned(w.scales, 2))
-            return fail(CK_ERR_INVALID_ARG, "%s: weight scales must be 2-byte aligned", fn);
+        if (!aligned(w.scales, w.kind == CK_WS_PER_GROUP ? 16 : 2))
+            return fail(CK_ERR_INVALID_ARG, "%s: weight scales must be %d-byte aligned", fn,
+                        w.kind == CK_WS_PER_GROUP ? 16 : 2);
     }
     return CK_OK;
 }

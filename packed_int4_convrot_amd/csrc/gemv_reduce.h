@@ -28,13 +28,28 @@ __device__ __forceinline__ uint32_t add32(uint32_t a, uint32_t b)
         return a + b;
 }
 
-// Sum of p[r] over the 64 lanes for r < R (R = 8 or 16).  Afterwards lane l
-// holds the total of row l >> (6 - log2 R) (every lane of that row group
+// One halving step of the transposed reduction on V values per lane: lanes with
+// bit MASK set keep the upper V / 2 rows, the others the lower, and each adds
+// its partner's (lane ^ MASK) share of the rows it keeps.
+template <int MASK, int V, bool F>
+__device__ __forceinline__ void halve_rows(uint32_t *p, int lane)
+{
+    const bool hi = lane & MASK;
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+        const uint32_t keep = hi ? p[j + V / 2] : p[j];
+        const uint32_t send = hi ? p[j] : p[j + V / 2];
+        p[j] = add32<F>(keep, lane_xor_u<MASK>(send));
+    }
+}
+
+// Sum of p[r] over the 64 lanes for r < R (R = 8, 16 or 32).  Afterwards lane
+// l holds the total of row l >> (6 - log2 R) (every lane of that row group
 // holds the same value).
 template <int R, bool F>
 __device__ __forceinline__ uint32_t transposed_row_sum(uint32_t (&p)[R], int lane)
 {
-    static_assert(R == 8 || R == 16, "R");
+    static_assert(R == 8 || R == 16 || R == 32, "R");
 #pragma unroll
     for (int j = 0; j < R / 2; ++j) {  // lane ^ 32: upper half keeps rows + R/2
         const auto s = __builtin_amdgcn_permlane32_swap(p[j], p[j + R / 2], false, false);
@@ -45,23 +60,12 @@ __device__ __forceinline__ uint32_t transposed_row_sum(uint32_t (&p)[R], int lan
         const auto s = __builtin_amdgcn_permlane16_swap(p[j], p[j + R / 4], false, false);
         p[j] = add32<F>(s[0], s[1]);
     }
-    const bool b3 = lane & 8;
-#pragma unroll
-    for (int j = 0; j < R / 8; ++j) {  // lane ^ 8
-        const uint32_t keep = b3 ? p[j + R / 8] : p[j];
-        const uint32_t send = b3 ? p[j] : p[j + R / 8];
-        p[j] = add32<F>(keep, lane_xor_u<8>(send));
-    }
+    halve_rows<8, R / 4, F>(p, lane);                       // R / 8 rows left
+    if constexpr (R >= 16) halve_rows<4, R / 8, F>(p, lane);
+    if constexpr (R >= 32) halve_rows<2, R / 16, F>(p, lane);
     uint32_t v = p[0];
-    if constexpr (R == 16) {  // lane ^ 4 (two rows left)
-        const bool b2 = lane & 4;
-        const uint32_t keep = b2 ? p[1] : p[0];
-        const uint32_t send = b2 ? p[0] : p[1];
-        v = add32<F>(keep, lane_xor_u<4>(send));
-    } else {
-        v = add32<F>(v, lane_xor_u<4>(v));
-    }
-    v = add32<F>(v, lane_xor_u<2>(v));
+    if constexpr (R == 8) v = add32<F>(v, lane_xor_u<4>(v));
+    if constexpr (R <= 16) v = add32<F>(v, lane_xor_u<2>(v));
     v = add32<F>(v, lane_xor_u<1>(v));
     return v;
 }

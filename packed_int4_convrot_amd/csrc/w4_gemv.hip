@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kMaxWaves = 8;  // K <= 16384
 #ifndef CK_GEMV_ROWS
-#define CK_GEMV_ROWS 8  // weight rows per block (8 or 16)
+#define CK_GEMV_ROWS 8  // weight rows per block (8, 16 or 32)
 #endif
 // The fused form pays the rotation once per block; measured on MI355X it is
 // faster than a separate rotate-quant launch only for a single activation row.
@@ -103,11 +103,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
                 araw[m][c] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + kc + 16 * c);
         }
     }
-    uint16_t sv[PER_GROUP ? R : 1];
+    // The R scales of the lane's group are contiguous: R / 8 16-byte loads.
+    // (Eight 2-byte loads per row block were measured ~0.5 us slower.)
+    u32x4 sv[PER_GROUP ? R / 8 : 1];
     if constexpr (PER_GROUP) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            sv[r] = w_scales[(int64_t)(kc / 64) * N + n0 + r];
+        for (int q = 0; q < R / 8; ++q)
+            sv[q] = *reinterpret_cast<const u32x4 *>(w_scales + (int64_t)(kc / 64) * N + n0 + 8 * q);
     }
     u32x4 wv[R];
 #pragma unroll
@@ -230,14 +232,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
             }
             acc -= asum8[m];
             if constexpr (FSUM)
-                part[m][r] = __float_as_uint(bf16_to_f32(sv[r]) * (float)acc);
+                part[m][r] = __float_as_uint(__uint_as_float(r % 2 ? sv[r / 8][(r % 8) / 2] & 0xffff0000u
+                                                                   : sv[r / 8][(r % 8) / 2] << 16) *
+                                             (float)acc);
             else
                 part[m][r] = (uint32_t)acc;
         }
     }
 
     // 4. sum over the lanes of the wave, then over the waves (fixed order).
-    constexpr int kShift = R == 16 ? 2 : 3;
+    constexpr int kShift = R == 32 ? 1 : R == 16 ? 2 : 3;
     const int row = lane >> kShift;
     const bool owner = (lane & ((1 << kShift) - 1)) == 0;
 #pragma unroll
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
             s_red[wave][row][m] = t;
     }
     __syncthreads();
-    if (threadIdx.x < R * M) {
-        const int r = threadIdx.x / M, m = threadIdx.x % M;
+    for (int e = threadIdx.x; e < R * M; e += blockDim.x) {
+        const int r = e / M, m = e % M;
         const int n = n0 + r;
         uint32_t t = s_red[0][r][m];
         for (int w = 1; w < nw; ++w)

@@ -107,6 +107,12 @@ def test_gemm_q_rejects(kw, status):
     assert gq(**kw) == status
 
 
+def test_per_group_scales_need_16_byte_alignment():
+    # the decode kernels read a row block's per-group scales with 16-byte loads
+    assert gq(ws=P4 + 8, kind=1) == ck.CK_ERR_INVALID_ARG
+    assert b"16-byte" in lib.ck_last_error_msg()
+
+
 def test_launch_size_limits():
     # rows beyond one launch's grid, and a tiled GEMM whose tile grid would overflow
     assert rq(M=(1 << 22) + 1) == ck.CK_ERR_UNSUPPORTED
