@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -60,6 +61,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the secondary measurements and the clock readings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-oracle-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copies", type=int, default=32, help="weight copies cycled through (cold cache)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain elementwise copy of CALIB_BYTES (counter calibration)")
@@ -318,6 +320,9 @@ def measured_traffic(bytes_per_launch_alg):
 
 def main():
     args = parse()
+    if args.cpu_oracle_child:
+        oracle_child()
+        return
     if args.write_traffic:
         write_traffic(*args.write_traffic, alg_bytes=headline_alg_bytes(1, 3840, 10240))
         return
@@ -375,14 +380,13 @@ def main():
     def step(i):
         ck.linear(x, G, 8, packs[i % args.copies], scls[i % args.copies], True, out=out, workspace=ws)
 
-    # W warm-up steps: W mod K steps from a graph of their own, then W // K replays
-    # of the timed graph itself, so that the timed replay is not that graph's first
-    # (a graph's first replay measured ~3-5% slower than the next ones).
+    # Warm-up: at least W steps, as whole replays of the timed graph itself (at least
+    # one), so that the timed replay is never that graph's first: a graph's first
+    # replay measured 3-5% slower than the next ones (with --steps 20, about 0.4 us
+    # per step).  warmup_steps_run in the result is the number of steps this ran.
     g_steps = capture(torch, step, args.steps)
-    rest = args.warmup % args.steps
-    if rest:
-        capture(torch, step, rest).replay()
-    for _ in range(args.warmup // args.steps):
+    warm_replays = max(1, -(-args.warmup // args.steps))
+    for _ in range(warm_replays):
         g_steps.replay()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -424,6 +428,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_replays * args.steps,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -452,7 +457,7 @@ def main():
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(workloads, inp, G, packed_bytes)
+        result["cpu_baseline"] = cpu_baseline(packed_bytes, result.get("also"), ms_step * 1e3)
 
     print(json.dumps(result), flush=True)
 
@@ -600,9 +605,17 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
         codes, rs = ck.rotate_quant(x, 64, 8)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         us = _time(lambda i: ck.gemv(codes, rs, packs[i % 32], scl, True, out=out), stream, 100)
-        lin = _time(lambda i: ck.linear(x, 64, 8, packs[i % 32], scl, True, out=out), stream, 100)
-        res["w4a8_decode_gemv_m%d" % M] = {"gemv_us": round(us, 3), "linear_us": round(lin, 3),
-                                          "packed_GBps": round(N * K / 2 / us / 1e3, 1)}
+        ws = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)
+        lin = _time(lambda i: ck.linear(x, 64, 8, packs[i % 32], scl, True, out=out, workspace=ws), stream, 100)
+        # algorithmic bytes: packed weights, group scales, the activations (codes for the
+        # GEMV, bf16 x for the whole linear) and the bf16 output
+        wb = N * K // 2 + (K // 64) * N * 2 + 2 * M * N
+        gemv_bytes, lin_bytes = wb + M * K + 4 * M, wb + 2 * M * K
+        res["w4a8_decode_gemv_m%d" % M] = {
+            "gemv_us": round(us, 3), "linear_us": round(lin, 3), "packed_GBps": round(N * K / 2 / us / 1e3, 1),
+            "gemv_algorithmic_bytes": gemv_bytes, "gemv_frac_hbm": round(gemv_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+            "linear_algorithmic_bytes": lin_bytes,
+            "linear_frac_hbm": round(lin_bytes / lin / 1e3 / HBM_PEAK_GBS, 4)}
     del packs
     log("bench: decode extras done")
 
@@ -614,8 +627,13 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
     packs = [u8(inp["packed"]) for _ in range(64)]
     scl = bf16(inp["w_scales"])
     out = torch.empty((32, w["N"]), dtype=torch.bfloat16, device=dev)
-    us = _time(lambda i: ck.linear(x, 64, 8, packs[i % 64], scl, True, out=out), stream, 100)
-    res["w4a8_linear_m32_k3840_n3840_g64"] = {"linear_us": round(us, 3)}
+    work = torch.empty((ck.workspace_bytes(32, w["K"], w["N"]),), dtype=torch.uint8, device=dev)
+    us = _time(lambda i: ck.linear(x, 64, 8, packs[i % 64], scl, True, out=out, workspace=work), stream, 100)
+    # x, codes written and read, row scales, packed weights, group scales, output
+    alg = 368768 + 8202368
+    res["w4a8_linear_m32_k3840_n3840_g64"] = {"linear_us": round(us, 3), "algorithmic_bytes": alg,
+                                              "GBps": round(alg / us / 1e3, 1),
+                                              "frac_hbm": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)}
     del packs
     log("bench: M=32 done")
 
@@ -625,14 +643,21 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
         inp = workloads.workload_inputs(name)
         M, K, N, G = w["M"], w["K"], w["N"], w["G"]
         x = bf16(inp["x"])
+        # enough copies of x that the activations come from HBM (> 512 MB together,
+        # twice the 256 MB Infinity Cache): the rotate-quant and whole-linear figures
+        # below are cold; the GEMM's operands (packed codes and weights, 23-62 MB) stay
+        # cache-resident, which an MFMA-bound kernel does not notice
+        nx = max(2, -(-512 * 2 ** 20 // (M * K * 2)))
+        xs = [x] + [x.clone() for _ in range(nx - 1)]
         packed = u8(inp["packed"])
         scl = bf16(inp["w_scales"])
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         work = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)  # held by the caller
         # the linear's own two launches: packed rotate-quant, then the GEMM on packed codes
         codes4, rs = ck.rotate_quant_packed4(x, G)
-        lin = _time(lambda i: ck.linear(x, G, 4, packed, scl, False, out=out, workspace=work), stream, 20)
-        rq = _time(lambda i: ck.rotate_quant_packed4(x, G, codes4, rs), stream, 20)
+        lin = _time(lambda i: ck.linear(xs[i % nx], G, 4, packed, scl, False, out=out, workspace=work), stream, 20)
+        rq = _time(lambda i: ck.rotate_quant_packed4(xs[i % nx], G, codes4, rs), stream, 20)
+        rq_warm = _time(lambda i: ck.rotate_quant_packed4(x, G, codes4, rs), stream, 20)
         gm = _time(lambda i: ck.gemm_packed4(codes4, rs, packed, scl, False, out=out), stream, 20)
         # codes one per byte (ck_rotate_quant + ck_w4_gemm_q), for comparison
         codes, rs8 = ck.rotate_quant(x, G, 4)
@@ -640,7 +665,10 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
         ops = 2.0 * M * N * K
         rq_bytes = M * K * 2 + M * K // 2 + M * 4
         clk = gfx_clock_mhz(torch, capture(torch, lambda i: ck.gemm_packed4(codes4, rs, packed, scl, False, out=out), 40))
-        res[name] = {"linear_us": round(lin, 2), "rotate_quant_us": round(rq, 2), "gemm_us": round(gm, 2),
+        res[name] = {"x_copies_cycled": nx, "linear_us": round(lin, 2), "rotate_quant_us": round(rq, 2),
+                     "rotate_quant_warm_us": round(rq_warm, 2), "gemm_us": round(gm, 2),
+                     "timing": "linear_us and rotate_quant_us cycle x_copies_cycled copies of x (cold); "
+                               "rotate_quant_warm_us re-reads one x; gemm_us re-reads cache-resident operands",
                      "gemm_gfx_clock_mhz": clk,
                      "gemm_int8_TOPS": round(ops / gm / 1e6, 1),
                      "gemm_frac_int8_peak": round(ops / gm / 1e6 / INT8_PEAK_TOPS, 4),
@@ -648,7 +676,7 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
                      "rotate_quant_GBps": round(rq_bytes / rq / 1e3, 1),
                      "rotate_quant_frac_hbm": round(rq_bytes / rq / 1e3 / HBM_PEAK_GBS, 4),
                      "byte_codes_gemm_us": round(gm8, 2)}
-        del x, packed, out, codes, codes4, work
+        del x, xs, packed, out, codes, codes4, work
         log("bench: %s done" % name)
 
     # standalone rotate-quant, strided [8192, 10240] in [8192, 10752]
@@ -717,23 +745,130 @@ def extras(ck, workloads, torch, dev, bf16, u8, stream):
     return res
 
 
-def cpu_baseline(workloads, inp, G, packed_bytes):
-    """The oracle (single-threaded C, fp64 sums) on the same M = 1 decode step, repeated
-    for a bounded ~10 s of host time."""
+def _host_cpu():
+    """CPU model name and core counts of the host the oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+# Rows of the M = 8192 workloads and of rotate-quant on which the oracle is timed
+# (the same kind of sample the parity tests check); the oracle's work is linear in
+# the rows, so its time for the whole workload is this time x M / rows.
+ORACLE_SAMPLE_ROWS = {"w4a4_linear_m8192_k3840_n3840_g64": 8, "w4a4_linear_m8192_k10240_n3840_g256": 4,
+                      "rotate_quant_m8192_k10240_ld10752": 16}
+
+
+def oracle_child():
+    """Time the oracle (single-threaded C) on every workload, pinned to one core.  Runs
+    in its own process (bench.py --cpu-oracle-child) so that the pinning does not touch
+    the GPU process; prints one JSON line."""
+    cpu = min(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {cpu})
     import oracle
+    import workloads
     oracle.build()
+
+    def stages(x, G, bits, packed, w_scales, per_group, K=None):
+        t = {}
+        t0 = time.perf_counter()
+        xr = oracle.rotate(x, G, K)
+        t["rotate"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        codes, sx = oracle.quantize(xr, bits)
+        t["quantize"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        w = oracle.unpack(packed, codes.shape[1])
+        t["unpack"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        acc = oracle.int_gemm(codes, w, 64 if per_group else None)
+        t["int_gemm"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.epilogue(acc, sx, w_scales, per_group)
+        t["epilogue"] = time.perf_counter() - t0
+        return t
+
+    res = {}
+    name = "w4a8_decode_gemv_k3840_n10240_g64"
+    w = workloads.WORKLOADS[name]
+    for M in w["Ms"]:
+        inp = workloads.workload_inputs(name, M=M)
+        reps = 10 if M == 1 else 3
+        tot = {}
+        for _ in range(reps):
+            for k, v in stages(inp["x"], w["G"], w["bits"], inp["packed"], inp["w_scales"], True).items():
+                tot[k] = tot.get(k, 0.0) + v / reps
+        res["%s_m%d" % (name, M)] = {"rows_timed": M, "rows": M, "stages_us": {k: round(v * 1e6, 1) for k, v in tot.items()},
+                                     "us": round(sum(tot.values()) * 1e6, 1), "repeats": reps}
+    for name in ("w4a8_linear_m32_k3840_n3840_g64", "w4a4_linear_m8192_k3840_n3840_g64",
+                 "w4a4_linear_m8192_k10240_n3840_g256"):
+        w = workloads.WORKLOADS[name]
+        inp = workloads.workload_inputs(name)
+        rows = ORACLE_SAMPLE_ROWS.get(name, w["M"])
+        t = stages(inp["x"][:rows], w["G"], w["bits"], inp["packed"], inp["w_scales"], w["scale"] == "group")
+        # every stage but the weight unpack is per row
+        per_row = sum(v for k, v in t.items() if k != "unpack")
+        res[name] = {"rows_timed": rows, "rows": w["M"], "stages_us": {k: round(v * 1e6, 1) for k, v in t.items()},
+                     "us": round((per_row * w["M"] / rows + t["unpack"]) * 1e6, 1)}
+    name = "rotate_quant_m8192_k10240_ld10752"
+    w = workloads.WORKLOADS[name]
+    x = workloads.workload_inputs(name)["x"]
+    rows = ORACLE_SAMPLE_ROWS[name]
+    for G in w["Gs"]:
+        t0 = time.perf_counter()
+        xr = oracle.rotate(x[:rows], G, w["K"])
+        t1 = time.perf_counter()
+        oracle.quantize(xr, w["bits"])
+        t2 = time.perf_counter()
+        res["%s_g%d" % (name, G)] = {"rows_timed": rows, "rows": w["M"],
+                                     "stages_us": {"rotate": round((t1 - t0) * 1e6, 1), "quantize": round((t2 - t1) * 1e6, 1)},
+                                     "us": round((t2 - t0) * w["M"] / rows * 1e6, 1)}
+    name = "awq_w4a16_gemv_m1_k3072_n18432"
+    d = workloads.workload_inputs(name)
     t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.linear(inp["x"], G, 8, inp["packed"], inp["w_scales"], True)
-        n += 1
-        if time.perf_counter() - t0 > 10.0 or n >= 200:
-            break
-    dt = (time.perf_counter() - t0) / n
-    return {"value": round(packed_bytes / dt / 1e9, 4), "unit": "GB/s (packed weight, M=1 step)",
-            "cores": 1, "kind": "oracle",
-            "sample": "%d full M=1 steps (rotation by explicit H_64 product, quantisation, unpack, "
-                      "exact integer sums, fp64 epilogue), %.3f s each" % (n, dt)}
+    oracle.awq_gemv(d["x"], d["packed"], d["scales"], d["zeros"])
+    res[name] = {"rows_timed": 1, "rows": 1, "us": round((time.perf_counter() - t0) * 1e6, 1)}
+    print(json.dumps({"cpu": cpu, "host": _host_cpu(), "workloads": res}), flush=True)
+
+
+# The GPU figure (microseconds of the whole step) that each oracle entry is set beside.
+def _gpu_us(also, headline_us, key):
+    if key == "w4a8_decode_gemv_k3840_n10240_g64_m1":
+        return headline_us
+    if key.startswith("w4a8_decode_gemv_k3840_n10240_g64_m"):
+        return also.get("w4a8_decode_gemv_m%s" % key.rsplit("_m", 1)[1], {}).get("linear_us")
+    if key.startswith("rotate_quant") or key.startswith("awq"):
+        return also.get(key, {}).get("us")
+    return also.get(key, {}).get("linear_us")
+
+
+def cpu_baseline(packed_bytes, also, headline_us):
+    """The oracle on every workload, single-threaded and pinned to one core, in a child
+    process; the headline value is the packed-weight rate of the M = 1 decode step."""
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-oracle-child"], capture_output=True,
+                       text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-500:]}
+    rec = json.loads(r.stdout.strip().splitlines()[-1])
+    per = {}
+    for key, v in rec["workloads"].items():
+        g = _gpu_us(also or {}, headline_us, key)
+        per[key] = dict(v, gpu_us=g, speedup=round(v["us"] / g, 1) if g else None)
+    head = per["w4a8_decode_gemv_k3840_n10240_g64_m1"]
+    return {"value": round(packed_bytes / (head["us"] * 1e-6) / 1e9, 4), "unit": "GB/s (packed weight, M=1 step)",
+            "cores": 1, "kind": "oracle", "host": rec["host"], "pinned_cpu": rec["cpu"],
+            "sample": "each workload's oracle steps (rotation by explicit H_G product, quantisation, unpack, exact "
+                      "integer sums, fp64 epilogue; AWQ: fp64 dequantised product) in one process pinned to one "
+                      "core; decode M = 1 / 4 / 8, the M = 32 linear and AWQ whole, the M = 8192 linears and "
+                      "rotate-quant on the first rows_timed rows, scaled by rows / rows_timed",
+            "per_workload": per}
 
 
 if __name__ == "__main__":

@@ -94,3 +94,18 @@ def test_traffic_is_null_once_the_kernel_changes(tmp_path, monkeypatch):
     rec["sources_sha"] = bench.sources_sha(bench.GEMV_SOURCES)
     p.write_text("header\nJSON: %s\n" % json.dumps(rec))
     assert bench.measured_traffic(1) == 123
+
+
+def test_oracle_baseline_pairs_each_workload_with_its_gpu_figure():
+    also = {"w4a8_decode_gemv_m4": {"linear_us": 11.0}, "w4a8_linear_m32_k3840_n3840_g64": {"linear_us": 12.0},
+            "rotate_quant_m8192_k10240_ld10752_g64": {"us": 43.0}, "awq_w4a16_gemv_m1_k3072_n18432": {"us": 8.7},
+            "w4a4_linear_m8192_k3840_n3840_g64": {"linear_us": 115.0}}
+    assert bench._gpu_us(also, 6.8, "w4a8_decode_gemv_k3840_n10240_g64_m1") == 6.8
+    assert bench._gpu_us(also, 6.8, "w4a8_decode_gemv_k3840_n10240_g64_m4") == 11.0
+    assert bench._gpu_us(also, 6.8, "w4a8_linear_m32_k3840_n3840_g64") == 12.0
+    assert bench._gpu_us(also, 6.8, "rotate_quant_m8192_k10240_ld10752_g64") == 43.0
+    assert bench._gpu_us(also, 6.8, "awq_w4a16_gemv_m1_k3072_n18432") == 8.7
+    assert bench._gpu_us(also, 6.8, "w4a4_linear_m8192_k3840_n3840_g64") == 115.0
+    assert bench._gpu_us({}, 6.8, "w4a4_linear_m8192_k10240_n3840_g256") is None
+    host = bench._host_cpu()
+    assert host["nproc"] >= 1 and host["affinity_cpus"] >= 1
