@@ -222,13 +222,13 @@ ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, i
  * with the codes and row scales held in a scratch array owned by the library
  * instead of a caller workspace.  Same arguments minus ws / ws_bytes, same
  * kernels, same results bit for bit.
- *   - The scratch is a static device array of 64 MiB (67108864 bytes), one
+ *   - The scratch is a static device array of 64 MiB + 64 KiB (67174400 bytes), one
  *     copy on each GPU that loads the library, kept until the process ends.
  *     A call needing more returns CK_ERR_UNSUPPORTED before anything is
  *     enqueued: M * K / 2 bytes of packed codes (tiled path, M > 64) or M * K
  *     bytes (fewer rows), each rounded up to 256, plus 4 * M bytes of row
  *     scales rounded up to 256; M = 1 uses no scratch.  For example M = 8192
- *     rows fit up to K = 16384.
+ *     rows fit up to K = 16384, and M = 16384 rows up to K = 8192.
  *   - The call allocates nothing (no hipMalloc, no allocating library call).
  *     Its scratch address on a device is looked up (hipGetSymbolAddress) on the
  *     first call made with that device current; `stream` must belong to the
@@ -272,7 +272,8 @@ ck_status ck_w4a16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  * (which keeps W exact) by W's bf16 rounding.
  *   x       bf16 [M, ldx], ldx <= 2^22, any M >= 0
  *   packed  uint8 [N, ldw] as in ck_w4_gemm_q; N % 16 == 0
- *   scales, zeros  bf16 [K/Gw, N], Gw = 64, 2-byte aligned
+ *   scales, zeros  bf16 [K/Gw, N], Gw = 64, each 16-byte aligned
+ *           (CK_ERR_INVALID_ARG otherwise)
  *   bias    bf16 [N] or NULL;  out bf16 [M, ldo] (16-byte aligned rows)
  */
 ck_status ck_w4a16_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,

@@ -110,6 +110,8 @@ int oracle_rotate(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  *   a > 0 : s = fp32(a / qmax), inv = fp32(qmax / a),
  *           code = clamp(rne(fp32(xr * inv)), -qmax, qmax)
  *   a == 0: code = 0, s = 1.0
+ * Defined for finite values only: a row holding Inf or NaN is BAD_ARG (the
+ * pages give no rule for it, and a NaN code has no integer value).
  */
 int oracle_quantize(const float *xr, int64_t M, int64_t K, int64_t ldr,
                     int32_t qmax, int8_t *codes, int64_t ldq, float *scales)
@@ -122,6 +124,8 @@ int oracle_quantize(const float *xr, int64_t M, int64_t K, int64_t ldr,
         const float *row = xr + m * ldr;
         float a = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(row[k]))
+                return BAD_ARG;
             float v = fabsf(row[k]);
             if (v > a)
                 a = v;
@@ -171,6 +175,7 @@ static uint16_t bf16_round(float f)
  *   code = clamp(rne(fp32(wr * fp32(1 / s))), -7, 7), else code = 0;
  *   stored q = code + 8, byte j of a row = q[2j] | q[2j + 1] << 4.
  * scales: bf16 bits, [N] (group == 0) or [K/group, N] (N contiguous).
+ * Finite weights only (BAD_ARG otherwise), as in oracle_quantize.
  */
 int oracle_quantize_weights(const float *wr, int64_t N, int64_t K, int64_t ldr, int32_t group,
                             uint8_t *packed, int64_t ldp, uint16_t *scales)
@@ -185,6 +190,8 @@ int oracle_quantize_weights(const float *wr, int64_t N, int64_t K, int64_t ldr, 
         for (int64_t g0 = 0; g0 < K; g0 += glen) {
             float a = 0.0f;
             for (int64_t k = g0; k < g0 + glen; ++k) {
+                if (!isfinite(row[k]))
+                    return BAD_ARG;
                 float v = fabsf(row[k]);
                 if (v > a)
                     a = v;

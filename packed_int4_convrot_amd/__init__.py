@@ -272,7 +272,7 @@ def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
     return out
 
 
-NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's static scratch per GPU (include/ck.h)
+NOALLOC_SCRATCH_BYTES = (64 << 20) + (64 << 10)   # the library's static scratch per GPU (include/ck.h)
 
 
 def w4a4_linear_noalloc(x, G: int, packed, w_scales, per_group: bool, bias=None,

@@ -11,6 +11,8 @@ C++ compiled with g++.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
+import json
 import os
 import subprocess
 import sys
@@ -43,6 +45,37 @@ def _run(cmd):
     return out
 
 
+RESOURCE_REPORT = os.path.join(BUILD, "resource_usage.json")
+_FIELDS = {"VGPRs": "vgpr", "AGPRs": "agpr", "SGPRs": "sgpr", "ScratchSize [bytes/lane]": "scratch",
+           "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill", "LDS Size [bytes/block]": "lds",
+           "Occupancy [waves/SIMD]": "occupancy"}
+
+
+def _resource_usage(src, text):
+    """Per-kernel records from the compiler's kernel-resource-usage remarks."""
+    recs, cur = [], None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = {"source": src, "kernel": body.split(":", 1)[1].strip()}
+            recs.append(cur)
+        elif cur is not None and ":" in body:
+            key, val = (t.strip() for t in body.split(":", 1))
+            if key in _FIELDS:
+                cur[_FIELDS[key]] = int(val)
+    return recs
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    for src in HIP_SOURCES + CXX_SOURCES + sorted(f for f in os.listdir(CSRC) if f.endswith(".h")):
+        with open(os.path.join(CSRC, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = []
@@ -50,15 +83,21 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
         objs.append(obj)
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    usage = []
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
-        for out in ex.map(_run, jobs):
-            if verbose and out.strip():
-                print(out)
+        for src, out in zip(HIP_SOURCES + CXX_SOURCES, ex.map(_run, jobs)):
+            usage += _resource_usage(src, out)
+            text = "\n".join(l for l in out.splitlines() if "remark:" not in l)
+            if verbose and text.strip():
+                print(text)
+    with open(RESOURCE_REPORT, "w") as f:
+        json.dump({"sources_sha": sources_sha(), "kernels": usage}, f, indent=1)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

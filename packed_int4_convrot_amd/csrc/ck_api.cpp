@@ -601,8 +601,8 @@ int ck_w4a16_gemm_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, con
     CK_TRY(check_k(fn, K));
     const Weights w{packed, ldw, scales, CK_WS_PER_GROUP, Gw, N};
     CK_TRY(check_weights(fn, w, K, true));
-    if (!zeros || !aligned(zeros, 2))
-        return fail(CK_ERR_INVALID_ARG, "%s: zeros must be a non-NULL 2-byte aligned pointer", fn);
+    if (!zeros || !aligned(zeros, 16))
+        return fail(CK_ERR_INVALID_ARG, "%s: zeros must be a non-NULL 16-byte aligned pointer", fn);
     if (M == 0)
         return ok();
     CK_TRY(check_x(fn, x, K, ldx));

@@ -3,6 +3,7 @@
 // returns the hipError_t of the launch as an int (0 = success).
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace ck {
@@ -31,8 +32,16 @@ int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t
                    const float *row_scales, int M, int K, const uint8_t *packed, int64_t ldw,
                    const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias, float x_scale,
                    uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
-bool w4_gemv_supports(int64_t M, int64_t K);
-bool w4_gemv_fused_supports(int64_t M, int64_t K);  // G != 0 form
+// The decode GEMV: 1 <= M <= 8 activation rows, one wave per 2048 columns of K,
+// at most 8 waves; the fused rotate-quant form takes a single row.
+constexpr int kGemvMaxWaves = 8;
+constexpr int kGemvMaxM = 8;
+constexpr int kGemvMaxFusedRows = 1;
+inline bool w4_gemv_supports(int64_t M, int64_t K)
+{
+    return M >= 1 && M <= kGemvMaxM && K <= 2048 * kGemvMaxWaves;
+}
+inline bool w4_gemv_fused_supports(int64_t M, int64_t K) { return w4_gemv_supports(M, K) && M <= kGemvMaxFusedRows; }
 
 // Skinny path: M <= 64, weights streamed once, activations held in registers.
 // acc_out != nullptr selects the int32 test epilogue.
@@ -40,7 +49,28 @@ int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, 
                      const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                      bool per_group, int N, const uint16_t *bias, float x_scale,
                      uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
-bool w4_skinny_supports(int64_t M, int64_t K);
+// Shape of the few-row kernel: MT = ceil(M / 16) m-tiles; GPW groups per wave,
+// chosen so that the register copy of the activations (GPW * MT * 4 VGPRs)
+// stays at most 128; KS = ceil(K / 64 / GPW) <= 8 waves.
+constexpr int kSkinnyMaxWaves = 8;
+struct SkinnyShape {
+    int mt, ks, gpw;
+};
+inline bool skinny_shape(int64_t M, int64_t K, SkinnyShape &s)
+{
+    if (M < 1 || M > 64)
+        return false;
+    const int ng = (int)(K / 64);
+    s.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    s.gpw = s.mt == 1 ? 16 : s.mt == 2 ? (ng <= 8 * kSkinnyMaxWaves ? 8 : 16) : 8;
+    s.ks = (ng + s.gpw - 1) / s.gpw;
+    return s.ks >= 1 && s.ks <= kSkinnyMaxWaves;
+}
+inline bool w4_skinny_supports(int64_t M, int64_t K)
+{
+    SkinnyShape s;
+    return skinny_shape(M, K, s);
+}
 
 // Tiled MFMA GEMM for larger M.
 int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
@@ -51,10 +81,13 @@ int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, in
 int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed,
                       int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int N,
                       const uint16_t *bias, uint16_t *out, int64_t ldo, void *stream);
-bool w4a16_supports(int64_t K);
+inline bool w4a16_supports(int64_t K) { return K >= 64 && K <= 2048 * kGemvMaxWaves; }
 
 // Library-owned device scratch of the allocation-free linear (static_scratch.hip):
-// its size in bytes, and its address on the current device, which must be the
+// 64 MiB of codes plus 64 KiB of row scales, so that 8192 rows of K = 16384 (or
+// 16384 rows of K = 8192) packed two codes per byte fit.
+constexpr size_t kStaticScratchBytes = (size_t(64) << 20) + (size_t(64) << 10);
+// Its size in bytes, and its address on the current device, which must be the
 // device of `stream` (NULL: the null stream); looked up once per device.  Returns
 // 0 or a hipError_t.
 size_t static_scratch_bytes();

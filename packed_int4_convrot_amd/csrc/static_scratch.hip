@@ -14,7 +14,7 @@
 
 #include "launch.h"
 
-static constexpr size_t kScratchBytes = size_t(64) << 20;
+static constexpr size_t kScratchBytes = ck::kStaticScratchBytes;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 

@@ -300,7 +300,10 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     // keep every pair's decodes (6 VALU ops per tile) inside the previous
     // pair's 64 MFMA cycles.  fn holds the next step's fragments; the last
     // stage runs the plain form (its K steps may end early).
-    constexpr bool ILV = TRANS && WM == 4 && WN == 2;
+    // The bf16 tile on byte codes keeps the compiler's order: with the fixed
+    // order its fragments, the next step's head and the accumulators need one
+    // register more than the 256 it has (a spill in every K step).
+    constexpr bool ILV = TRANS && WM == 4 && WN == 2 && (A4 || OUT_I32);
     struct Head {
         v4i b[WN];
         v4i a;

@@ -34,16 +34,13 @@
 namespace ck {
 namespace {
 
-constexpr int kMaxWaves = 8;  // K <= 16384
+constexpr int kMaxWaves = kGemvMaxWaves;  // K <= 16384
 #ifndef CK_GEMV_ROWS
 #define CK_GEMV_ROWS 8  // weight rows per block (8, 16 or 32)
 #endif
 // The fused form pays the rotation once per block; measured on MI355X it is
 // faster than a separate rotate-quant launch only for a single activation row.
-constexpr int kMaxFusedRows = 1;
-#ifndef CK_GEMV_MAX_M
-#define CK_GEMV_MAX_M 8
-#endif
+constexpr int kMaxFusedRows = kGemvMaxFusedRows;
 
 // One cross-lane butterfly stage on 32 values per lane (fused rotation).
 template <int MASK>
@@ -312,8 +309,6 @@ hipError_t launch_m(int G, bool pg, bool i32, const uint16_t *x, int64_t ldx, fl
 
 }  // namespace
 
-bool w4_gemv_supports(int64_t M, int64_t K) { return M >= 1 && M <= CK_GEMV_MAX_M && K <= 2048 * kMaxWaves; }
-bool w4_gemv_fused_supports(int64_t M, int64_t K) { return w4_gemv_supports(M, K) && M <= kMaxFusedRows; }
 
 int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
                    const float *row_scales, int M, int K, const uint8_t *packed, int64_t ldw,
@@ -332,12 +327,10 @@ int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t
     case 2: e = launch_m<2, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 3: e = launch_m<3, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 4: e = launch_m<4, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-#if CK_GEMV_MAX_M > 4
     case 5: e = launch_m<5, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 6: e = launch_m<6, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 7: e = launch_m<7, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
     case 8: e = launch_m<8, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-#endif
     default: e = hipErrorInvalidValue; break;
     }
     return (int)e;

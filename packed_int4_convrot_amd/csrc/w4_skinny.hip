@@ -38,7 +38,7 @@
 namespace ck {
 namespace {
 
-constexpr int kMaxWaves = 8;  // 512 threads: up to 256 VGPRs per lane
+constexpr int kMaxWaves = kSkinnyMaxWaves;  // 512 threads: up to 256 VGPRs per lane
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -194,24 +194,6 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     }
 }
 
-struct SkinnyShape {
-    int mt, ks, gpw;
-};
-
-// MT = ceil(M / 16) m-tiles; GPW groups per wave, chosen so that the
-// register copy of the activations (GPW * MT * 4 VGPRs) stays at most 128;
-// KS = ceil(K / 64 / GPW) <= 8 waves.
-bool skinny_shape(int64_t M, int64_t K, SkinnyShape &s)
-{
-    if (M < 1 || M > 64)
-        return false;
-    const int ng = (int)(K / 64);
-    s.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    s.gpw = s.mt == 1 ? 16 : s.mt == 2 ? (ng <= 8 * kMaxWaves ? 8 : 16) : 8;
-    s.ks = (ng + s.gpw - 1) / s.gpw;
-    return s.ks >= 1 && s.ks <= kMaxWaves;
-}
-
 template <int MT, int GPW, bool PG, bool I32>
 hipError_t launch_t(const SkinnyShape &sh, const int8_t *codes, int64_t ldq, const float *rs, int M,
                     int K, const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N,
@@ -249,12 +231,6 @@ hipError_t launch_mt(const SkinnyShape &sh, bool pg, bool i32, const int8_t *cod
 }
 
 }  // namespace
-
-bool w4_skinny_supports(int64_t M, int64_t K)
-{
-    SkinnyShape s;
-    return skinny_shape(M, K, s);
-}
 
 int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
                      const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,

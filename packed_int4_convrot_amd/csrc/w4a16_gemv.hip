@@ -84,9 +84,11 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
         wv[r] = load_nt16(packed + (int64_t)(n0 + r) * ldw + kc / 2);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads in this order
 
-    uint32_t part[M][R];
+    const int row = lane >> 3;
+    const bool owner = (lane & 7) == 0;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
+        uint32_t part[MC][R];
         const int mb = pass * MC;
         if (pass > 0) {
             __builtin_amdgcn_sched_barrier(0);  // passes run one after another
@@ -141,21 +143,21 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
             const float zc = __builtin_fmaf(-136.f, s, z);
 #pragma unroll
             for (int m = 0; m < MC; ++m)
-                if (mb + m < M)
-                    part[mb + m][r] = __float_as_uint(__builtin_fmaf(s, acc[m], zc * xs[m]));
+                part[m][r] = __float_as_uint(__builtin_fmaf(s, acc[m], zc * xs[m]));
             if constexpr (M > 1)
                 __builtin_amdgcn_sched_barrier(0);  // one row's decode live at a time
         }
-    }
-
-    // 4. Sum over the lanes of the wave, then over the waves (fixed order).
-    const int row = lane >> 3;
-    const bool owner = (lane & 7) == 0;
+        // 4. Sum the pass's rows over the lanes of the wave (the waves are summed
+        //    below, in a fixed order); done per pass, so that only one pass's
+        //    partials are live.
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const uint32_t t = transposed_row_sum<R, true>(part[m], lane);
-        if (owner)
-            s_red[wave][row][m] = t;
+        for (int m = 0; m < MC; ++m) {
+            if (mb + m < M) {
+                const uint32_t t = transposed_row_sum<R, true>(part[m], lane);
+                if (owner)
+                    s_red[wave][row][mb + m] = t;
+            }
+        }
     }
     __syncthreads();
     if (threadIdx.x < R * M) {
@@ -183,8 +185,6 @@ hipError_t launch_m(const uint16_t *x, int64_t ldx, int K, const uint8_t *packed
 }
 
 }  // namespace
-
-bool w4a16_supports(int64_t K) { return K >= 64 && K <= 2048 * kMaxWaves; }
 
 int launch_w4a16_gemv(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t *packed,
                       int64_t ldw, const uint16_t *scales, const uint16_t *zeros, int N,

@@ -173,6 +173,8 @@ def test_awq_gemm_rejects():
             a[int(i[1:])] = v
         return f(*a)
     assert call(a7=None) == ck.CK_ERR_INVALID_ARG          # zeros
+    assert call(a6=P4 + 2) == ck.CK_ERR_INVALID_ARG        # scales 16-byte aligned
+    assert call(a7=P2 + 8) == ck.CK_ERR_INVALID_ARG        # zeros 16-byte aligned
     assert call(a8=32) == ck.CK_ERR_UNSUPPORTED             # Gw
     assert call(a9=40) == ck.CK_ERR_UNSUPPORTED             # N % 16
     assert call(a3=200) == ck.CK_ERR_INVALID_ARG            # ldx < K
@@ -232,7 +234,7 @@ def test_test_hooks_reject():
 
 def test_noalloc_linear_rejects_before_any_hip_call():
     """The allocation-free linear validates like ck_w4a4_linear and refuses sizes beyond
-    its 64 MiB static scratch with CK_ERR_UNSUPPORTED, all before any HIP call."""
+    its 64 MiB + 64 KiB static scratch with CK_ERR_UNSUPPORTED, all before any HIP call."""
     f = lib.ck_w4a4_linear_noalloc
 
     def call(M=4, K=256, ldx=256, G=64, N=16, scale_kind=0, x_scale=1.0, out=P4, ldo=16):
@@ -243,11 +245,11 @@ def test_noalloc_linear_rejects_before_any_hip_call():
     assert call(K=96, ldx=96) == ck.CK_ERR_INVALID_ARG
     assert call(x_scale=0.0) == ck.CK_ERR_INVALID_ARG
     assert call(out=P + 64) == ck.CK_ERR_INVALID_ARG          # output overlaps x
-    # packed codes of the tiled path: 8192 * 32768 / 2 = 128 MiB > 64 MiB
+    # packed codes of the tiled path: 8192 * 32768 / 2 = 128 MiB, beyond the scratch
     assert call(M=8192, K=32768, ldx=32768, N=16) == ck.CK_ERR_UNSUPPORTED
     assert b"static scratch" in lib.ck_last_error_msg()
-    # few-row path keeps one code per byte: 64 rows of 32768 fit, as do 8192 rows of 16384
-    # (those would launch, so they are not called here)
+    # 64 rows of 32768 fit, as do 8192 rows of 16384 (those would launch, so they are
+    # not called here; tests/sanitize/abi_driver.cpp runs them against stub launchers)
 
 
 def test_error_message_is_thread_local():
