@@ -178,9 +178,10 @@ ck_status ck_w4a4_gemm_packed(const uint8_t *codes4, int64_t ldq, const float *r
                         uint16_t *out, int64_t ldo, void *stream);
 
 /* Bytes of workspace ck_w4a8_linear / ck_w4a4_linear need for M rows of K
- * columns and N outputs: the int8 codes [M, K] plus the fp32 row scales, each
- * 256-byte aligned inside the workspace (no part depends on N, which is taken
- * so that a later matmul needing per-output scratch keeps this signature). */
+ * columns and N outputs: int8 codes for M rows rounded up to a multiple of 16
+ * (K bytes per row), then the fp32 row scales, each part 256-byte aligned
+ * inside the workspace.  No part depends on N, which is taken so that a later
+ * matmul needing per-output scratch keeps this signature.  0 for M <= 0. */
 size_t ck_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
@@ -225,8 +226,9 @@ ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, i
  *   - The scratch is a static device array of 64 MiB + 64 KiB (67174400 bytes), one
  *     copy on each GPU that loads the library, kept until the process ends.
  *     A call needing more returns CK_ERR_UNSUPPORTED before anything is
- *     enqueued: M * K / 2 bytes of packed codes (tiled path, M > 64) or M * K
- *     bytes (fewer rows), each rounded up to 256, plus 4 * M bytes of row
+ *     enqueued: M * K / 2 bytes of packed codes (tiled GEMM, M > 64),
+ *     ceil(M / 16) * 16 * K bytes (the few-row kernel's 16-row tiles) or M * K
+ *     bytes (the GEMV), each rounded up to 256, plus 4 * M bytes of row
  *     scales rounded up to 256; M = 1 uses no scratch.  For example M = 8192
  *     rows fit up to K = 16384, and M = 16384 rows up to K = 8192.
  *   - The call allocates nothing (no hipMalloc, no allocating library call).

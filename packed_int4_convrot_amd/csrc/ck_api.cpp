@@ -197,12 +197,15 @@ int check_out(const char *fn, const void *out, int64_t N, int64_t ldo, size_t es
 constexpr size_t kWsAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Whole-linear workspace: the int8 codes [M, K], then the fp32 row scales.
+// Whole-linear workspace: the int8 codes of M rows padded to a multiple of 16
+// (the tiled layout of the few-row kernel fills whole 16-row tiles), then the
+// fp32 row scales.
+size_t codes_bytes_padded(int64_t M, int64_t K) { return (size_t)((M + 15) / 16 * 16) * (size_t)K; }
 size_t workspace_bytes(int64_t M, int64_t K)
 {
     if (M <= 0 || K <= 0)
         return 0;
-    return round_up((size_t)(M * K), kWsAlign) + round_up((size_t)M * sizeof(float), kWsAlign);
+    return round_up(codes_bytes_padded(M, K), kWsAlign) + round_up((size_t)M * sizeof(float), kWsAlign);
 }
 
 // Dispatch of the integer matmul + epilogue by M.
@@ -230,20 +233,23 @@ int check_tiles(const char *fn, int64_t M, int64_t N)
 }
 
 // a4: the codes are W4A4 codes packed two per byte (ldq in bytes); only the
-// tiled GEMM takes them.
+// tiled GEMM takes them.  tiled: the codes are in the few-row kernel's operand
+// layout (CodesLayout::kTiled16); only that kernel takes them.
 int run_gemm(const char *fn, const void *codes, int64_t ldq, const float *rs, int64_t M, int64_t K,
              const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
-             int32_t *acc, int64_t lda, bool a4, void *stream)
+             int32_t *acc, int64_t lda, bool a4, void *stream, bool tiled = false)
 {
     const bool pg = w.kind == CK_WS_PER_GROUP;
     const GemmPath path = a4 ? GemmPath::kTiled : pick_path(M, K);
+    if (tiled && path != GemmPath::kSkinny)
+        return fail(CK_ERR_UNSUPPORTED, "%s: tiled codes reach only the few-row kernel", fn);
     const int8_t *c8 = static_cast<const int8_t *>(codes);
     int e;
     if (path == GemmPath::kGemv) {
         e = ck::launch_w4_gemv(nullptr, 0, 0, 0, c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw,
                                w.scales, pg, (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
     } else if (path == GemmPath::kSkinny) {
-        e = ck::launch_w4_skinny(c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
+        e = ck::launch_w4_skinny(c8, ldq, tiled, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
                                  (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
     } else {
         CK_TRY(check_tiles(fn, M, w.N));
@@ -285,12 +291,14 @@ int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, c
 // How the whole linear runs for M rows: one fused launch (decode), or rotate-quant
 // into scratch followed by the matmul kernel that pick_path() chooses.  W4A4
 // codes bound for the tiled GEMM are stored two per byte, which halves the
-// codes traffic on both sides of the scratch.
+// codes traffic on both sides of the scratch; codes bound for the few-row
+// kernel are stored in its operand layout (whole 16-row tiles).
 struct LinearPlan {
     bool fused;
     GemmPath path;
     bool a4;
-    int64_t ldq;          // bytes per row of codes in the scratch
+    bool tiled;           // codes in CodesLayout::kTiled16
+    int64_t ldq;          // bytes per row of row-major codes in the scratch
     size_t scales_off;    // offset of the fp32 row scales
     size_t used;          // scratch bytes the plan touches (0 when fused)
 };
@@ -301,8 +309,9 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t K)
     p.fused = ck::w4_gemv_fused_supports(M, K);
     p.path = pick_path(M, K);
     p.a4 = !p.fused && bits == 4 && p.path == GemmPath::kTiled;
+    p.tiled = !p.fused && p.path == GemmPath::kSkinny;
     p.ldq = p.a4 ? K / 2 : K;
-    p.scales_off = round_up((size_t)(M * p.ldq), kWsAlign);
+    p.scales_off = round_up(p.tiled ? codes_bytes_padded(M, K) : (size_t)(M * p.ldq), kWsAlign);
     p.used = p.fused ? 0 : p.scales_off + round_up((size_t)M * sizeof(float), kWsAlign);
     return p;
 }
@@ -371,11 +380,15 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
     }
     int8_t *codes = static_cast<int8_t *>(ws);
     float *rs = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + plan.scales_off);
+    const ck::CodesLayout layout = plan.a4      ? ck::CodesLayout::kPacked4
+                                   : plan.tiled ? ck::CodesLayout::kTiled16
+                                                : ck::CodesLayout::kRowMajor;
     const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, qmax, codes, plan.ldq, rs, nullptr, 0,
-                                          plan.a4, stream);
+                                          layout, stream);
     if (e != 0)
         return hip_status(e, fn);
-    return run_gemm(fn, codes, plan.ldq, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, plan.a4, stream);
+    return run_gemm(fn, codes, plan.ldq, rs, M, K, w, bias, x_scale, out, ldo, nullptr, 0, plan.a4, stream,
+                    plan.tiled);
 }
 
 }  // namespace
@@ -414,7 +427,7 @@ int ck_rotate_quant_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, i
         overlap(span(codes, M, K, ldq, 1), span(row_scales, 1, M, M, 4)))
         return fail(CK_ERR_INVALID_ARG, "%s: codes, row_scales and x must not overlap", fn);
     const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, bits == 8 ? 127 : 7, codes, ldq,
-                                          row_scales, nullptr, 0, false, stream);
+                                          row_scales, nullptr, 0, ck::CodesLayout::kRowMajor, stream);
     return hip_status(e, fn);
 }
 
@@ -464,7 +477,7 @@ int ck_test_rotate_f32_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
     if (overlap(span(x, M, K, ldx, 2), span(xr, M, K, ldr, 4)))
         return fail(CK_ERR_INVALID_ARG, "%s: xr overlaps x", fn);
     const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, 127, nullptr, 0, nullptr, xr, ldr,
-                                          false, stream);
+                                          ck::CodesLayout::kRowMajor, stream);
     return hip_status(e, fn);
 }
 
@@ -486,7 +499,7 @@ int ck_rotate_quant_packed4_impl(const uint16_t *x, int64_t M, int64_t K, int64_
     if (overlap(rx, rc) || overlap(rx, rr) || overlap(rc, rr))
         return fail(CK_ERR_INVALID_ARG, "%s: codes4, row_scales and x must not overlap", fn);
     const int e = ck::launch_rotate_quant(x, M, (int)K, ldx, G, 7, reinterpret_cast<int8_t *>(codes4),
-                                          ldq, row_scales, nullptr, 0, true, stream);
+                                          ldq, row_scales, nullptr, 0, ck::CodesLayout::kPacked4, stream);
     return hip_status(e, fn);
 }
 

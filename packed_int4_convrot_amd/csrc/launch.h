@@ -8,9 +8,22 @@
 
 namespace ck {
 
+// Layouts of the activation codes written by rotate-quant.
+//   kRowMajor: int8 [M, ldq], one code per byte.
+//   kPacked4:  W4A4 codes two per byte (4-bit two's complement, column 2j in
+//              the low nibble), [M, ldq] bytes.
+//   kTiled16:  int8 codes in the operand order of the few-row MFMA kernel:
+//              rows in tiles of 16, each tile K/64 blocks of 1 KiB (one per
+//              64-column group g); inside a block, the 16 bytes at
+//              16 * (16 * kb + r) hold row r of the tile, columns
+//              64 g + 16 kb .. + 15 in the order [0,2,4,6, 1,3,5,7, 8,10,12,14,
+//              9,11,13,15] (the order of the nibble decode).  Tile t starts at
+//              byte 16 * K * t; rows past M in the last tile are not written.
+enum class CodesLayout { kRowMajor, kPacked4, kTiled16 };
+
 int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
-                        bool packed4, void *stream);
+                        CodesLayout layout, void *stream);
 
 // AWQ W4A16 prefill GEMM: out = x . W^T (+ bias), W rebuilt in bf16 as the
 // page's dequantize() does; Gw = 64 scales and zero points [K/64, N].
@@ -45,8 +58,9 @@ inline bool w4_gemv_fused_supports(int64_t M, int64_t K) { return w4_gemv_suppor
 
 // Skinny path: M <= 64, weights streamed once, activations held in registers.
 // acc_out != nullptr selects the int32 test epilogue.
-int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
-                     const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+// codes: row-major int8 [M, ldq], or (tiled, ldq ignored) the kTiled16 layout.
+int launch_w4_skinny(const int8_t *codes, int64_t ldq, bool tiled, const float *row_scales, int M,
+                     int K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                      bool per_group, int N, const uint16_t *bias, float x_scale,
                      uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
 // Shape of the few-row kernel: MT = ceil(M / 16) m-tiles; GPW groups per wave,

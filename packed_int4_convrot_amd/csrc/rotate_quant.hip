@@ -127,7 +127,9 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 // column 2j in bits 0..3), which halves the codes traffic of the W4A4 GEMM,
 // or packed weights (stored code q = value + 8) with bf16 scales per row or
 // per 64-column group.
-enum OutMode { kCodes8 = 0, kF32 = 1, kPacked4 = 2, kWeightRow = 3, kWeightGroup = 4 };
+// kTiled16 writes int8 codes in the few-row kernel's operand layout
+// (CodesLayout::kTiled16 in launch.h).
+enum OutMode { kCodes8 = 0, kF32 = 1, kPacked4 = 2, kWeightRow = 3, kWeightGroup = 4, kTiled16 = 5 };
 
 // Weight quantisation of rotated values y = sqrt(G) * wr (see the launcher):
 // scale s = bf16(fp32(a / 7)) for the absmax a of wr over the scale group,
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
 {
     constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
     static_assert(G == 16 || G == 64 || G == 256, "G");
-    static_assert(CW == 8 || (CW == 16 && (MODE == kCodes8 || MODE == kPacked4 || MODE == kF32)),
+    static_assert(CW == 8 || (CW == 16 && (MODE == kCodes8 || MODE == kPacked4 || MODE == kF32 ||
+                                           MODE == kTiled16)),
                   "chunk width");
     __shared__ float wmax[BLOCK / kWave];
 
@@ -252,6 +255,32 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
                                        v[i][4 * q + 2] * kInvSqrtG, v[i][4 * q + 3] * kInvSqrtG);
             }
         }
+    } else if constexpr (MODE == kTiled16) {
+        // Each 8 columns become 8 bytes of a 16-byte operand chunk: the even
+        // columns, then the odd ones.  Row m is row m % 16 of tile m / 16.
+        const float inv = am > 0.f ? qmax / am : 0.f;
+        int8_t *trow = codes + (m >> 4) * (int64_t)K * 16 + (m & 15) * 16;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = t + i * BLOCK;
+            uint32_t b[CW];
+#pragma unroll
+            for (int r = 0; r < CW; ++r)
+                b[r] = rne_byte(v[i][r] * inv);
+            if (FULL || c < nchunk) {
+#pragma unroll
+                for (int q = 0; q < CW / 8; ++q) {
+                    const uint32_t *bq = b + 8 * q;
+                    const int c8 = (CW / 8) * c + q;  // 8-column unit of the row
+                    const int c16 = c8 >> 1;          // 16-column chunk: group c16 / 4, kb = c16 % 4
+                    int8_t *dst = trow + (c16 >> 2) * 1024 + (c16 & 3) * 256 + 8 * (c8 & 1);
+                    *reinterpret_cast<uint2 *>(dst) =
+                        uint2{pack4(bq[0], bq[2], bq[4], bq[6]), pack4(bq[1], bq[3], bq[5], bq[7])};
+                }
+            }
+        }
+        if (t == 0)
+            row_scales[m] = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;
     } else {
         // am == 0 (all-zero row): inv = 0 makes every code 0; the scale is 1.
         const float inv = am > 0.f ? qmax / am : 0.f;
@@ -340,7 +369,7 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
                      uint16_t *wsc = nullptr, int64_t ldsc = 0)
 {
     const dim3 grid((unsigned)M);
-    if constexpr ((MODE == kCodes8 || MODE == kPacked4 || MODE == kF32) && G >= 64) {
+    if constexpr ((MODE == kCodes8 || MODE == kPacked4 || MODE == kF32 || MODE == kTiled16) && G >= 64) {
         // Activation codes from G = 64 on: 16-column chunks (K is a multiple
         // of G).  The fp32 test output takes the same instantiation, so the
         // rotation it exposes is the one the activation codes are made from.  Up to 10240 columns 128 threads of up to 5 chunks, then 256,
@@ -382,13 +411,16 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
 
 int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax,
                         int8_t *codes, int64_t ldq, float *row_scales, float *xr, int64_t ldr,
-                        bool packed4, void *stream)
+                        CodesLayout layout, void *stream)
 {
     if (M <= 0)
         return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const float q = (float)qmax;
-    const int mode = xr ? kF32 : packed4 ? kPacked4 : kCodes8;
+    const int mode = xr ? kF32
+                        : layout == CodesLayout::kPacked4 ? kPacked4
+                        : layout == CodesLayout::kTiled16 ? kTiled16
+                                                          : kCodes8;
 #define CK_RQ_G(MODE)                                                                                  \
     switch (G) {                                                                                     \
     case 16: return (int)launch_rq<16, MODE>(M, K, s, x, ldx, q, codes, ldq, row_scales, xr, ldr);   \
@@ -399,6 +431,8 @@ int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G,
         CK_RQ_G(kF32)
     } else if (mode == kPacked4) {
         CK_RQ_G(kPacked4)
+    } else if (mode == kTiled16) {
+        CK_RQ_G(kTiled16)
     } else {
         CK_RQ_G(kCodes8)
     }

@@ -20,13 +20,20 @@
 //   * a workgroup computes 16 output columns (weight rows n0 .. n0 + 15) for
 //     all M activation rows; it has KS waves, and wave w owns a contiguous
 //     range of GPW K-groups;
-//   * each wave first loads the activation operands of its groups into VGPRs
-//     (permuted once), then streams its slice of the 16 weight rows
-//     (GPW * 32 bytes per row) into its own LDS region with
-//     global_load_lds_dwordx4: every 1 KiB instruction covers whole 16-byte
-//     chunks of at most 8 rows, at least 128 contiguous bytes of each, which
-//     HBM serves at full rate (8-byte fragment loads straight from global
-//     memory would touch 16 rows x 32 bytes per instruction);
+//   * each wave loads the activation operands of its groups into VGPRs and
+//     streams its slice of the 16 weight rows (GPW * 32 bytes per row) into
+//     its own LDS region with global_load_lds_dwordx4: every 1 KiB
+//     instruction covers whole 16-byte chunks of at most 8 rows, at least 128
+//     contiguous bytes of each, which HBM serves at full rate (8-byte fragment
+//     loads straight from global memory would touch 16 rows x 32 bytes per
+//     instruction);
+//   * activation codes come either row-major (permuted in registers) or, from
+//     the whole linear's own rotate-quant, in the tiled operand layout
+//     (CodesLayout::kTiled16), where each operand is one contiguous 1 KiB
+//     block: row-major operand loads touch 16 rows x 64 bytes per instruction,
+//     which the memory pipeline serves as 64 separate requests, and every
+//     workgroup reads all the codes (measured on MI355X at M = 32, N = 3840:
+//     7.3 us per launch row-major, 5.4 us tiled);
 //   * chunk slots inside an LDS row are XOR-swizzled by row, so the 8-byte
 //     fragment reads of 16 rows hit 16 different bank groups; a wave reads
 //     only its own region, so its own vmcnt wait is the only synchronisation;
@@ -45,7 +52,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // s_waitcnt vmcnt(0), other counters untouched.
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int MT, int GPW, bool PER_GROUP, bool OUT_I32>
+template <int MT, int GPW, bool PER_GROUP, bool OUT_I32, bool TILED>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int M,
     int K, const uint8_t *__restrict__ packed, int64_t ldw, const uint16_t *__restrict__ w_scales,
@@ -75,48 +82,91 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     lds_u8 *slice = smem + wave * SLICE;
     int *red_smem = reinterpret_cast<int *>(smem_generic + ks * SLICE);  // [KS][MT][64][4]
 
-    // 1. Loads, in this order: the activations of this wave's groups (clamped
-    //    addresses; out-of-range values are replaced by zero below), the
-    //    weight scales, then the weight slice into LDS.
+    // 1. Loads.  Row-major codes: the activations of this wave's groups first
+    //    (clamped addresses; out-of-range values are replaced by zero below),
+    //    then the weight scales, then the weight slice into LDS.  Tiled codes
+    //    (each 1 KiB block is one operand, so the loads are whole lines): the
+    //    weight slice first, as it comes from HBM, then scales and codes.
     u32x4 raw[GPW][MT];
+    uint16_t sw[GPW];
+    auto load_weights = [&]() {
 #pragma unroll
-    for (int j = 0; j < GPW; ++j)
+        for (int j = 0; j < NLD; ++j) {
+            const int s = 64 * j + lane;  // slot in the slice
+            const int r = s / CPR;
+            const int c = (s % CPR) ^ (r >> SH);  // chunk of row r stored in that slot
+            if (c < 2 * cnt)
+                __builtin_amdgcn_global_load_lds(packed + (int64_t)(n0 + r) * ldw + 32 * g0 + 16 * c,
+                                                 slice + 1024 * j, 16, 0, 0);
+        }
+    };
+    auto load_scales = [&]() {
+        if constexpr (PER_GROUP) {
+#pragma unroll
+            for (int j = 0; j < GPW; ++j)
+                sw[j] = w_scales[(int64_t)min(g0 + j, ng - 1) * N + n0 + col];
+        }
+    };
+    if constexpr (TILED) {
+        load_weights();
+        load_scales();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int m = min(mt * 16 + col, M - 1);
-            const int g = min(g0 + j, ng - 1);
-            raw[j][mt] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + 64 * g + 16 * kb);
+            const int8_t *tile = codes + (int64_t)mt * K * 16 + 16 * lane;
+            if (M >= 16 * (mt + 1)) {
+#pragma unroll
+                for (int j = 0; j < GPW; ++j)
+                    raw[j][mt] = *reinterpret_cast<const u32x4 *>(tile + min(g0 + j, ng - 1) * 1024);
+            } else {
+                // Partial last tile: rows past M were never written; skip them.
+#pragma unroll
+                for (int j = 0; j < GPW; ++j) {
+                    raw[j][mt] = u32x4{0u, 0u, 0u, 0u};
+                    if (mt * 16 + col < M)
+                        raw[j][mt] = *reinterpret_cast<const u32x4 *>(tile + min(g0 + j, ng - 1) * 1024);
+                }
+            }
         }
-    uint16_t sw[GPW];
-    if constexpr (PER_GROUP) {
+    } else {
 #pragma unroll
         for (int j = 0; j < GPW; ++j)
-            sw[j] = w_scales[(int64_t)min(g0 + j, ng - 1) * N + n0 + col];
-    }
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-        const int s = 64 * j + lane;  // slot in the slice
-        const int r = s / CPR;
-        const int c = (s % CPR) ^ (r >> SH);  // chunk of row r stored in that slot
-        if (c < 2 * cnt)
-            __builtin_amdgcn_global_load_lds(packed + (int64_t)(n0 + r) * ldw + 32 * g0 + 16 * c,
-                                             slice + 1024 * j, 16, 0, 0);
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = min(mt * 16 + col, M - 1);
+                const int g = min(g0 + j, ng - 1);
+                raw[j][mt] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + 64 * g + 16 * kb);
+            }
+        load_scales();
+        load_weights();
     }
 
-    // 2. Activation operands, permuted to the decode order (overlaps the DMA).
+    // 2. Activation operands in the decode order (tiled codes already are),
+    //    zero for rows past M and groups past K.
     v4i a[GPW][MT];
 #pragma unroll
     for (int j = 0; j < GPW; ++j)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const bool live = j < cnt && mt * 16 + col < M;
-            const v4i p = act_perm16(raw[j][mt][0], raw[j][mt][1], raw[j][mt][2], raw[j][mt][3]);
+            const v4i p = TILED ? v4i{(int)raw[j][mt][0], (int)raw[j][mt][1], (int)raw[j][mt][2],
+                                      (int)raw[j][mt][3]}
+                                : act_perm16(raw[j][mt][0], raw[j][mt][1], raw[j][mt][2], raw[j][mt][3]);
             a[j][mt] = live ? p : v4i{0, 0, 0, 0};
         }
 
-    // 3. This wave's slice has landed once its own loads have retired.
+    // 3. This wave's slice has landed once its own loads have retired.  Every
+    //    group runs, without a branch, so that the LDS reads issue together:
+    //    past K the slice holds stale bytes, multiplied by zero activations.
     wait_vmcnt0();
 
+    u32x2 wq[GPW];
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        // Lane (col, kb) holds k = 64 g + 16 kb .. + 15: bytes 32 j + 8 kb of row col.
+        const int c = 2 * j + (kb >> 1);
+        wq[j] = *(const __attribute__((address_space(3))) u32x2 *)(slice + col * P + 16 * (c ^ (col >> SH)) +
+                                                                    8 * (kb & 1));
+    }
     float y[MT][4];
     v4i acc[MT];
 #pragma unroll
@@ -127,28 +177,23 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
             y[mt][i] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < GPW; ++j)
-        if (j < cnt) {
-            // Lane (col, kb) holds k = 64 g + 16 kb .. + 15: bytes 32 j + 8 kb of row col.
-            const int c = 2 * j + (kb >> 1);
-            const u32x2 wq = *(const __attribute__((address_space(3))) u32x2 *)(
-                slice + col * P + 16 * (c ^ (col >> SH)) + 8 * (kb & 1));
-            const v4i b = w4_operand_x16(wq[0], wq[1]);
-            if constexpr (PER_GROUP) {
-                const float sc = bf16_to_f32(sw[j]);
+    for (int j = 0; j < GPW; ++j) {
+        const v4i b = w4_operand_x16(wq[j][0], wq[j][1]);
+        if constexpr (PER_GROUP) {
+            const float sc = bf16_to_f32(sw[j]);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, v4i{0, 0, 0, 0}, 0, 0, 0);
+            for (int mt = 0; mt < MT; ++mt) {
+                const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        y[mt][i] = __builtin_fmaf(sc, (float)d[i], y[mt][i]);
-                }
-            } else {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, acc[mt], 0, 0, 0);
+                for (int i = 0; i < 4; ++i)
+                    y[mt][i] = __builtin_fmaf(sc, (float)d[i], y[mt][i]);
             }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, acc[mt], 0, 0, 0);
         }
+    }
 
     // 4. Cross-wave reduction: red[w][mt][lane][i], summed in wave order.
 #pragma unroll
@@ -194,7 +239,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     }
 }
 
-template <int MT, int GPW, bool PG, bool I32>
+template <int MT, int GPW, bool PG, bool I32, bool TL>
 hipError_t launch_t(const SkinnyShape &sh, const int8_t *codes, int64_t ldq, const float *rs, int M,
                     int K, const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N,
                     const uint16_t *bias, float xs, uint16_t *out, int64_t ldo, int32_t *acc,
@@ -202,7 +247,7 @@ hipError_t launch_t(const SkinnyShape &sh, const int8_t *codes, int64_t ldq, con
 {
     const int ntiles = N / 16;
     const size_t smem = (size_t)sh.ks * (16 * 32 * GPW + MT * kWave * 4 * sizeof(int));
-    auto kern = w4_skinny_kernel<MT, GPW, PG, I32>;
+    auto kern = w4_skinny_kernel<MT, GPW, PG, I32, TL>;
     constexpr size_t smem_max = (size_t)kMaxWaves * (16 * 32 * GPW + MT * kWave * 4 * sizeof(int));
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_max);
@@ -214,26 +259,36 @@ hipError_t launch_t(const SkinnyShape &sh, const int8_t *codes, int64_t ldq, con
     return hipGetLastError();
 }
 
+// The int32 test epilogue reads row-major codes only; tiled codes come from
+// the linear's own rotate-quant.
 template <int MT, int GPW>
-hipError_t launch_mt(const SkinnyShape &sh, bool pg, bool i32, const int8_t *codes, int64_t ldq,
-                     const float *rs, int M, int K, const uint8_t *packed, int64_t ldw,
+hipError_t launch_mt(const SkinnyShape &sh, bool pg, bool i32, bool tiled, const int8_t *codes,
+                     int64_t ldq, const float *rs, int M, int K, const uint8_t *packed, int64_t ldw,
                      const uint16_t *ws, int N, const uint16_t *bias, float xs, uint16_t *out,
                      int64_t ldo, int32_t *acc, int64_t lda, hipStream_t s)
 {
     if (i32)
-        return launch_t<MT, GPW, false, true>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias,
-                                              xs, out, ldo, acc, lda, s);
+        return tiled ? hipErrorInvalidValue
+                     : launch_t<MT, GPW, false, true, false>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N,
+                                                             bias, xs, out, ldo, acc, lda, s);
+    if (tiled) {
+        if (pg)
+            return launch_t<MT, GPW, true, false, true>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias,
+                                                        xs, out, ldo, acc, lda, s);
+        return launch_t<MT, GPW, false, false, true>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias,
+                                                     xs, out, ldo, acc, lda, s);
+    }
     if (pg)
-        return launch_t<MT, GPW, true, false>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias,
-                                              xs, out, ldo, acc, lda, s);
-    return launch_t<MT, GPW, false, false>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias, xs,
-                                           out, ldo, acc, lda, s);
+        return launch_t<MT, GPW, true, false, false>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias,
+                                                     xs, out, ldo, acc, lda, s);
+    return launch_t<MT, GPW, false, false, false>(sh, codes, ldq, rs, M, K, packed, ldw, ws, N, bias, xs,
+                                                  out, ldo, acc, lda, s);
 }
 
 }  // namespace
 
-int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
-                     const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,
+int launch_w4_skinny(const int8_t *codes, int64_t ldq, bool tiled, const float *row_scales, int M,
+                     int K, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,
                      int N, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
                      int32_t *acc_out, int64_t lda, void *stream)
 {
@@ -245,19 +300,19 @@ int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, 
     hipError_t e;
     switch (sh.mt * 100 + sh.gpw) {
     case 116:
-        e = launch_mt<1, 16>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
+        e = launch_mt<1, 16>(sh, per_group, i32, tiled, codes, ldq, row_scales, M, K, packed, ldw,
                              w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
         break;
     case 208:
-        e = launch_mt<2, 8>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
+        e = launch_mt<2, 8>(sh, per_group, i32, tiled, codes, ldq, row_scales, M, K, packed, ldw,
                             w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
         break;
     case 216:
-        e = launch_mt<2, 16>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
+        e = launch_mt<2, 16>(sh, per_group, i32, tiled, codes, ldq, row_scales, M, K, packed, ldw,
                              w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
         break;
     case 408:
-        e = launch_mt<4, 8>(sh, per_group, i32, codes, ldq, row_scales, M, K, packed, ldw,
+        e = launch_mt<4, 8>(sh, per_group, i32, tiled, codes, ldq, row_scales, M, K, packed, ldw,
                             w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s);
         break;
     default:

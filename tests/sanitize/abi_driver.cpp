@@ -104,8 +104,8 @@ void test_workspace_bytes()
 {
     EXPECT(ck_linear_workspace_bytes(0, 3840, 16) == 0);
     EXPECT(ck_linear_workspace_bytes(-3, 3840, 16) == 0);
-    EXPECT(ck_linear_workspace_bytes(1, 64, 16) == 512);
-    EXPECT(ck_linear_workspace_bytes(300, 3840, 16) == 1152000 + 1280);
+    EXPECT(ck_linear_workspace_bytes(1, 64, 16) == 1024 + 256);         // codes padded to 16 rows
+    EXPECT(ck_linear_workspace_bytes(300, 3840, 16) == 304 * 3840 + 1280);
     EXPECT(ck_linear_workspace_bytes(8192, 3840, 3840) == (size_t)8192 * 3840 + 32768);
 }
 
@@ -376,7 +376,9 @@ void test_linear()
                 continue;
             const stub::Call &rq = stub::log[0], &g = stub::log[1];
             const bool a4 = bits == 4 && mm == stub::Kernel::kGemm;
+            const bool tiled = mm == stub::Kernel::kSkinny;
             EXPECT(rq.kernel == stub::Kernel::kRotateQuant && rq.G == c.G && rq.packed4 == a4);
+            EXPECT(rq.tiled == tiled && g.tiled == tiled);
             EXPECT(rq.qmax == (bits == 8 ? 127 : 7) && rq.ldq == (a4 ? c.K / 2 : c.K));
             EXPECT(rq.codes == ws && contains(ws, need, rq.row_scales));
             EXPECT(reinterpret_cast<uintptr_t>(rq.row_scales) % 256 == 0);
@@ -433,9 +435,10 @@ void test_noalloc()
         int64_t M, K;
         bool fits;
     };
-    const Case cases[] = {{1, 3840, true},      {4, 3840, true},      {64, 32768, true},
-                          {300, 3840, true},    {8192, 3840, true},   {8192, 16384, true},
-                          {16384, 8192, true},  {8192, 16448, false}, {16448, 8192, false}};
+    const Case cases[] = {{1, 3840, true},      {4, 3840, true},      {17, 3840, true},
+                          {32, 3840, true},     {64, 32768, true},    {300, 3840, true},
+                          {8192, 3840, true},   {8192, 16384, true},  {16384, 8192, true},
+                          {8192, 16448, false}, {16448, 8192, false}};
     for (const Case &c : cases) {
         Pool pool;
         const int64_t N = 16, ldx = c.K, ldo = N;
@@ -463,6 +466,7 @@ void test_noalloc()
         EXPECT(rq.codes == base && contains(base, ck::kStaticScratchBytes, rq.row_scales));
         const bool tiled = expected_kernel(c.M, c.K) == stub::Kernel::kGemm;
         EXPECT(rq.packed4 == tiled && g.a4 == tiled && g.codes == rq.codes && g.kernel == expected_kernel(c.M, c.K));
+        EXPECT(rq.tiled == (g.kernel == stub::Kernel::kSkinny) && g.tiled == rq.tiled);
     }
 }
 

@@ -96,16 +96,27 @@ std::vector<uint8_t> g_scratch;
 namespace ck {
 
 int launch_rotate_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, int G, int qmax, int8_t *codes,
-                        int64_t ldq, float *row_scales, float *xr, int64_t ldr, bool packed4, void *stream)
+                        int64_t ldq, float *row_scales, float *xr, int64_t ldr, CodesLayout layout, void *stream)
 {
     using namespace stub;
+    const bool packed4 = layout == CodesLayout::kPacked4, tiled = layout == CodesLayout::kTiled16;
     read_rows(x, M, 2 * (int64_t)K, 2 * ldx);
-    write_rows(codes, M, packed4 ? K / 2 : K, ldq);
+    if (tiled && codes) {
+        // Row m: 16 bytes at 16 * (m % 16) of every 256-byte kb slot of its
+        // tile's K / 64 blocks; first and last of them.
+        for (int64_t m = 0; m < M; ++m) {
+            int8_t *t = codes + (m / 16) * (int64_t)K * 16 + (m % 16) * 16;
+            t[0] = 1;
+            t[(K / 64 - 1) * 1024 + 3 * 256 + 15] = 1;
+        }
+    } else {
+        write_rows(codes, M, packed4 ? K / 2 : K, ldq);
+    }
     write_rows(row_scales, 1, 4 * M, 4 * M);
     write_rows(xr, M, 4 * (int64_t)K, 4 * ldr);
     Call c{};
     c.kernel = Kernel::kRotateQuant;
-    c.M = M, c.K = K, c.G = G, c.qmax = qmax, c.ldq = ldq, c.packed4 = packed4;
+    c.M = M, c.K = K, c.G = G, c.qmax = qmax, c.ldq = ldq, c.packed4 = packed4, c.tiled = tiled;
     c.x = x, c.codes = codes, c.row_scales = row_scales, c.xr = xr, c.stream = stream;
     return finish(c);
 }
@@ -162,17 +173,29 @@ int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t
     return finish(c);
 }
 
-int launch_w4_skinny(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
+int launch_w4_skinny(const int8_t *codes, int64_t ldq, bool tiled, const float *row_scales, int M, int K,
                      const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group, int N,
                      const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo, int32_t *acc_out,
                      int64_t lda, void *stream)
 {
     using namespace stub;
-    touch_matmul(codes, ldq, row_scales, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo, acc_out,
-                 lda, false);
+    if (tiled) {
+        // Whole 16-row tiles are read; in a partial last tile only the rows below M.
+        for (int t = 0; t * 16 < M; ++t) {
+            const int8_t *base = codes + (int64_t)t * K * 16;
+            const int live = M - 16 * t < 16 ? M - 16 * t : 16;
+            g_sink = base[0];
+            g_sink = live == 16 ? base[(int64_t)K * 16 - 1] : base[(K / 64 - 1) * 1024 + 3 * 256 + (live - 1) * 16 + 15];
+        }
+        touch_matmul(nullptr, 0, row_scales, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo, acc_out,
+                     lda, false);
+    } else {
+        touch_matmul(codes, ldq, row_scales, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo,
+                     acc_out, lda, false);
+    }
     Call c{};
     c.kernel = Kernel::kSkinny;
-    c.M = M, c.K = K, c.N = N, c.ldq = ldq, c.per_group = per_group, c.x_scale = x_scale;
+    c.M = M, c.K = K, c.N = N, c.ldq = ldq, c.tiled = tiled, c.per_group = per_group, c.x_scale = x_scale;
     c.codes = codes, c.row_scales = row_scales, c.out = out, c.acc = acc_out, c.stream = stream;
     return finish(c);
 }

@@ -16,7 +16,7 @@ struct Call {
     int64_t M = 0, K = 0, N = 0;
     int G = 0, qmax = 0;
     int64_t ldq = 0;
-    bool packed4 = false, a4 = false, per_group = false;
+    bool packed4 = false, tiled = false, a4 = false, per_group = false;
     float x_scale = 0.f;
     const void *x = nullptr, *codes = nullptr, *row_scales = nullptr, *xr = nullptr;
     const void *out = nullptr, *acc = nullptr, *stream = nullptr;

@@ -357,6 +357,33 @@ def test_fused_decode_linear_equals_two_step_path(M, K, G):
         assert torch.equal(fused, two)
 
 
+@pytest.mark.parametrize("G", [16, 64, 256])
+@pytest.mark.parametrize("M,K", [(6, 3840), (8, 3840), (13, 1024), (16, 3840), (17, 3840), (24, 2048),
+                                 (32, 3840), (33, 3840), (48, 1024), (64, 3840)])
+def test_linear_tiled_codes_equal_row_major_path(M, K, G):
+    """From 6 to 64 rows the whole linear stores its codes in the few-row kernel's
+    tiled operand layout.  Its outputs are bit-identical to ck_rotate_quant
+    (row-major codes) followed by ck_w4_gemm_q, which runs the same kernel on
+    row-major codes: both bit widths and scale kinds, full and partial last tiles,
+    a zero row, and the input scale."""
+    N = 272
+    for bits in (8, 4):
+        for per_group in (True, False):
+            inp = workloads.linear_inputs(M, K, N, seed=G + M + bits, outliers=8,
+                                          scale="group" if per_group else "channel", zero_rows=(1,),
+                                          with_bias=True)
+            xd, wd = bf16_dev(inp["x"]), u8_dev(inp["packed"])
+            sd, bd = bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+            lin = ck.linear(xd, G, bits, wd, sd, per_group, bias=bd)
+            codes, scales = ck.rotate_quant(xd, G, bits)
+            two = ck.gemm_q(codes, scales, wd, sd, per_group, bias=bd)
+            assert torch.equal(lin, two), (bits, per_group)
+            # the input scale multiplies the row scales on both paths
+            lin3 = ck.linear(xd, G, bits, wd, sd, per_group, bias=bd, x_scale=3.0)
+            two3 = ck.gemm_q(codes, scales * 3.0, wd, sd, per_group, bias=bd)
+            assert torch.equal(lin3, two3), (bits, per_group)
+
+
 def test_fused_decode_linear_strided_input_ignores_padding():
     """Row stride > K: the fused kernel reads only the K columns (the padding is NaN)."""
     K, N, ld = 3840, 512, 4096
