@@ -38,7 +38,7 @@ int launch_quantize_weights(const uint16_t *w, int64_t N, int K, int64_t ldw_in,
                             uint8_t *packed, int64_t ldp, uint16_t *scales, void *stream);
 
 // Decode GEMV for 1 <= M <= 8 (VALU dot4, 1 KiB coalesced weight rows).  With
-// G != 0 (M = 1) it rotates and quantises the bf16 row x itself (fused linear); with
+// G != 0 (M <= 2) it rotates and quantises the bf16 rows x itself (fused linear); with
 // G == 0 it reads given codes and row_scales.  acc_out != nullptr (G == 0
 // only) selects the int32 test epilogue.
 int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
@@ -46,10 +46,10 @@ int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t
                    const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias, float x_scale,
                    uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
 // The decode GEMV: 1 <= M <= 8 activation rows, one wave per 2048 columns of K,
-// at most 8 waves; the fused rotate-quant form takes a single row.
+// at most 8 waves; the fused rotate-quant form takes one or two rows.
 constexpr int kGemvMaxWaves = 8;
 constexpr int kGemvMaxM = 8;
-constexpr int kGemvMaxFusedRows = 1;
+constexpr int kGemvMaxFusedRows = 2;
 inline bool w4_gemv_supports(int64_t M, int64_t K)
 {
     return M >= 1 && M <= kGemvMaxM && K <= 2048 * kGemvMaxWaves;

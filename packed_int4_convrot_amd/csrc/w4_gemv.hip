@@ -1,5 +1,5 @@
-// Decode GEMV for 1 <= M <= 8 activation rows, optionally (M = 1) fused with
-// the rotate-quant of that row.
+// Decode GEMV for 1 <= M <= 8 activation rows, optionally (M <= 2) fused with
+// the rotate-quant of those rows.
 //
 // Prior art: the W4A8 decode GEMV of "[PR #182] HIP port of #176: W4A8 decode
 // GEMV and fused GatedDeltaNet decode" (description): register-side int4
@@ -38,8 +38,12 @@ constexpr int kMaxWaves = kGemvMaxWaves;  // K <= 16384
 #ifndef CK_GEMV_ROWS
 #define CK_GEMV_ROWS 8  // weight rows per block (8, 16 or 32)
 #endif
-// The fused form pays the rotation once per block; measured on MI355X it is
-// faster than a separate rotate-quant launch only for a single activation row.
+// The fused form pays the rotation of every row once per block.  Measured on
+// MI355X (K = 3840, N = 10240, per-group scales, graph replay, cold weights),
+// fused against rotate-quant + GEMV on codes: M = 1 6.84 / 9.44 us, M = 2
+// 9.16 / 10.35, M = 3 12.40 / 11.04, M = 4 16.02 / 11.78, M = 5 19.12 / 12.45:
+// each further row adds about 3.1 us of rotation across the 1280 blocks, so
+// the fused form stops at two rows.
 constexpr int kMaxFusedRows = kGemvMaxFusedRows;
 
 // One cross-lane butterfly stage on 32 values per lane (fused rotation).

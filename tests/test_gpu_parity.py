@@ -340,12 +340,13 @@ def test_linear_end_to_end(M, G, per_group, bits):
         assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
 
 
-@pytest.mark.parametrize("M,K", [(1, 3840), (2, 3840), (1, 256), (1, 2304), (1, 8192)])
+@pytest.mark.parametrize("M,K", [(1, 3840), (2, 3840), (1, 256), (2, 256), (1, 2304), (2, 2304), (1, 8192),
+                                 (2, 16384)])
 @pytest.mark.parametrize("G", [16, 64, 256])
 def test_fused_decode_linear_equals_two_step_path(M, K, G):
-    """The one-launch decode linear (rotate-quant inside the GEMV) gives bit-identical
-    outputs to ck_rotate_quant followed by ck_w4_gemv: one wave with 8 active lanes,
-    a partial second wave, and four waves."""
+    """The one-launch decode linear (rotate-quant inside the GEMV, one or two rows)
+    gives bit-identical outputs to ck_rotate_quant followed by ck_w4_gemv: one wave
+    with 8 active lanes, a partial second wave, four and eight waves."""
     N = 1024
     for per_group in (True, False):
         inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=8, scale="group" if per_group else "channel",
