@@ -164,6 +164,11 @@ PROFILE_WORKLOADS = {
     "awq_w4a16_gemv_m1_k3072_n18432": dict(
         kernel="w4a16_gemv_kernel", M=1, K=3072, N=18432, mops=None,
         alg_bytes=18432 * 3072 // 2 + 2 * 2 * 48 * 18432 + 3072 * 2 + 18432 * 2),
+    # The matmul half of the M = 32 W4A8 linear: packed weights, group scales, the
+    # tiled codes and row scales, the bf16 output.
+    "w4a8_skinny_m32_k3840_n3840_g64": dict(
+        kernel="w4_skinny_kernel", M=32, K=3840, N=3840, mops=None,
+        alg_bytes=3840 * 3840 // 2 + 60 * 3840 * 2 + 32 * 3840 + 32 * 4 + 32 * 3840 * 2),
 }
 KERNEL_SOURCES = {
     "w4_gemm_kernel": ["packed_int4_convrot_amd/csrc/w4_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
@@ -172,6 +177,7 @@ KERNEL_SOURCES = {
                             "packed_int4_convrot_amd/csrc/ck_device.h"],
     "w4a16_gemv_kernel": ["packed_int4_convrot_amd/csrc/w4a16_gemv.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
                           "packed_int4_convrot_amd/csrc/ck_device.h"],
+    "w4_skinny_kernel": ["packed_int4_convrot_amd/csrc/w4_skinny.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
 }
 
 
@@ -206,6 +212,18 @@ def profile_workload(name, reps=5):
 
         def fn():
             ck.gemm_packed4(codes4, rs, packed, scl, False, out=out)
+    elif name.startswith("w4a8_skinny"):
+        wl = "w4a8_linear_m32_k3840_n3840_g64"
+        w = workloads.WORKLOADS[wl]
+        inp = workloads.workload_inputs(wl)
+        x = bf16(inp["x"])
+        packed = torch.from_numpy(inp["packed"]).to(dev)
+        scl = bf16(inp["w_scales"])
+        out = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device=dev)
+        work = torch.empty((ck.workspace_bytes(w["M"], w["K"], w["N"]),), dtype=torch.uint8, device=dev)
+
+        def fn():
+            ck.linear(x, w["G"], 8, packed, scl, True, out=out, workspace=work)
     elif name.startswith("awq_w4a16_gemv"):
         d = workloads.workload_inputs("awq_w4a16_gemv_m1_k3072_n18432")
         xv = bf16(d["x"])

@@ -318,7 +318,8 @@ ck_status ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t l
 /* The rotation of ck_rotate_quant as held in registers, divided by sqrt(G)
  * (exact, sqrt(G) is a power of two): xr fp32 [M, ldr].  It runs the kernel
  * instantiation that ck_rotate_quant and ck_rotate_quant_packed4 run for the
- * same K and G (16-column chunks from G = 64 on, 8-column chunks at G = 16).
+ * same M, K and G (8-column chunks at G = 16 and for up to 64 rows of up to
+ * 4096 columns, 16-column chunks otherwise).
  * The weight producer (ck_quantize_weights) always uses 8-column chunks; those
  * apply the same butterfly stages to the same operands in the same order, so
  * the values are identical, which its bit-exact test checks. */

@@ -363,6 +363,15 @@ hipError_t launch_g(int cpt, dim3 grid, hipStream_t s, const uint16_t *x, int64_
     return hipGetLastError();
 }
 
+// Up to this many rows the kernel is latency-bound (a few workgroups on an
+// otherwise idle chip): rows of up to 4096 columns then run 512 threads of
+// one 8-column chunk each, so that each thread's serial chain is shortest.
+// Measured on MI355X (K = 3840, G = 64) in the whole W4A8 linear: M = 32
+// 10.36 us with 128 threads of two 16-column chunks, 9.51 with 256 threads of
+// one, 9.37 with 512 threads of one 8-column chunk, 11.75 with one wave of
+// four 16-column chunks; M = 4 11.91 / 10.94 / 10.74 / 13.29 us.
+constexpr int64_t kFewRows = 64;
+
 template <int G, int MODE>
 hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t ldx, float qmax,
                      int8_t *codes, int64_t ldq, float *rs, float *xr, int64_t ldr,
@@ -371,9 +380,11 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
     const dim3 grid((unsigned)M);
     if constexpr ((MODE == kCodes8 || MODE == kPacked4 || MODE == kF32 || MODE == kTiled16) && G >= 64) {
         // Activation codes from G = 64 on: 16-column chunks (K is a multiple
-        // of G).  The fp32 test output takes the same instantiation, so the
-        // rotation it exposes is the one the activation codes are made from.  Up to 10240 columns 128 threads of up to 5 chunks, then 256,
-        // then 1024 threads of up to 2.  The in-register distance-8 stage and
+        // of G), except for the few-row shapes above.  The fp32 test output
+        // takes the same instantiation for the same M, K and G, so the
+        // rotation it exposes is the one the activation codes are made from.
+        // Up to 10240 columns 128 threads of up to 5 chunks, then 256, then
+        // 1024 threads of up to 2.  The in-register distance-8 stage and
         // the longer rows per thread take 1-2 VALU instructions per element
         // off (13.3 instead of 15.3 at G = 256, K = 10240), which is what
         // sets the time here: 5-10% faster at G = 64 and 256.  At G = 16 the
@@ -381,6 +392,8 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
         // cache lines per instruction (a 16-column chunk is two 16-byte loads
         // 32 bytes apart), measured 8% faster.
         const int nchunk = K / 16;
+        if (M <= kFewRows && K / 8 <= 512)
+            return launch_g<G, 512, MODE, 8>(1, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
         if (nchunk <= 128 * 5)
             return launch_g<G, 128, MODE, 16>((nchunk + 127) / 128, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr,
                                               ldr, wsc, ldsc);
@@ -391,6 +404,8 @@ hipError_t launch_rq(int64_t M, int K, hipStream_t s, const uint16_t *x, int64_t
                                            ldr, wsc, ldsc);
     } else {
         const int nchunk = K / 8;
+        if (M <= kFewRows && nchunk <= 512)
+            return launch_g<G, 512, MODE, 8>(1, grid, s, x, ldx, K, qmax, codes, ldq, rs, xr, ldr, wsc, ldsc);
         // Rows of up to 8192 columns: 128 threads with up to 8 chunks each, which
         // measured 3-10% faster than 256 threads at K = 2048 and 3840 (more loads
         // in flight per thread, more resident rows per CU).
