@@ -242,14 +242,33 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     }
 
     // 4. sum over the lanes of the wave, then over the waves (fixed order).
-    constexpr int kShift = R == 32 ? 1 : R == 16 ? 2 : 3;
-    const int row = lane >> kShift;
-    const bool owner = (lane & ((1 << kShift) - 1)) == 0;
+    //    When M * R is 16 or 32 the (activation row, weight row) partials go
+    //    through one transposed reduction together, which takes fewer lane
+    //    exchanges than M separate ones.
+    constexpr bool kJoint = M > 1 && (M * R == 16 || M * R == 32);
+    if constexpr (kJoint) {
+        constexpr int V = M * R;
+        constexpr int kShift = V == 32 ? 1 : 2;
+        uint32_t flat[V];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const uint32_t t = transposed_row_sum<R, FSUM>(part[m], lane);
-        if (owner)
-            s_red[wave][row][m] = t;
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                flat[m * R + r] = part[m][r];
+        const uint32_t t = transposed_row_sum<V, FSUM>(flat, lane);
+        const int v = lane >> kShift;  // m * R + r
+        if ((lane & ((1 << kShift) - 1)) == 0)
+            s_red[wave][v % R][v / R] = t;
+    } else {
+        constexpr int kShift = R == 32 ? 1 : R == 16 ? 2 : 3;
+        const int row = lane >> kShift;
+        const bool owner = (lane & ((1 << kShift) - 1)) == 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint32_t t = transposed_row_sum<R, FSUM>(part[m], lane);
+            if (owner)
+                s_red[wave][row][m] = t;
+        }
     }
     __syncthreads();
     for (int e = threadIdx.x; e < R * M; e += blockDim.x) {
