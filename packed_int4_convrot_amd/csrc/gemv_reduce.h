@@ -19,6 +19,22 @@ __device__ __forceinline__ uint32_t lane_xor_u(uint32_t v)
         return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (MASK << 10));
 }
 
+// v from a partner lane in another half of its 8-lane group (DPP
+// row_half_mirror: lane i <-> 7 - i within each group of 8), so the pair
+// differs in bit 2 like lane ^ 4, without the LDS-pipe round trip of
+// ds_swizzle.  Enough wherever only the set of pairs across bit 2 matters
+// (sums and maxima over the 8 lanes).
+__device__ __forceinline__ uint32_t lane_mirror8_u(uint32_t v)
+{
+    return __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, true);
+}
+
+// v from lane 15 - i of its 16-lane row (DPP row_mirror): pairs across bit 3.
+__device__ __forceinline__ uint32_t lane_mirror16_u(uint32_t v)
+{
+    return __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, true);
+}
+
 template <bool F>
 __device__ __forceinline__ uint32_t add32(uint32_t a, uint32_t b)
 {
@@ -64,7 +80,7 @@ __device__ __forceinline__ uint32_t transposed_row_sum(uint32_t (&p)[R], int lan
     if constexpr (R >= 16) halve_rows<4, R / 8, F>(p, lane);
     if constexpr (R >= 32) halve_rows<2, R / 16, F>(p, lane);
     uint32_t v = p[0];
-    if constexpr (R == 8) v = add32<F>(v, lane_xor_u<4>(v));
+    if constexpr (R == 8) v = add32<F>(v, lane_mirror8_u(v));
     if constexpr (R <= 16) v = add32<F>(v, lane_xor_u<2>(v));
     v = add32<F>(v, lane_xor_u<1>(v));
     return v;

@@ -155,13 +155,15 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
 #pragma unroll
             for (int r = 0; r < 32; ++r)
                 am = fmaxf(am, fabsf(v[r]));
+            // Maximum over each 16-lane row by DPP alone, then over the four rows.
             am = fmaxf(am, __uint_as_float(lane_xor_u<1>(__float_as_uint(am))));
             am = fmaxf(am, __uint_as_float(lane_xor_u<2>(__float_as_uint(am))));
-            am = fmaxf(am, __uint_as_float(lane_xor_u<4>(__float_as_uint(am))));
-            am = fmaxf(am, __uint_as_float(lane_xor_u<8>(__float_as_uint(am))));
-            am = fmaxf(am, __uint_as_float(lane_xor_u<16>(__float_as_uint(am))));
-            am = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 0)),
-                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32)));
+            am = fmaxf(am, __uint_as_float(lane_mirror8_u(__float_as_uint(am))));
+            am = fmaxf(am, __uint_as_float(lane_mirror16_u(__float_as_uint(am))));
+            am = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 0)),
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16))),
+                       fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32)),
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48))));
             if (lane == 0)
                 s_am[wave][m] = am;
         }
