@@ -99,16 +99,20 @@ __device__ __forceinline__ void fht(float (&v)[CPT][CW], int lane)
     if constexpr (L >= 32) lane_stage<16, CPT, CW, SWZ>(v, (lane & 16) ? -1.f : 1.f);
 }
 
+// Maximum over the wave: over each 16-lane row by DPP alone (quad permutes,
+// then row_half_mirror and row_mirror, which pair lanes across bits 2 and 3),
+// then over the four rows' first lanes.
 __device__ __forceinline__ float wave_max(float v)
 {
     v = fmaxf(v, lane_xor<1>(v));
     v = fmaxf(v, lane_xor<2>(v));
-    v = fmaxf(v, lane_xor<4>(v));
-    v = fmaxf(v, lane_xor<8>(v));
-    v = fmaxf(v, lane_xor<16>(v));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true)));
     const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    return fmaxf(a, b);
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 // Low byte of fp32(t) + 1.5 * 2^23 is the two's-complement of rne(t) for
@@ -222,7 +226,8 @@ __global__ __launch_bounds__(BLOCK) void rotate_quant_kernel(
                     gm = fmaxf(gm, fabsf(v[i][r]));
                 gm = fmaxf(gm, lane_xor<1>(gm));
                 gm = fmaxf(gm, lane_xor<2>(gm));
-                gm = fmaxf(gm, lane_xor<4>(gm));
+                gm = fmaxf(gm, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gm), 0x141, 0xF, 0xF,
+                                                                          true)));  // row_half_mirror
                 ws = weight_scale<G>(gm);
                 if ((FULL || c < nchunk) && (c & 7) == 0)
                     wscales[(int64_t)(c >> 3) * ldsc + m] = ws.bits;
