@@ -88,7 +88,12 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     //    (each 1 KiB block is one operand, so the loads are whole lines): the
     //    weight slice first, as it comes from HBM, then scales and codes.
     u32x4 raw[GPW][MT];
-    uint16_t sw[GPW];
+    // Per-group weight scales, one dword per lane and 8 groups: lane l holds
+    // the scales of columns n0 + 2 (l % 8) and + 1 in group g0 + l / 8 (+ 8 q),
+    // a coalesced 256-byte load instead of GPW two-byte loads per lane; each
+    // lane picks its column's scale from the owning lane with ds_bpermute.
+    constexpr int kSwLd = PER_GROUP ? (GPW + 7) / 8 : 1;
+    uint32_t swd[kSwLd];
     auto load_weights = [&]() {
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
@@ -103,8 +108,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     auto load_scales = [&]() {
         if constexpr (PER_GROUP) {
 #pragma unroll
-            for (int j = 0; j < GPW; ++j)
-                sw[j] = w_scales[(int64_t)min(g0 + j, ng - 1) * N + n0 + col];
+            for (int q = 0; q < kSwLd; ++q)
+                swd[q] = *reinterpret_cast<const uint32_t *>(
+                    w_scales + (int64_t)min(g0 + 8 * q + lane / 8, ng - 1) * N + n0 + 2 * (lane % 8));
         }
     };
     if constexpr (TILED) {
@@ -180,7 +186,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     for (int j = 0; j < GPW; ++j) {
         const v4i b = w4_operand_x16(wq[j][0], wq[j][1]);
         if constexpr (PER_GROUP) {
-            const float sc = bf16_to_f32(sw[j]);
+            const uint32_t pair = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((j % 8) * 8 + col / 2),
+                                                                        (int)swd[j / 8]);
+            const float sc = __uint_as_float((col & 1) ? pair & 0xffff0000u : pair << 16);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j][mt], b, v4i{0, 0, 0, 0}, 0, 0, 0);
