@@ -41,7 +41,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_decode_gemv_m1_k3840_n10240_traffic.txt")
-GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv.hip", "packed_int4_convrot_amd/csrc/ck_device.h"]
+GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
+                "packed_int4_convrot_amd/csrc/ck_device.h", "packed_int4_convrot_amd/csrc/launch.h"]
 
 
 def log(msg):
@@ -170,14 +171,14 @@ PROFILE_WORKLOADS = {
         kernel="w4_skinny_kernel", M=32, K=3840, N=3840, mops=None,
         alg_bytes=3840 * 3840 // 2 + 60 * 3840 * 2 + 32 * 3840 + 32 * 4 + 32 * 3840 * 2),
 }
+_COMMON = ["packed_int4_convrot_amd/csrc/ck_device.h", "packed_int4_convrot_amd/csrc/launch.h"]
 KERNEL_SOURCES = {
-    "w4_gemm_kernel": ["packed_int4_convrot_amd/csrc/w4_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
-    "awq_gemm_kernel": ["packed_int4_convrot_amd/csrc/awq_gemm.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
-    "rotate_quant_kernel": ["packed_int4_convrot_amd/csrc/rotate_quant.hip",
-                            "packed_int4_convrot_amd/csrc/ck_device.h"],
-    "w4a16_gemv_kernel": ["packed_int4_convrot_amd/csrc/w4a16_gemv.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
-                          "packed_int4_convrot_amd/csrc/ck_device.h"],
-    "w4_skinny_kernel": ["packed_int4_convrot_amd/csrc/w4_skinny.hip", "packed_int4_convrot_amd/csrc/ck_device.h"],
+    "w4_gemm_kernel": ["packed_int4_convrot_amd/csrc/w4_gemm.hip"] + _COMMON,
+    "awq_gemm_kernel": ["packed_int4_convrot_amd/csrc/awq_gemm.hip"] + _COMMON,
+    "rotate_quant_kernel": ["packed_int4_convrot_amd/csrc/rotate_quant.hip"] + _COMMON,
+    "w4a16_gemv_kernel": ["packed_int4_convrot_amd/csrc/w4a16_gemv.hip",
+                          "packed_int4_convrot_amd/csrc/gemv_reduce.h"] + _COMMON,
+    "w4_skinny_kernel": ["packed_int4_convrot_amd/csrc/w4_skinny.hip"] + _COMMON,
 }
 
 
