@@ -67,6 +67,31 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
     return perm(p23, p01, 0x05040100u);
 }
 
+// Transposed lane reduction of part[M0 .. M0 + B)[R] (B = 4, 2 or 1 rows, as
+// many as fit in 32 values), then the rest; the owner lanes store the wave's
+// sums to red[r][m].
+template <int M, int R, bool F, int M0>
+__device__ __forceinline__ void reduce_rows(uint32_t (&part)[M][R], int lane, uint32_t (&red)[R][M])
+{
+    if constexpr (M0 < M) {
+        constexpr int left = M - M0;
+        constexpr int B = (R == 8 && left >= 4) ? 4 : (R <= 16 && left >= 2 && 2 * R <= 32) ? 2 : 1;
+        constexpr int V = B * R;
+        constexpr int kShift = V == 32 ? 1 : V == 16 ? 2 : 3;
+        uint32_t flat[V];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                flat[b * R + r] = part[M0 + b][r];
+        const uint32_t t = transposed_row_sum<V, F>(flat, lane);
+        const int v = lane >> kShift;  // b * R + r
+        if ((lane & ((1 << kShift) - 1)) == 0)
+            red[v % R][M0 + v / R] = t;
+        reduce_rows<M, R, F, M0 + B>(part, lane, red);
+    }
+}
+
 template <int M, int R, int G, bool PER_GROUP, bool OUT_I32>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, float qmax, const int8_t *__restrict__ codes,
@@ -244,34 +269,12 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     }
 
     // 4. sum over the lanes of the wave, then over the waves (fixed order).
-    //    When M * R is 16 or 32 the (activation row, weight row) partials go
-    //    through one transposed reduction together, which takes fewer lane
-    //    exchanges than M separate ones.
-    constexpr bool kJoint = M > 1 && (M * R == 16 || M * R == 32);
-    if constexpr (kJoint) {
-        constexpr int V = M * R;
-        constexpr int kShift = V == 32 ? 1 : 2;
-        uint32_t flat[V];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                flat[m * R + r] = part[m][r];
-        const uint32_t t = transposed_row_sum<V, FSUM>(flat, lane);
-        const int v = lane >> kShift;  // m * R + r
-        if ((lane & ((1 << kShift) - 1)) == 0)
-            s_red[wave][v % R][v / R] = t;
-    } else {
-        constexpr int kShift = R == 32 ? 1 : R == 16 ? 2 : 3;
-        const int row = lane >> kShift;
-        const bool owner = (lane & ((1 << kShift) - 1)) == 0;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint32_t t = transposed_row_sum<R, FSUM>(part[m], lane);
-            if (owner)
-                s_red[wave][row][m] = t;
-        }
-    }
+    //    The (activation row, weight row) partials go through transposed lane
+    //    reductions of up to 32 values at once (4, 2 or 1 activation rows of
+    //    8 weight rows), which take fewer lane exchanges than one reduction
+    //    per activation row; each is the same binary tree over the lanes, so
+    //    the sums are the same bit for bit.
+    reduce_rows<M, R, FSUM, 0>(part, lane, s_red[wave]);
     __syncthreads();
     for (int e = threadIdx.x; e < R * M; e += blockDim.x) {
         const int r = e / M, m = e % M;
