@@ -127,13 +127,22 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8 *smem = (lds_u8 *)smem_generic;
 
-    // XCD-aware renumbering of the block index.
+    // XCD-aware renumbering of the block index, then a grouped raster: runs
+    // of kGroupM tile rows are walked column by column, so the tiles an XCD
+    // runs at the same time share a few activation and weight blocks (at
+    // M = 8192, N = 3840, the 32 tiles of an XCD's first round read 4
+    // activation and 8 weight blocks instead of 3 and 15).
+    constexpr int kGroupM = 4;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int tile = xcd_block(blockIdx.x, tiles);
-    const int m0 = (tile / tiles_n) * BM;
-    const int n0 = (tile % tiles_n) * BN;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int group_m = min(kGroupM, tiles_m - first_m);
+    const int in_group = tile - group * kGroupM * tiles_n;
+    const int m0 = (first_m + in_group % group_m) * BM;
+    const int n0 = (in_group / group_m) * BN;
 
     const int t = threadIdx.x;
     const int wave = t / kWave, lane = t % kWave;
