@@ -107,11 +107,19 @@ __global__ __launch_bounds__(NW * kWave) void awq_gemm_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8 *smem = (lds_u8 *)smem_generic;
 
+    // XCD-aware renumbering, then a grouped raster (runs of kGroupM tile rows
+    // walked column by column), so that the tiles an XCD runs at the same time
+    // share a few activation and weight blocks.
+    constexpr int kGroupM = 4;
     const int tiles_m = (M + kBM - 1) / kBM;
     const int tiles_n = (N + kBN - 1) / kBN;
     const int tile = xcd_block(blockIdx.x, tiles_m * tiles_n);
-    const int m0 = (tile / tiles_n) * kBM;
-    const int n0 = (tile % tiles_n) * kBN;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int group_m = min(kGroupM, tiles_m - first_m);
+    const int in_group = tile - group * kGroupM * tiles_n;
+    const int m0 = (first_m + in_group % group_m) * kBM;
+    const int n0 = (in_group / group_m) * kBN;
 
     const int t = threadIdx.x;
     const int wave = t / kWave, lane = t % kWave;
