@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_decode_gemv_m1_k3840_n10240_traffic.txt")
-GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
+GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv_fused.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
                 "packed_int4_convrot_amd/csrc/ck_device.h", "packed_int4_convrot_amd/csrc/launch.h"]
 
 
@@ -85,7 +85,7 @@ def sources_sha(paths):
 
 CALIB_BYTES = 256 << 20        # bytes read and bytes written by the calibration copy
 CALIB_KERNEL = "neg_kernel"    # torch's elementwise negation: one read and one write per element
-HEADLINE_KERNEL = "w4_gemv_kernel<1,"
+HEADLINE_KERNEL = "w4_gemv_fused_kernel<1,"
 
 
 def calibration_copy():
@@ -459,7 +459,7 @@ def main():
                    "weight_scales": "per-group (64), bf16", "weight_copies_cycled": args.copies,
                    "step": "ck_w4a8_linear (rotate-quant fused into the decode GEMV, one launch)",
                    "timing": "K steps captured in one HIP graph, replayed between synchronisations"},
-        "roofline": {"bound": "hbm", "kernel": "w4_gemv_kernel (fused rotate-quant + decode GEMV)",
+        "roofline": {"bound": "hbm", "kernel": "w4_gemv_fused_kernel (rotate-quant + decode GEMV, one workgroup per CU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(ms_step * 1e3, 3)},

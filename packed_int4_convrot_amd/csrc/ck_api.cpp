@@ -246,7 +246,7 @@ int run_gemm(const char *fn, const void *codes, int64_t ldq, const float *rs, in
     const int8_t *c8 = static_cast<const int8_t *>(codes);
     int e;
     if (path == GemmPath::kGemv) {
-        e = ck::launch_w4_gemv(nullptr, 0, 0, 0, c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw,
+        e = ck::launch_w4_gemv(c8, ldq, rs, (int)M, (int)K, w.packed, w.ldw,
                                w.scales, pg, (int)w.N, bias, x_scale, out, ldo, acc, lda, stream);
     } else if (path == GemmPath::kSkinny) {
         e = ck::launch_w4_skinny(c8, ldq, tiled, rs, (int)M, (int)K, w.packed, w.ldw, w.scales, pg,
@@ -373,9 +373,9 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
     const int qmax = bits == 8 ? 127 : 7;
     if (plan.fused) {
         // Decode shapes: one launch that rotates, quantises and multiplies.
-        const int e = ck::launch_w4_gemv(x, ldx, G, qmax, nullptr, 0, nullptr, (int)M, (int)K, w.packed,
-                                         w.ldw, w.scales, w.kind == CK_WS_PER_GROUP, (int)w.N, bias,
-                                         x_scale, out, ldo, nullptr, 0, stream);
+        const int e = ck::launch_w4_gemv_fused(x, ldx, G, qmax, (int)M, (int)K, w.packed, w.ldw, w.scales,
+                                               w.kind == CK_WS_PER_GROUP, (int)w.N, bias, x_scale, out, ldo,
+                                               stream);
         return hip_status(e, fn);
     }
     int8_t *codes = static_cast<int8_t *>(ws);

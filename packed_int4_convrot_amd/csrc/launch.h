@@ -37,24 +37,74 @@ int launch_awq_gemm(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t 
 int launch_quantize_weights(const uint16_t *w, int64_t N, int K, int64_t ldw_in, int G, bool per_group,
                             uint8_t *packed, int64_t ldp, uint16_t *scales, void *stream);
 
-// Decode GEMV for 1 <= M <= 8 (VALU dot4, 1 KiB coalesced weight rows).  With
-// G != 0 (M <= 2) it rotates and quantises the bf16 rows x itself (fused linear); with
-// G == 0 it reads given codes and row_scales.  acc_out != nullptr (G == 0
-// only) selects the int32 test epilogue.
-int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
-                   const float *row_scales, int M, int K, const uint8_t *packed, int64_t ldw,
-                   const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias, float x_scale,
-                   uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream);
+// Decode GEMV for 1 <= M <= 8 (VALU dot4, 1 KiB coalesced weight rows) on
+// given codes and row_scales.  acc_out != nullptr selects the int32 test
+// epilogue.
+int launch_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group, int N,
+                   const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo, int32_t *acc_out,
+                   int64_t lda, void *stream);
 // The decode GEMV: 1 <= M <= 8 activation rows, one wave per 2048 columns of K,
-// at most 8 waves; the fused rotate-quant form takes one or two rows.
+// at most 8 waves.
 constexpr int kGemvMaxWaves = 8;
 constexpr int kGemvMaxM = 8;
-constexpr int kGemvMaxFusedRows = 2;
 inline bool w4_gemv_supports(int64_t M, int64_t K)
 {
     return M >= 1 && M <= kGemvMaxM && K <= 2048 * kGemvMaxWaves;
 }
-inline bool w4_gemv_fused_supports(int64_t M, int64_t K) { return w4_gemv_supports(M, K) && M <= kGemvMaxFusedRows; }
+
+// The whole decode linear in one launch (w4_gemv_fused.hip): rotate-quant of
+// 1 <= M <= 4 bf16 rows and the GEMV, one workgroup of up to 16 waves per
+// compute unit.  Workgroup shape: nws streaming waves (S = ceil(K / 2048)
+// column slices for each of RB blocks of 8 weight rows, at most 12 waves) and
+// nwr rotation waves (a multiple of 4 that fits in 16, no more than the
+// 8-column chunks of a row need), cpr chunks per rotation thread and row (M * cpr <= 8: the
+// rotated values stay in registers), lds bytes of dynamic LDS (the M * K
+// codes, raised above half the CU's LDS when the grid fits the chip, so that
+// no CU runs two workgroups).  RB is the largest that covers N with one
+// workgroup per CU and leaves the rotation enough waves.
+constexpr int kGemvFusedMaxRows = 4;
+constexpr int kFusedMaxWaves = 16, kFusedMaxStreamWaves = 12, kFusedMaxChunks = 8;
+struct FusedGemvShape {
+    int nb, nws, nwr, s, rb, cpr, lds;
+};
+inline bool w4_gemv_fused_shape(int64_t M, int64_t K, int64_t N, int ncu, FusedGemvShape &sh)
+{
+    if (M < 1 || M > kGemvFusedMaxRows || K < 64 || K > 2048 * kGemvMaxWaves || K % 64 != 0 || N < 8 ||
+        N % 8 != 0 || ncu < 1)
+        return false;
+    const int64_t nrb = N / 8, nchunk = K / 8, s = (K + 2047) / 2048;
+    int64_t rb = (nrb + ncu - 1) / ncu;
+    if (rb * s > kFusedMaxStreamWaves)
+        rb = kFusedMaxStreamWaves / s;
+    for (; rb >= 1; --rb) {
+        const int64_t nws = rb * s;
+        // A multiple of 4 rotation waves: consecutive waves of a workgroup go
+        // to the CU's 4 SIMDs in turn, so each SIMD gets the same share.
+        int64_t nwr = (kFusedMaxWaves - nws) / 4 * 4;
+        if (nwr > (nchunk + 63) / 64)
+            nwr = (nchunk + 63) / 64;
+        const int64_t c = (nchunk + 64 * nwr - 1) / (64 * nwr);
+        const int64_t cpr = c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8;
+        if (c > 8 || M * cpr > kFusedMaxChunks)
+            continue;
+        sh.s = (int)s, sh.rb = (int)rb, sh.nws = (int)nws, sh.nwr = (int)nwr, sh.cpr = (int)cpr;
+        sh.nb = (int)((nrb + rb - 1) / rb);
+        const int64_t lds = M * K;
+        constexpr int64_t kOneWorkgroupPerCu = 80 * 1024 + 16;
+        sh.lds = (int)(sh.nb <= ncu && lds < kOneWorkgroupPerCu ? kOneWorkgroupPerCu : lds);
+        return true;
+    }
+    return false;
+}
+inline bool w4_gemv_fused_supports(int64_t M, int64_t K)
+{
+    FusedGemvShape sh;
+    return w4_gemv_fused_shape(M, K, 8, 1, sh);
+}
+int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M, int K, const uint8_t *packed,
+                         int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
+                         float x_scale, uint16_t *out, int64_t ldo, void *stream);
 
 // Skinny path: M <= 64, weights streamed once, activations held in registers.
 // acc_out != nullptr selects the int32 test epilogue.

@@ -1,26 +1,19 @@
-// Decode GEMV for 1 <= M <= 8 activation rows, optionally (M <= 2) fused with
-// the rotate-quant of those rows.
+// Decode GEMV for 1 <= M <= 8 activation rows on given int8 codes.
 //
 // Prior art: the W4A8 decode GEMV of "[PR #182] HIP port of #176: W4A8 decode
 // GEMV and fused GatedDeltaNet decode" (description): register-side int4
 // decode feeding v_dot4 integer dot products and a rowwise x weight-scale
-// epilogue, with no decoded weight copy in memory.  The fused form follows the
-// activation-side fusion of "[PR #155] [Feat][Ascend] Add fused RotateQuant
-// backend" one step further: the rotate-quant of the few activation rows runs
-// inside the GEMV launch, while the weights are already streaming in.
+// epilogue, with no decoded weight copy in memory.  (The whole decode linear
+// from bf16 rows, with the rotate-quant in the same launch, is
+// w4_gemv_fused.hip; it keeps this kernel's per-wave layout and arithmetic.)
 //
 // Layout (built for HBM streaming, one K slice per wave):
 //   * wave w of a block owns columns k in [2048 w, 2048 w + 2048); lane l owns
 //     the 32 columns starting at 2048 w + 32 l, i.e. 16 packed bytes of every
 //     weight row, so one load instruction reads 1 KiB of contiguous weights;
-//   * a block handles R consecutive weight rows; each lane issues its R
-//     16-byte weight loads first, then builds its activation operands (int8
-//     codes for its 32 columns, split into even / odd k to match the nibble
-//     decode) from either given codes or, fused, from bf16 x:
-//       load 32 bf16 -> fp32 -> butterflies of H_G (in registers for strides
-//       < 32, DPP / ds_swizzle across lanes above) -> row absmax over all lanes
-//       and waves -> codes = rne(y * qmax / absmax) (the same arithmetic as the
-//       rotate-quant kernel, so the codes are bit-identical to it);
+//   * a block handles R consecutive weight rows; each lane issues its
+//     activation-code loads, then its R 16-byte weight loads, then splits its
+//     32 codes into even / odd k to match the nibble decode;
 //   * per weight row: unsigned nibbles (0..15) times codes with v_dot4_i32_i8,
 //     then subtract 8 * sum(codes) (the code-8 offset), then the per-group
 //     scale for the lane's group;
@@ -38,35 +31,6 @@ constexpr int kMaxWaves = kGemvMaxWaves;  // K <= 16384
 #ifndef CK_GEMV_ROWS
 #define CK_GEMV_ROWS 8  // weight rows per block (8, 16 or 32)
 #endif
-// The fused form pays the rotation of every row once per block.  Measured on
-// MI355X (K = 3840, N = 10240, per-group scales, graph replay, cold weights),
-// fused against rotate-quant + GEMV on codes: M = 1 6.84 / 9.44 us, M = 2
-// 9.16 / 10.35, M = 3 12.40 / 11.04, M = 4 16.02 / 11.78, M = 5 19.12 / 12.45:
-// each further row adds about 3.1 us of rotation across the 1280 blocks, so
-// the fused form stops at two rows.
-constexpr int kMaxFusedRows = kGemvMaxFusedRows;
-
-// One cross-lane butterfly stage on 32 values per lane (fused rotation).
-template <int MASK>
-__device__ __forceinline__ void lane_stage32(float (&v)[32], int lane)
-{
-    const float sgn = (lane & MASK) ? -1.f : 1.f;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        const float p = __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[r])));
-        v[r] = __builtin_fmaf(v[r], sgn, p);
-    }
-}
-
-__device__ __forceinline__ uint32_t rne_byte(float t) { return __float_as_uint(t + 12582912.0f); }
-
-__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
-{
-    const uint32_t p01 = perm(b1, b0, 0x0C0C0400u);
-    const uint32_t p23 = perm(b3, b2, 0x0C0C0400u);
-    return perm(p23, p01, 0x05040100u);
-}
-
 // Transposed lane reduction of part[M0 .. M0 + B)[R] (B = 4, 2 or 1 rows, as
 // many as fit in 32 values), then the rest; the owner lanes store the wave's
 // sums to red[r][m].
@@ -92,16 +56,14 @@ __device__ __forceinline__ void reduce_rows(uint32_t (&part)[M][R], int lane, ui
     }
 }
 
-template <int M, int R, int G, bool PER_GROUP, bool OUT_I32>
+template <int M, int R, bool PER_GROUP, bool OUT_I32>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
-    const uint16_t *__restrict__ x, int64_t ldx, float qmax, const int8_t *__restrict__ codes,
-    int64_t ldq, const float *__restrict__ row_scales, int K, const uint8_t *__restrict__ packed,
-    int64_t ldw, const uint16_t *__restrict__ w_scales, int N, const uint16_t *__restrict__ bias,
-    float x_scale, uint16_t *__restrict__ out, int64_t ldo, int32_t *__restrict__ acc_out, int64_t lda)
+    const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int K,
+    const uint8_t *__restrict__ packed, int64_t ldw, const uint16_t *__restrict__ w_scales, int N,
+    const uint16_t *__restrict__ bias, float x_scale, uint16_t *__restrict__ out, int64_t ldo,
+    int32_t *__restrict__ acc_out, int64_t lda)
 {
-    constexpr bool FUSED = G != 0;
     constexpr bool FSUM = PER_GROUP && !OUT_I32;  // partials are fp32 (scaled) or exact int32
-    __shared__ float s_am[kMaxWaves][M];
     __shared__ uint32_t s_red[kMaxWaves][R][M];
 
     const int nw = blockDim.x / kWave;
@@ -111,24 +73,17 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     const bool active = kbase < K;
     const int kc = active ? kbase : K - 32;  // clamped: every address stays inside the row
 
-    // 1. Loads, in this order: the activations (small, usually L2-resident),
-    //    the weight scales, then the R weight rows.  Loads retire in issue
-    //    order, so the activation work below waits only for the activations,
-    //    and row r's dot products only for rows 0..r, while the remaining
-    //    weight rows are still streaming in.
-    u32x4 araw[M][FUSED ? 4 : 2];
+    // 1. Loads, in this order: the activation codes (small, usually
+    //    L2-resident), the weight scales, then the R weight rows.  Loads retire
+    //    in issue order, so the activation work below waits only for the
+    //    codes, and row r's dot products only for rows 0..r, while the
+    //    remaining weight rows are still streaming in.
+    u32x4 araw[M][2];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        if constexpr (FUSED) {
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                araw[m][c] = *reinterpret_cast<const u32x4 *>(x + (int64_t)m * ldx + kc + 8 * c);
-        } else {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                araw[m][c] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + kc + 16 * c);
-        }
-    }
+        for (int c = 0; c < 2; ++c)
+            araw[m][c] = *reinterpret_cast<const u32x4 *>(codes + (int64_t)m * ldq + kc + 16 * c);
     // The R scales of the lane's group are contiguous: R / 8 16-byte loads.
     // (Eight 2-byte loads per row block were measured ~0.5 us slower.)
     u32x4 sv[PER_GROUP ? R / 8 : 1];
@@ -147,86 +102,20 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     // 2. activation codes for this lane's 32 columns: even k in alo, odd k in ahi.
     uint32_t alo[M][4], ahi[M][4];
     float sx[M];
-    if constexpr (FUSED) {
-        constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
-        float inv[M];
-        float vv[M][32];
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float(&v)[32] = vv[m];
+    for (int m = 0; m < M; ++m) {
+        const u32x4 c0 = araw[m][0];
+        const u32x4 c1 = araw[m][1];
+        const v4i p0 = act_perm16(c0[0], c0[1], c0[2], c0[3]);
+        const v4i p1 = act_perm16(c1[0], c1[1], c1[2], c1[3]);
+        const uint32_t q[8] = {(uint32_t)p0[0], (uint32_t)p0[1], (uint32_t)p0[2], (uint32_t)p0[3],
+                               (uint32_t)p1[0], (uint32_t)p1[1], (uint32_t)p1[2], (uint32_t)p1[3]};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 w = araw[m][c];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[8 * c + 2 * j] = active ? __uint_as_float(w[j] << 16) : 0.f;
-                    v[8 * c + 2 * j + 1] = active ? __uint_as_float(w[j] & 0xffff0000u) : 0.f;
-                }
-            }
-            // Butterflies of H_G: strides 1 .. min(G/2, 16) in registers, then across lanes.
-#pragma unroll
-            for (int h = 1; h < 32 && h < G; h <<= 1)
-#pragma unroll
-                for (int r = 0; r < 32; ++r)
-                    if ((r & h) == 0) {
-                        const float a = v[r], b = v[r + h];
-                        v[r] = a + b;
-                        v[r + h] = a - b;
-                    }
-            if constexpr (G >= 64) lane_stage32<1>(v, lane);
-            if constexpr (G >= 128) lane_stage32<2>(v, lane);
-            if constexpr (G >= 256) lane_stage32<4>(v, lane);
-            float am = 0.f;
-#pragma unroll
-            for (int r = 0; r < 32; ++r)
-                am = fmaxf(am, fabsf(v[r]));
-            // Maximum over each 16-lane row by DPP alone, then over the four rows.
-            am = fmaxf(am, __uint_as_float(lane_xor_u<1>(__float_as_uint(am))));
-            am = fmaxf(am, __uint_as_float(lane_xor_u<2>(__float_as_uint(am))));
-            am = fmaxf(am, __uint_as_float(lane_mirror8_u(__float_as_uint(am))));
-            am = fmaxf(am, __uint_as_float(lane_mirror16_u(__float_as_uint(am))));
-            am = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 0)),
-                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16))),
-                       fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32)),
-                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48))));
-            if (lane == 0)
-                s_am[wave][m] = am;
+        for (int i = 0; i < 4; ++i) {
+            alo[m][i] = active ? q[2 * i] : 0u;
+            ahi[m][i] = active ? q[2 * i + 1] : 0u;
         }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float am = s_am[0][m];
-            for (int w = 1; w < nw; ++w)
-                am = fmaxf(am, s_am[w][m]);
-            inv[m] = am > 0.f ? qmax / am : 0.f;
-            sx[m] = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;
-            const float(&v)[32] = vv[m];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t b[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    b[j] = rne_byte(v[8 * i + j] * inv[m]);
-                alo[m][i] = pack4(b[0], b[2], b[4], b[6]);
-                ahi[m][i] = pack4(b[1], b[3], b[5], b[7]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const u32x4 c0 = araw[m][0];
-            const u32x4 c1 = araw[m][1];
-            const v4i p0 = act_perm16(c0[0], c0[1], c0[2], c0[3]);
-            const v4i p1 = act_perm16(c1[0], c1[1], c1[2], c1[3]);
-            const uint32_t q[8] = {(uint32_t)p0[0], (uint32_t)p0[1], (uint32_t)p0[2], (uint32_t)p0[3],
-                                   (uint32_t)p1[0], (uint32_t)p1[1], (uint32_t)p1[2], (uint32_t)p1[3]};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                alo[m][i] = active ? q[2 * i] : 0u;
-                ahi[m][i] = active ? q[2 * i + 1] : 0u;
-            }
-            sx[m] = OUT_I32 ? 1.f : row_scales[m];
-        }
+        sx[m] = OUT_I32 ? 1.f : row_scales[m];
     }
     int asum8[M];  // 8 * sum of this lane's codes (the code - 8 offset)
 #pragma unroll
@@ -294,73 +183,56 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     }
 }
 
-template <int M, int R, int G>
-hipError_t launch_mg(bool pg, bool i32, const uint16_t *x, int64_t ldx, float qmax, const int8_t *codes,
-                     int64_t ldq, const float *rs, int K, const uint8_t *packed, int64_t ldw,
-                     const uint16_t *ws, int N, const uint16_t *bias, float xs, uint16_t *out, int64_t ldo,
-                     int32_t *acc, int64_t lda, hipStream_t s)
+template <int M, int R>
+hipError_t launch_m(bool pg, bool i32, const int8_t *codes, int64_t ldq, const float *rs, int K,
+                    const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N, const uint16_t *bias,
+                    float xs, uint16_t *out, int64_t ldo, int32_t *acc, int64_t lda, hipStream_t s)
 {
     const dim3 grid((unsigned)(N / R));
     const dim3 block((unsigned)(kWave * ((K + 2047) / 2048)));
-    if (i32) {
-        if constexpr (G == 0)
-            hipLaunchKernelGGL((w4_gemv_kernel<M, R, G, false, true>), grid, block, 0, s, x, ldx, qmax, codes,
-                               ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda);
-    } else if (pg) {
-        hipLaunchKernelGGL((w4_gemv_kernel<M, R, G, true, false>), grid, block, 0, s, x, ldx, qmax, codes,
-                           ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda);
-    } else {
-        hipLaunchKernelGGL((w4_gemv_kernel<M, R, G, false, false>), grid, block, 0, s, x, ldx, qmax, codes,
-                           ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda);
-    }
+    if (i32)
+        hipLaunchKernelGGL((w4_gemv_kernel<M, R, false, true>), grid, block, 0, s, codes, ldq, rs, K, packed,
+                           ldw, ws, N, bias, xs, out, ldo, acc, lda);
+    else if (pg)
+        hipLaunchKernelGGL((w4_gemv_kernel<M, R, true, false>), grid, block, 0, s, codes, ldq, rs, K, packed,
+                           ldw, ws, N, bias, xs, out, ldo, acc, lda);
+    else
+        hipLaunchKernelGGL((w4_gemv_kernel<M, R, false, false>), grid, block, 0, s, codes, ldq, rs, K, packed,
+                           ldw, ws, N, bias, xs, out, ldo, acc, lda);
     return hipGetLastError();
-}
-
-template <int M, int R>
-hipError_t launch_m(int G, bool pg, bool i32, const uint16_t *x, int64_t ldx, float qmax,
-                    const int8_t *codes, int64_t ldq, const float *rs, int K, const uint8_t *packed,
-                    int64_t ldw, const uint16_t *ws, int N, const uint16_t *bias, float xs,
-                    uint16_t *out, int64_t ldo, int32_t *acc, int64_t lda, hipStream_t s)
-{
-    if (G == 0)
-        return launch_mg<M, R, 0>(pg, i32, x, ldx, qmax, codes, ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda, s);
-    if constexpr (M <= kMaxFusedRows) {
-        switch (G) {
-        case 16: return launch_mg<M, R, 16>(pg, false, x, ldx, qmax, codes, ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda, s);
-        case 64: return launch_mg<M, R, 64>(pg, false, x, ldx, qmax, codes, ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda, s);
-        case 256: return launch_mg<M, R, 256>(pg, false, x, ldx, qmax, codes, ldq, rs, K, packed, ldw, ws, N, bias, xs, out, ldo, acc, lda, s);
-        default: break;
-        }
-    }
-    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 
-int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
-                   const float *row_scales, int M, int K, const uint8_t *packed, int64_t ldw,
-                   const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias, float x_scale,
-                   uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream)
+int launch_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group, int N,
+                   const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo, int32_t *acc_out,
+                   int64_t lda, void *stream)
 {
     if (!w4_gemv_supports(M, K) || N % 16 != 0)
         return (int)hipErrorInvalidValue;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool i32 = acc_out != nullptr;
-    const float q = (float)qmax;
     constexpr int R = CK_GEMV_ROWS;
     hipError_t e;
+#define CK_GEMV_M(MM)                                                                                       \
+    case MM:                                                                                                \
+        e = launch_m<MM, R>(per_group, i32, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias,     \
+                            x_scale, out, ldo, acc_out, lda, s);                                            \
+        break;
     switch (M) {
-    case 1: e = launch_m<1, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 2: e = launch_m<2, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 3: e = launch_m<3, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 4: e = launch_m<4, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 5: e = launch_m<5, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 6: e = launch_m<6, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 7: e = launch_m<7, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
-    case 8: e = launch_m<8, R>(G, per_group, i32, x, ldx, q, codes, ldq, row_scales, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, acc_out, lda, s); break;
+        CK_GEMV_M(1)
+        CK_GEMV_M(2)
+        CK_GEMV_M(3)
+        CK_GEMV_M(4)
+        CK_GEMV_M(5)
+        CK_GEMV_M(6)
+        CK_GEMV_M(7)
+        CK_GEMV_M(8)
     default: e = hipErrorInvalidValue; break;
     }
+#undef CK_GEMV_M
     return (int)e;
 }
 

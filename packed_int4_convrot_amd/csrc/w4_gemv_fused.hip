@@ -1,0 +1,442 @@
+// Whole W4A8/W4A4 decode linear for 1 <= M <= 4 activation rows in one launch:
+// rotate-quant of the bf16 rows and the packed-int4 GEMV, with one workgroup
+// per compute unit.
+//
+// Prior art: the fused RotateQuant operator of "[PR #155] [Feat][Ascend] Add
+// fused RotateQuant backend" ("What this PR does": the group-wise Hadamard
+// rotation and the per-row quantisation in one pass) and the register-side
+// int4 decode + v_dot4 + rowwise-scale epilogue of "[PR #182] HIP port of
+// #176: W4A8 decode GEMV and fused GatedDeltaNet decode" (description).
+//
+// Why one workgroup per CU.  A decode step is a single ~21 MB weight read, so
+// the kernel must have nearly every weight byte in flight from its first
+// microsecond.  Many small workgroups per CU do that well, but each then
+// rotates the activation rows again; with five per CU the redundant rotations
+// cost about a microsecond of VALU time per row.  Here a workgroup owns RB
+// blocks of 8 consecutive weight rows (all the rows one CU streams), each
+// wave keeps the per-wave layout of the decode GEMV on codes (wave = one
+// 2048-column slice of one 8-row block, lane = 16 packed bytes of each row,
+// so one load instruction reads 1 KiB of one row), and the rotation is
+// computed once per workgroup:
+//   1. every wave issues its activation loads (8 bf16 columns per thread and
+//      row), then its weight-scale loads, then its 8 weight-row loads;
+//   2. while the weights stream in, the workgroup rotates the M rows in
+//      8-column chunks: butterfly strides 1, 2, 4 in registers, the rest
+//      across lanes (DPP, ds_swizzle), then the row absmax (DPP within the
+//      wave, LDS across waves), then rne(y * qmax / absmax) -- the same fp32
+//      operations in the same order as the rotate-quant kernel, so the codes
+//      are bit-identical to it;
+//   3. the codes go to LDS, even and odd columns of each 32-column piece
+//      apart (the order of the nibble decode), and every lane reads its own;
+//   4. dot products (unsigned nibbles x codes, v_dot4_i32_i8, minus
+//      8 * sum(codes)), per-group scale, the transposed lane reduction and the
+//      fixed-order sum over the slices of a row block: the same operations as
+//      the GEMV on codes, so the outputs equal rotate-quant + GEMV bit for bit.
+// LDS: M * K bytes of codes; at least 80 KiB is requested whenever the grid
+// fits the chip, so that no CU receives two workgroups.
+#include "ck_device.h"
+#include "gemv_reduce.h"
+#include "launch.h"
+
+namespace ck {
+namespace {
+
+constexpr int kRows = 8;  // weight rows per wave
+
+__device__ __forceinline__ uint32_t rne_byte(float t) { return __float_as_uint(t + 12582912.0f); }
+
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
+{
+    const uint32_t p01 = perm(b1, b0, 0x0C0C0400u);
+    const uint32_t p23 = perm(b3, b2, 0x0C0C0400u);
+    return perm(p23, p01, 0x05040100u);
+}
+
+// Cross-lane butterfly on U chunks of 8 values: the lower lane of a pair keeps
+// a + b, the upper one a - b (fma(b, -1, a), one rounding).
+template <int MASK, int U>
+__device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
+{
+    const float sgn = (lane & MASK) ? -1.f : 1.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float p = __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[u][r])));
+            v[u][r] = __builtin_fmaf(v[u][r], sgn, p);
+        }
+}
+
+__device__ __forceinline__ float wave_max(float am)
+{
+    am = fmaxf(am, __uint_as_float(lane_xor_u<1>(__float_as_uint(am))));
+    am = fmaxf(am, __uint_as_float(lane_xor_u<2>(__float_as_uint(am))));
+    am = fmaxf(am, __uint_as_float(lane_mirror8_u(__float_as_uint(am))));
+    am = fmaxf(am, __uint_as_float(lane_mirror16_u(__float_as_uint(am))));
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48))));
+}
+
+// Transposed lane reduction of part[M0 .. M0 + B)[kRows] (B = 4, 2 or 1 rows),
+// then the rest; the owner lanes store the wave's sums to red[r][m].
+template <int M, bool F, int M0>
+__device__ __forceinline__ void reduce_rows(uint32_t (&part)[M][kRows], int lane, uint32_t (&red)[kRows][M])
+{
+    if constexpr (M0 < M) {
+        constexpr int left = M - M0;
+        constexpr int B = left >= 4 ? 4 : left >= 2 ? 2 : 1;
+        constexpr int V = B * kRows;
+        constexpr int kShift = V == 32 ? 1 : V == 16 ? 2 : 3;
+        uint32_t flat[V];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+                flat[b * kRows + r] = part[M0 + b][r];
+        const uint32_t t = transposed_row_sum<V, F>(flat, lane);
+        const int v = lane >> kShift;  // b * kRows + r
+        if ((lane & ((1 << kShift) - 1)) == 0)
+            red[v % kRows][M0 + v / kRows] = t;
+        reduce_rows<M, F, M0 + B>(part, lane, red);
+    }
+}
+
+// LDS of a workgroup besides the codes.
+template <int M>
+struct FusedShared {
+    uint32_t red[kFusedMaxStreamWaves][kRows][M];  // per-wave lane sums of the streaming waves
+    uint32_t amax[M];                                // row absmax (fp32 bits; non-negative, so ordered as integers)
+    uint32_t arrived;                                // rotation waves whose maxima are in amax
+    uint32_t done[kFusedMaxStreamWaves];             // slices of each row block summed into red
+};
+
+// Rotation waves: thread rt of the rstride rotation threads holds chunks
+// rt + j * rstride (j < CPR) of every row.  A G-column group is G / 8
+// consecutive chunks on neighbouring lanes of one wave (rstride and nchunk are
+// multiples of G / 8).  Barriers: the workgroup's two, in the same order as
+// the streaming waves.
+template <int M, int G, int CPR>
+__device__ __forceinline__ void rotate_role(const uint16_t *__restrict__ x, int64_t ldx, float qmax, int K,
+                                            int rt, int rstride, int nwr, int lane, uint8_t *s_codes,
+                                            FusedShared<M> &sh)
+{
+    const int nchunk = K / 8;
+    u32x4 xraw[M][CPR];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < CPR; ++j) {
+            const int c = rt + j * rstride;
+            xraw[m][j] = *reinterpret_cast<const u32x4 *>(x + (int64_t)m * ldx + 8 * (c < nchunk ? c : nchunk - 1));
+        }
+    if (rt == 0) {
+        sh.arrived = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            sh.amax[m] = 0;
+    }
+    __syncthreads();  // the counters are published
+
+    float v[M * CPR][8];
+#pragma unroll
+    for (int u = 0; u < M * CPR; ++u) {
+        const bool live = rt + (u % CPR) * rstride < nchunk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = live ? xraw[u / CPR][u % CPR][j] : 0u;
+            v[u][2 * j] = __uint_as_float(w << 16);
+            v[u][2 * j + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int h = 1; h < 8 && h < G; h <<= 1)
+#pragma unroll
+        for (int u = 0; u < M * CPR; ++u)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if ((r & h) == 0) {
+                    const float a = v[u][r], b = v[u][r + h];
+                    v[u][r] = a + b;
+                    v[u][r + h] = a - b;
+                }
+    if constexpr (G >= 16) lane_stage8<1, M * CPR>(v, lane);
+    if constexpr (G >= 32) lane_stage8<2, M * CPR>(v, lane);
+    if constexpr (G >= 64) lane_stage8<4, M * CPR>(v, lane);
+    if constexpr (G >= 128) lane_stage8<8, M * CPR>(v, lane);
+    if constexpr (G >= 256) lane_stage8<16, M * CPR>(v, lane);
+    // Row absmax over the rotation waves: LDS atomic maximum, then an arrival
+    // count that every rotation wave waits on (they are all resident in this
+    // workgroup, so the wait ends).
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPR; ++j)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                am = fmaxf(am, fabsf(v[m * CPR + j][r]));
+        am = wave_max(am);
+        if (lane == 0)
+            atomicMax(&sh.amax[m], __float_as_uint(am));
+    }
+    if (lane == 0)
+        __hip_atomic_fetch_add(&sh.arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(&sh.arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < (uint32_t)nwr)
+        __builtin_amdgcn_s_sleep(1);
+    // Quantise: rne(y * qmax / absmax), the codes of the rotate-quant kernel
+    // bit for bit.  Chunk c is columns 8 (c % 4) .. + 7 of 32-column piece
+    // c / 4: its even columns go to bytes 4 (c % 4) .. + 3 of the piece's
+    // first 16 bytes, its odd columns to the same bytes of the next 16.
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float am = __uint_as_float(sh.amax[m]);
+        const float inv = am > 0.f ? qmax / am : 0.f;
+#pragma unroll
+        for (int j = 0; j < CPR; ++j) {
+            const int c = rt + j * rstride;
+            const float(&y)[8] = v[m * CPR + j];
+            uint32_t b[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                b[r] = rne_byte(y[r] * inv);
+            if (c < nchunk) {
+                uint8_t *piece = s_codes + m * K + 32 * (c >> 2) + 4 * (c & 3);
+                *reinterpret_cast<uint32_t *>(piece) = pack4(b[0], b[2], b[4], b[6]);
+                *reinterpret_cast<uint32_t *>(piece + 16) = pack4(b[1], b[3], b[5], b[7]);
+            }
+        }
+    }
+    __syncthreads();  // the codes are in LDS
+}
+
+// Streaming waves: an 8-row block n0 .. n0 + 7 and the 2048-column slice of
+// wave % S; lane l owns columns kbase = 2048 (wave % S) + 32 l .. + 31.
+template <int M, int G, bool PER_GROUP>
+__device__ __forceinline__ void stream_role(float qmax, int K, const uint8_t *__restrict__ packed, int64_t ldw,
+                                            const uint16_t *__restrict__ w_scales, int N,
+                                            const uint16_t *__restrict__ bias, float x_scale,
+                                            uint16_t *__restrict__ out, int64_t ldo, int S, int wave, int lane,
+                                            int n0, bool has_rows, const uint8_t *s_codes, FusedShared<M> &sh)
+{
+    constexpr float kInvSqrtG = G == 16 ? 0.25f : G == 64 ? 0.125f : 0.0625f;
+    constexpr bool FSUM = PER_GROUP;  // partials are fp32 (scaled) or exact int32
+    const int kbase = 2048 * (wave % S) + 32 * lane;
+    const bool active = has_rows && kbase < K;
+    const int kc = kbase < K ? kbase : K - 32;  // every address stays inside the row
+
+    // The weight scales and the 8 weight rows go out right after the first
+    // barrier, all in flight at once.  Their issue stalls while the CU's
+    // memory pipeline is full, which is why the rotation runs in other waves.
+    // (Issuing some of them before the first barrier measured slower: the
+    // barrier, and with it the rotation, then waits for their issue.)
+    if (threadIdx.x < kFusedMaxStreamWaves)
+        sh.done[threadIdx.x] = 0;
+    __syncthreads();  // the counters are published
+    u32x4 sv = {0u, 0u, 0u, 0u};
+    if constexpr (PER_GROUP)
+        sv = *reinterpret_cast<const u32x4 *>(w_scales + (int64_t)(kc / 64) * N + n0);
+    u32x4 wv[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+        wv[r] = load_nt16(packed + (int64_t)(n0 + r) * ldw + kc / 2);
+    __syncthreads();  // the codes are in LDS
+
+    // Every path below uses the weights (waves without rows compute on rows
+    // 0 .. 7 and drop the result), so the compiler cannot sink the loads
+    // into a conditional block after the barriers.
+    // This lane's codes: even columns in alo, odd ones in ahi.
+    uint32_t alo[M][4], ahi[M][4];
+    int asum8[M];  // 8 * sum of the lane's codes (the code - 8 offset)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const u32x4 e = active ? *reinterpret_cast<const u32x4 *>(s_codes + m * K + kbase) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 o = active ? *reinterpret_cast<const u32x4 *>(s_codes + m * K + kbase + 16)
+                               : u32x4{0u, 0u, 0u, 0u};
+        int s = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            alo[m][i] = e[i];
+            ahi[m][i] = o[i];
+            s = __builtin_amdgcn_sdot4((int)alo[m][i], 0x01010101, s, false);
+            s = __builtin_amdgcn_sdot4((int)ahi[m][i], 0x01010101, s, false);
+        }
+        asum8[m] = 8 * s;
+    }
+
+    // Dot products, one partial per (activation row, weight row) and lane.
+    uint32_t part[M][kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = wv[r][i] & 0x0f0f0f0fu;
+            hi[i] = (wv[r][i] >> 4) & 0x0f0f0f0fu;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            int acc = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = __builtin_amdgcn_sdot4((int)lo[i], (int)alo[m][i], acc, false);
+                acc = __builtin_amdgcn_sdot4((int)hi[i], (int)ahi[m][i], acc, false);
+            }
+            acc -= asum8[m];
+            if constexpr (FSUM)
+                part[m][r] = __float_as_uint(
+                    __uint_as_float(r % 2 ? sv[r / 2] & 0xffff0000u : sv[r / 2] << 16) * (float)acc);
+            else
+                part[m][r] = (uint32_t)acc;
+        }
+    }
+
+    // Sum over the lanes of the wave, then over the S slices of the row
+    // block: the last slice to finish sums them in slice order and writes the
+    // outputs.
+    reduce_rows<M, FSUM, 0>(part, lane, sh.red[wave]);
+    if (!has_rows)
+        return;
+    const int rbl = wave / S;
+    uint32_t prior = 0;
+    if (lane == 0)
+        prior = __hip_atomic_fetch_add(&sh.done[rbl], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(prior) != (uint32_t)(S - 1))
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (lane < kRows * M) {
+        const int r = lane / M, m = lane % M;
+        const int n = n0 + r;
+        uint32_t t = sh.red[rbl * S][r][m];
+        for (int k = 1; k < S; ++k)
+            t = add32<FSUM>(t, sh.red[rbl * S + k][r][m]);
+        const float am = __uint_as_float(sh.amax[m]);
+        const float sx = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;
+        float y = FSUM ? __uint_as_float(t) : bf16_to_f32(w_scales[n]) * (float)(int32_t)t;
+        y *= sx * x_scale;
+        if (bias)
+            y += bf16_to_f32(bias[n]);
+        out[(int64_t)m * ldo + n] = f32_to_bf16(y);
+    }
+}
+
+// CPR: 8-column rotation chunks per rotation thread and row.  Workgroup
+// (blockDim.x = 64 * (NWS + nwr)): streaming wave w < NWS serves row block
+// lb * RB + w / S, columns [2048 (w % S), 2048 (w % S) + 2048); the nwr
+// rotation waves after them rotate and quantise the M rows.  Every wave meets
+// the same two barriers.
+template <int M, int G, bool PER_GROUP, int CPR>
+__global__ __launch_bounds__(1024) void w4_gemv_fused_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, float qmax, int K, const uint8_t *__restrict__ packed,
+    int64_t ldw, const uint16_t *__restrict__ w_scales, int N, const uint16_t *__restrict__ bias,
+    float x_scale, uint16_t *__restrict__ out, int64_t ldo, int S, int RB, int NWS)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_codes[];  // [M][K]
+    __shared__ FusedShared<M> sh;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (wave >= NWS) {
+        const int nwr = (int)blockDim.x / kWave - NWS;
+        rotate_role<M, G, CPR>(x, ldx, qmax, K, (int)threadIdx.x - kWave * NWS, kWave * nwr, nwr, lane, s_codes,
+                               sh);
+    } else {
+        const int rb = xcd_block(blockIdx.x, gridDim.x) * RB + wave / S;
+        const bool has_rows = rb < N / kRows;
+        // a wave past the last row block loads (and drops) rows 0 .. 7
+        stream_role<M, G, PER_GROUP>(qmax, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, S, wave, lane,
+                                     has_rows ? rb * kRows : 0, has_rows, s_codes, sh);
+    }
+}
+
+// Compute units of the current device, looked up once per device.
+int cu_count()
+{
+    static int counts[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (counts[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        counts[dev] = n;
+    }
+    return counts[dev];
+}
+
+template <int M, int G, bool PG, int CPR>
+hipError_t launch_k(const FusedGemvShape &sh, const uint16_t *x, int64_t ldx, float qmax, int K,
+                    const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N, const uint16_t *bias,
+                    float xs, uint16_t *out, int64_t ldo, hipStream_t s)
+{
+    // Only the shapes w4_gemv_fused_shape() allows are instantiated.
+    if constexpr (M * CPR > kFusedMaxChunks) {
+        return hipErrorInvalidValue;
+    } else {
+        auto kern = w4_gemv_fused_kernel<M, G, PG, CPR>;
+        // The largest request of any shape: M * K codes, or just over 80 KiB.
+        constexpr int kMaxLds = M * 2048 * kGemvMaxWaves > 81 * 1024 ? M * 2048 * kGemvMaxWaves : 81 * 1024;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (attr != hipSuccess)
+            return attr;
+        hipLaunchKernelGGL(kern, dim3((unsigned)sh.nb), dim3((unsigned)((sh.nws + sh.nwr) * kWave)),
+                           (size_t)sh.lds, s, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, sh.s,
+                           sh.rb, sh.nws);
+        return hipGetLastError();
+    }
+}
+
+template <int M, int G, bool PG>
+hipError_t launch_mg(const FusedGemvShape &sh, const uint16_t *x, int64_t ldx, float qmax, int K,
+                     const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N, const uint16_t *bias,
+                     float xs, uint16_t *out, int64_t ldo, hipStream_t s)
+{
+    switch (sh.cpr) {
+    case 1: return launch_k<M, G, PG, 1>(sh, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, s);
+    case 2: return launch_k<M, G, PG, 2>(sh, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, s);
+    case 4: return launch_k<M, G, PG, 4>(sh, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, s);
+    case 8: return launch_k<M, G, PG, 8>(sh, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int M>
+hipError_t launch_m(const FusedGemvShape &sh, int G, bool pg, const uint16_t *x, int64_t ldx, float qmax, int K,
+                    const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N, const uint16_t *bias,
+                    float xs, uint16_t *out, int64_t ldo, hipStream_t s)
+{
+#define CK_FG_G(GG)                                                                                              \
+    return pg ? launch_mg<M, GG, true>(sh, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, s)          \
+              : launch_mg<M, GG, false>(sh, x, ldx, qmax, K, packed, ldw, ws, N, bias, xs, out, ldo, s);
+    switch (G) {
+    case 16: CK_FG_G(16)
+    case 64: CK_FG_G(64)
+    case 256: CK_FG_G(256)
+    default: return hipErrorInvalidValue;
+    }
+#undef CK_FG_G
+}
+
+}  // namespace
+
+int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M, int K, const uint8_t *packed,
+                         int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
+                         float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    FusedGemvShape sh;
+    if (!w4_gemv_fused_shape(M, K, N, cu_count(), sh))
+        return (int)hipErrorInvalidValue;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const float q = (float)qmax;
+    switch (M) {
+    case 1: return (int)launch_m<1>(sh, G, per_group, x, ldx, q, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, s);
+    case 2: return (int)launch_m<2>(sh, G, per_group, x, ldx, q, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, s);
+    case 3: return (int)launch_m<3>(sh, G, per_group, x, ldx, q, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, s);
+    case 4: return (int)launch_m<4>(sh, G, per_group, x, ldx, q, K, packed, ldw, w_scales, N, bias, x_scale, out, ldo, s);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ck

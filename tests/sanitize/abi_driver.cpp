@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <limits>
 #include <vector>
 
@@ -348,7 +349,7 @@ void test_linear()
         int64_t M, K;
         int G;
     };
-    const Case cases[] = {{1, 3840, 64}, {2, 3840, 16}, {4, 10240, 256}, {8, 3840, 64},
+    const Case cases[] = {{1, 3840, 64}, {2, 3840, 16}, {3, 16384, 64}, {4, 8192, 256}, {4, 10240, 256}, {8, 3840, 64},
                           {32, 3840, 64}, {64, 1024, 16}, {65, 3840, 256}, {300, 640, 64}};
     for (const Case &c : cases) {
         for (int bits : {8, 4}) {
@@ -364,9 +365,9 @@ void test_linear()
             EXPECT(lin(x, c.M, c.K, ldx, c.G, w.packed, w.ldw, w.scales, 1, 64, N, nullptr, 0.5f, out, ldo, ws,
                        need, nullptr) == CK_OK);
             const stub::Kernel mm = expected_kernel(c.M, c.K);
-            if (c.M <= 2) {
+            if (ck::w4_gemv_fused_supports(c.M, c.K)) {
                 // Decode: one fused launch rotates, quantises and multiplies.
-                EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kGemv);
+                EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kGemvFused);
                 EXPECT(stub::last.G == c.G && stub::last.x == x && stub::last.qmax == (bits == 8 ? 127 : 7));
                 EXPECT(stub::last.x_scale == 0.5f);
                 continue;
@@ -386,6 +387,45 @@ void test_linear()
             EXPECT(g.ldq == rq.ldq && g.x_scale == 0.5f && g.out == out);
         }
     }
+}
+
+// Workgroup shapes of the one-launch decode linear: for every M, K, N and CU
+// count, the row blocks are covered exactly once by the streaming waves, the
+// rotation threads cover every 8-column chunk with a chunk count the kernel is
+// instantiated for, the LDS holds the codes, and whether a shape exists
+// depends on M and K alone (the linear decides before it knows the device).
+void test_fused_gemv_shapes()
+{
+    for (int64_t M = 1; M <= 5; ++M)
+        for (int64_t K = 64; K <= 16384 + 64; K += 64)
+            for (int64_t N : {8, 16, 264, 3840, 10240, 18432, 65536})
+                for (int ncu : {1, 80, 256, 304}) {
+                    ck::FusedGemvShape sh;
+                    const bool ok = ck::w4_gemv_fused_shape(M, K, N, ncu, sh);
+                    EXPECT(ok == ck::w4_gemv_fused_supports(M, K));
+                    // with one row block per workgroup: M * cpr <= 8 chunks of 8 per rotation thread
+                    const int64_t s = (K + 2047) / 2048, nch = K / 8;
+                    const int64_t nwr1 = std::min<int64_t>((16 - s) / 4 * 4, (nch + 63) / 64);
+                    const int64_t c1 = (nch + 64 * nwr1 - 1) / (64 * nwr1);
+                    const int64_t cpr1 = c1 <= 1 ? 1 : c1 <= 2 ? 2 : c1 <= 4 ? 4 : 8;
+                    EXPECT(ok == (M <= 4 && K <= 16384 && M * cpr1 <= 8));
+                    if (!ok)
+                        continue;
+                    const int64_t nrb = N / 8;
+                    EXPECT(sh.s == s && sh.rb >= 1 && sh.nws == sh.rb * sh.s && sh.nws <= 12);
+                    EXPECT((int64_t)sh.nb * sh.rb >= nrb && (int64_t)(sh.nb - 1) * sh.rb < nrb);
+                    EXPECT(sh.nwr >= 1 && sh.nws + sh.nwr <= 16 && (sh.nwr % 4 == 0 || sh.nwr * 64 >= nch));
+                    EXPECT(sh.cpr == 1 || sh.cpr == 2 || sh.cpr == 4 || sh.cpr == 8);
+                    EXPECT((int64_t)sh.cpr * 64 * sh.nwr >= nch && M * sh.cpr <= ck::kFusedMaxChunks);
+                    EXPECT(sh.lds >= M * K && sh.lds <= 160 * 1024);
+                    EXPECT(sh.nb > ncu || sh.lds > 80 * 1024);
+                }
+    // The decode workloads: M = 1 .. 4 at K = 3840 fuse, with five 8-row blocks
+    // per workgroup on 256 CUs at N = 10240.
+    ck::FusedGemvShape sh;
+    EXPECT(ck::w4_gemv_fused_shape(1, 3840, 10240, 256, sh) && sh.nb == 256 && sh.rb == 5 && sh.nwr == 4);
+    EXPECT(ck::w4_gemv_fused_supports(4, 3840) && ck::w4_gemv_fused_supports(2, 16384));
+    EXPECT(!ck::w4_gemv_fused_supports(3, 16384) && !ck::w4_gemv_fused_supports(5, 64));
 }
 
 void test_linear_invalid()
@@ -454,8 +494,8 @@ void test_noalloc()
             continue;
         }
         EXPECT(st == CK_OK);
-        if (c.M <= 2) {
-            EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kGemv && stub::last.G == 64);
+        if (ck::w4_gemv_fused_supports(c.M, c.K)) {
+            EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kGemvFused && stub::last.G == 64);
             continue;
         }
         EXPECT(stub::calls == 2);
@@ -532,6 +572,7 @@ int main()
     test_gemm_invalid();
     test_gemm_packed();
     test_linear();
+    test_fused_gemv_shapes();
     test_linear_invalid();
     test_noalloc();
     test_w4a16();

@@ -151,25 +151,37 @@ int launch_quantize_weights(const uint16_t *w, int64_t N, int K, int64_t ldw_in,
     return finish(c);
 }
 
-int launch_w4_gemv(const uint16_t *x, int64_t ldx, int G, int qmax, const int8_t *codes, int64_t ldq,
-                   const float *row_scales, int M, int K, const uint8_t *packed, int64_t ldw,
-                   const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias, float x_scale,
-                   uint16_t *out, int64_t ldo, int32_t *acc_out, int64_t lda, void *stream)
+int launch_w4_gemv(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
+                   const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group, int N,
+                   const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo, int32_t *acc_out,
+                   int64_t lda, void *stream)
 {
     using namespace stub;
-    if (G != 0) {
-        read_rows(x, M, 2 * (int64_t)K, 2 * ldx);
-        touch_matmul(nullptr, 0, nullptr, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo, acc_out,
-                     lda, false);
-    } else {
-        touch_matmul(codes, ldq, row_scales, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo,
-                     acc_out, lda, false);
-    }
+    touch_matmul(codes, ldq, row_scales, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo, acc_out,
+                 lda, false);
     Call c{};
     c.kernel = Kernel::kGemv;
-    c.M = M, c.K = K, c.N = N, c.G = G, c.qmax = qmax, c.ldq = ldq, c.per_group = per_group;
-    c.x_scale = x_scale, c.x = x, c.codes = codes, c.row_scales = row_scales, c.out = out, c.acc = acc_out;
+    c.M = M, c.K = K, c.N = N, c.ldq = ldq, c.per_group = per_group;
+    c.x_scale = x_scale, c.codes = codes, c.row_scales = row_scales, c.out = out, c.acc = acc_out;
     c.stream = stream;
+    return finish(c);
+}
+
+int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M, int K, const uint8_t *packed,
+                         int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
+                         float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    using namespace stub;
+    FusedGemvShape sh;
+    if (!w4_gemv_fused_shape(M, K, N, 256, sh))
+        return 1;  // hipErrorInvalidValue
+    read_rows(x, M, 2 * (int64_t)K, 2 * ldx);
+    touch_matmul(nullptr, 0, nullptr, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo, nullptr, 0,
+                 false);
+    Call c{};
+    c.kernel = Kernel::kGemvFused;
+    c.M = M, c.K = K, c.N = N, c.G = G, c.qmax = qmax, c.per_group = per_group;
+    c.x_scale = x_scale, c.x = x, c.out = out, c.stream = stream;
     return finish(c);
 }
 

@@ -367,22 +367,33 @@ def test_linear_end_to_end(M, G, per_group, bits):
         assert np.array_equal(out[1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
 
 
-@pytest.mark.parametrize("M,K", [(1, 3840), (2, 3840), (1, 256), (2, 256), (1, 2304), (2, 2304), (1, 8192),
-                                 (2, 16384)])
+FUSED_CASES = [(1, 3840), (2, 3840), (3, 3840), (4, 3840), (1, 64), (4, 64), (2, 256), (3, 2112), (1, 8192),
+               (4, 8192), (1, 16384), (2, 16384), (3, 16384)]
+
+
+@pytest.mark.parametrize("M,K", FUSED_CASES)
 @pytest.mark.parametrize("G", [16, 64, 256])
 def test_fused_decode_linear_equals_two_step_path(M, K, G):
-    """The one-launch decode linear (rotate-quant inside the GEMV, one or two rows)
-    gives bit-identical outputs to ck_rotate_quant followed by ck_w4_gemv: one wave
-    with 8 active lanes, a partial second wave, four and eight waves."""
-    N = 1024
-    for per_group in (True, False):
-        inp = workloads.linear_inputs(M, K, N, seed=G + M, outliers=8, scale="group" if per_group else "channel",
-                                      with_bias=True)
-        xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
-        fused = ck.linear(xd, G, 8, wd, sd, per_group, bias=bd)
-        codes, scales = ck.rotate_quant(xd, G, 8)
-        two = ck.gemv(codes, scales, wd, sd, per_group, bias=bd)
-        assert torch.equal(fused, two)
+    """The one-launch decode linear (rotate-quant and GEMV in one workgroup per CU,
+    one to four rows) gives bit-identical outputs to ck_rotate_quant followed by
+    ck_w4_gemv, for both bit widths and scale kinds, with a zero row and an input
+    scale: one K slice with 2 active lanes, partial and full slices, up to eight
+    slices; N = 1024 (one 8-row block per workgroup), 4112 (three per workgroup,
+    the last workgroup partly empty) and 10240 (five)."""
+    if K % G:
+        pytest.skip("K must be a multiple of G")
+    for N in (1024, 4112, 10240):
+        for bits in (8, 4):
+            for per_group in (True, False):
+                inp = workloads.linear_inputs(M, K, N, seed=G + M + bits, outliers=min(8, K // 8),
+                                              scale="group" if per_group else "channel",
+                                              zero_rows=(1,) if M > 1 else (), with_bias=True)
+                xd, wd = bf16_dev(inp["x"]), u8_dev(inp["packed"])
+                sd, bd = bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+                fused = ck.linear(xd, G, bits, wd, sd, per_group, bias=bd, x_scale=0.3)
+                codes, scales = ck.rotate_quant(xd, G, bits)
+                two = ck.gemv(codes, scales * np.float32(0.3), wd, sd, per_group, bias=bd)
+                assert torch.equal(fused, two), (N, bits, per_group)
 
 
 @pytest.mark.parametrize("G", [16, 64, 256])
