@@ -106,6 +106,10 @@ int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M,
                          int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
                          float x_scale, uint16_t *out, int64_t ldo, void *stream);
 
+// Compute units of the current device (looked up once per device; 256 if the
+// query fails).
+int device_cu_count();
+
 // Skinny path: M <= 64, weights streamed once, activations held in registers.
 // acc_out != nullptr selects the int32 test epilogue.
 // codes: row-major int8 [M, ldq], or (tiled, ldq ignored) the kTiled16 layout.

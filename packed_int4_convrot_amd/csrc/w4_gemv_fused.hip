@@ -349,22 +349,6 @@ __global__ __launch_bounds__(1024) void w4_gemv_fused_kernel(
     }
 }
 
-// Compute units of the current device, looked up once per device.
-int cu_count()
-{
-    static int counts[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (counts[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        counts[dev] = n;
-    }
-    return counts[dev];
-}
-
 template <int M, int G, bool PG, int CPR>
 hipError_t launch_k(const FusedGemvShape &sh, const uint16_t *x, int64_t ldx, float qmax, int K,
                     const uint8_t *packed, int64_t ldw, const uint16_t *ws, int N, const uint16_t *bias,
@@ -421,12 +405,27 @@ hipError_t launch_m(const FusedGemvShape &sh, int G, bool pg, const uint16_t *x,
 
 }  // namespace
 
+int device_cu_count()
+{
+    static int counts[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (counts[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        counts[dev] = n;
+    }
+    return counts[dev];
+}
+
 int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M, int K, const uint8_t *packed,
                          int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
                          float x_scale, uint16_t *out, int64_t ldo, void *stream)
 {
     FusedGemvShape sh;
-    if (!w4_gemv_fused_shape(M, K, N, cu_count(), sh))
+    if (!w4_gemv_fused_shape(M, K, N, device_cu_count(), sh))
         return (int)hipErrorInvalidValue;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const float q = (float)qmax;

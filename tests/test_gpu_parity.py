@@ -145,6 +145,8 @@ def _rand_codes(M, K, qmax, seed):
     # with masked weight-slice lanes, and the widest (8-wave) slice set
     (40, 2048, 48), (20, 3840, 64), (12, 8192, 32), (9, 192, 16), (17, 4096, 16),
     (20, 6144, 32), (50, 1024, 64), (64, 3840, 16),
+    # more 16-row tiles than CUs (the grid runs in several rounds)
+    (8, 1024, 4112), (6, 3840, 10240), (16, 512, 10240), (33, 1024, 8192), (64, 512, 16384),
 ])
 @pytest.mark.parametrize("qmax", [127, 7])
 def test_accumulators_bit_exact(M, K, N, qmax):
@@ -330,6 +332,27 @@ def test_gemm_q_outputs(M, per_group):
                     bias=None if inp["bias"] is None else bf16_dev(inp["bias"]))
     ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
     assert_output_close(host(out), ref)
+
+
+@pytest.mark.parametrize("per_group", [True, False])
+@pytest.mark.parametrize("M,N", [(8, 4112), (33, 10240)])
+def test_gemm_q_outputs_more_tiles_than_cus(M, N, per_group):
+    """Few-row kernel with more 16-row tiles than CUs (257 and 640 workgroups), with
+    per-group and per-channel scales and a bias, against the oracle; the whole linear
+    (codes in the kernel's tiled layout) equals rotate-quant + gemm_q bit for bit."""
+    K = 1024
+    inp = workloads.linear_inputs(M, K, N, seed=M + N, outliers=9, scale="group" if per_group else "channel",
+                                  zero_rows=(1,), with_bias=True)
+    codes, scales = oracle.rotate_quant(inp["x"], 64, 8)
+    out = ck.gemm_q(i8_dev(codes), torch.from_numpy(scales).to(DEV), u8_dev(inp["packed"]),
+                    bf16_dev(inp["w_scales"]), per_group, bias=bf16_dev(inp["bias"]))
+    ref = oracle.gemm_q(codes, scales, inp["packed"], inp["w_scales"], per_group, bias=inp["bias"])
+    assert_output_close(host(out), ref)
+    lin = ck.linear(bf16_dev(inp["x"]), 64, 8, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), per_group,
+                    bias=bf16_dev(inp["bias"]))
+    c2, s2 = ck.rotate_quant(bf16_dev(inp["x"]), 64, 8)
+    two = ck.gemm_q(c2, s2, u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), per_group, bias=bf16_dev(inp["bias"]))
+    assert torch.equal(lin, two)
 
 
 @pytest.mark.parametrize("per_group", [True, False])
