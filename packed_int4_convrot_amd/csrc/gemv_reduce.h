@@ -86,4 +86,29 @@ __device__ __forceinline__ uint32_t transposed_row_sum(uint32_t (&p)[R], int lan
     return v;
 }
 
+// Transposed lane reduction of part[M0 .. M0 + B)[R] (B = 4, 2 or 1 rows, as
+// many as fit in 32 values), then the rest; the owner lanes store the wave's
+// sums to red[r][m].
+template <int M, int R, bool F, int M0>
+__device__ __forceinline__ void reduce_rows(uint32_t (&part)[M][R], int lane, uint32_t (&red)[R][M])
+{
+    if constexpr (M0 < M) {
+        constexpr int left = M - M0;
+        constexpr int B = (R == 8 && left >= 4) ? 4 : (R <= 16 && left >= 2 && 2 * R <= 32) ? 2 : 1;
+        constexpr int V = B * R;
+        constexpr int kShift = V == 32 ? 1 : V == 16 ? 2 : 3;
+        uint32_t flat[V];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                flat[b * R + r] = part[M0 + b][r];
+        const uint32_t t = transposed_row_sum<V, F>(flat, lane);
+        const int v = lane >> kShift;  // b * R + r
+        if ((lane & ((1 << kShift) - 1)) == 0)
+            red[v % R][M0 + v / R] = t;
+        reduce_rows<M, R, F, M0 + B>(part, lane, red);
+    }
+}
+
 }  // namespace ck

@@ -31,31 +31,6 @@ constexpr int kMaxWaves = kGemvMaxWaves;  // K <= 16384
 #ifndef CK_GEMV_ROWS
 #define CK_GEMV_ROWS 8  // weight rows per block (8, 16 or 32)
 #endif
-// Transposed lane reduction of part[M0 .. M0 + B)[R] (B = 4, 2 or 1 rows, as
-// many as fit in 32 values), then the rest; the owner lanes store the wave's
-// sums to red[r][m].
-template <int M, int R, bool F, int M0>
-__device__ __forceinline__ void reduce_rows(uint32_t (&part)[M][R], int lane, uint32_t (&red)[R][M])
-{
-    if constexpr (M0 < M) {
-        constexpr int left = M - M0;
-        constexpr int B = (R == 8 && left >= 4) ? 4 : (R <= 16 && left >= 2 && 2 * R <= 32) ? 2 : 1;
-        constexpr int V = B * R;
-        constexpr int kShift = V == 32 ? 1 : V == 16 ? 2 : 3;
-        uint32_t flat[V];
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                flat[b * R + r] = part[M0 + b][r];
-        const uint32_t t = transposed_row_sum<V, F>(flat, lane);
-        const int v = lane >> kShift;  // b * R + r
-        if ((lane & ((1 << kShift) - 1)) == 0)
-            red[v % R][M0 + v / R] = t;
-        reduce_rows<M, R, F, M0 + B>(part, lane, red);
-    }
-}
-
 template <int M, int R, bool PER_GROUP, bool OUT_I32>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
     const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int K,

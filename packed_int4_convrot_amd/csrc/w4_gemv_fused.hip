@@ -11,28 +11,34 @@
 // Why one workgroup per CU.  A decode step is a single ~21 MB weight read, so
 // the kernel must have nearly every weight byte in flight from its first
 // microsecond.  Many small workgroups per CU do that well, but each then
-// rotates the activation rows again; with five per CU the redundant rotations
-// cost about a microsecond of VALU time per row.  Here a workgroup owns RB
-// blocks of 8 consecutive weight rows (all the rows one CU streams), each
-// wave keeps the per-wave layout of the decode GEMV on codes (wave = one
-// 2048-column slice of one 8-row block, lane = 16 packed bytes of each row,
-// so one load instruction reads 1 KiB of one row), and the rotation is
-// computed once per workgroup:
-//   1. every wave issues its activation loads (8 bf16 columns per thread and
-//      row), then its weight-scale loads, then its 8 weight-row loads;
-//   2. while the weights stream in, the workgroup rotates the M rows in
-//      8-column chunks: butterfly strides 1, 2, 4 in registers, the rest
-//      across lanes (DPP, ds_swizzle), then the row absmax (DPP within the
-//      wave, LDS across waves), then rne(y * qmax / absmax) -- the same fp32
-//      operations in the same order as the rotate-quant kernel, so the codes
-//      are bit-identical to it;
-//   3. the codes go to LDS, even and odd columns of each 32-column piece
-//      apart (the order of the nibble decode), and every lane reads its own;
-//   4. dot products (unsigned nibbles x codes, v_dot4_i32_i8, minus
-//      8 * sum(codes)), per-group scale, the transposed lane reduction and the
-//      fixed-order sum over the slices of a row block: the same operations as
-//      the GEMV on codes, so the outputs equal rotate-quant + GEMV bit for bit.
-// LDS: M * K bytes of codes; at least 80 KiB is requested whenever the grid
+// rotates the activation rows again (five times per CU for the GEMV on codes'
+// 1280 workgroups).  Here a workgroup owns RB blocks of 8 consecutive weight
+// rows (all the rows one CU streams) and rotates the rows once.
+//
+// Two kinds of waves:
+//   * streaming waves keep the per-wave layout of the GEMV on codes (wave =
+//     one 2048-column slice of one 8-row block, lane = 16 packed bytes of
+//     each row, so one load instruction reads 1 KiB of one row).  They issue
+//     all their weight loads at once, which stalls their issue while the
+//     CU's memory pipeline is full (1.6 us median at the decode workload);
+//   * rotation waves (a multiple of 4, one per SIMD each) load the bf16 rows
+//     first, rotate them in 8-column chunks (butterfly strides 1, 2, 4 in
+//     registers, the rest across lanes), take the row absmax (DPP within a
+//     wave, an LDS atomic maximum and arrival count across the rotation
+//     waves), quantise with rne(y * qmax / absmax) -- the same fp32
+//     operations in the same order as the rotate-quant kernel, so the codes
+//     are bit-identical to it -- and write the codes to LDS, even and odd
+//     columns of each 32-column piece apart (the order of the nibble decode).
+// Two barriers: the first publishes the LDS counters (after the rotation
+// waves' activation loads, before any weight load); the second hands the
+// codes to the streaming waves.  Each streaming wave then forms dot products
+// (unsigned nibbles x codes, v_dot4_i32_i8, minus 8 * sum(codes)), applies
+// the per-group scale and sums over its lanes by the transposed reduction;
+// the last of the S slices of a row block to finish (an LDS arrival count)
+// sums the slices in slice order and writes the outputs.  These are the
+// operations of the GEMV on codes, so the outputs equal rotate-quant + GEMV
+// bit for bit.
+// LDS: M * K bytes of codes; just over 80 KiB is requested whenever the grid
 // fits the chip, so that no CU receives two workgroups.
 #include "ck_device.h"
 #include "gemv_reduce.h"
@@ -77,30 +83,6 @@ __device__ __forceinline__ float wave_max(float am)
                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16))),
                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32)),
                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48))));
-}
-
-// Transposed lane reduction of part[M0 .. M0 + B)[kRows] (B = 4, 2 or 1 rows),
-// then the rest; the owner lanes store the wave's sums to red[r][m].
-template <int M, bool F, int M0>
-__device__ __forceinline__ void reduce_rows(uint32_t (&part)[M][kRows], int lane, uint32_t (&red)[kRows][M])
-{
-    if constexpr (M0 < M) {
-        constexpr int left = M - M0;
-        constexpr int B = left >= 4 ? 4 : left >= 2 ? 2 : 1;
-        constexpr int V = B * kRows;
-        constexpr int kShift = V == 32 ? 1 : V == 16 ? 2 : 3;
-        uint32_t flat[V];
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-            for (int r = 0; r < kRows; ++r)
-                flat[b * kRows + r] = part[M0 + b][r];
-        const uint32_t t = transposed_row_sum<V, F>(flat, lane);
-        const int v = lane >> kShift;  // b * kRows + r
-        if ((lane & ((1 << kShift) - 1)) == 0)
-            red[v % kRows][M0 + v / kRows] = t;
-        reduce_rows<M, F, M0 + B>(part, lane, red);
-    }
 }
 
 // LDS of a workgroup besides the codes.
@@ -296,7 +278,7 @@ __device__ __forceinline__ void stream_role(float qmax, int K, const uint8_t *__
     // Sum over the lanes of the wave, then over the S slices of the row
     // block: the last slice to finish sums them in slice order and writes the
     // outputs.
-    reduce_rows<M, FSUM, 0>(part, lane, sh.red[wave]);
+    reduce_rows<M, kRows, FSUM, 0>(part, lane, sh.red[wave]);
     if (!has_rows)
         return;
     const int rbl = wave / S;
