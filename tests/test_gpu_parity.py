@@ -461,7 +461,7 @@ def test_fused_decode_linear_strided_input_ignores_padding():
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("M", [1, 8, 300])
+@pytest.mark.parametrize("M", [1, 3, 8, 300])
 def test_graph_replay_matches_eager(M):
     """Captured into a HIP graph, the linear gives the eager result on every replay."""
     K, N = 1024, 272
