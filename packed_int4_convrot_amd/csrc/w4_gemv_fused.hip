@@ -40,6 +40,8 @@
 // bit for bit.
 // LDS: M * K bytes of codes; just over 80 KiB is requested whenever the grid
 // fits the chip, so that no CU receives two workgroups.
+#include <mutex>
+
 #include "ck_device.h"
 #include "gemv_reduce.h"
 #include "launch.h"
@@ -389,16 +391,18 @@ hipError_t launch_m(const FusedGemvShape &sh, int G, bool pg, const uint16_t *x,
 
 int device_cu_count()
 {
-    static int counts[64] = {0};
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static int counts[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return 256;
-    if (counts[dev] == 0) {
+    std::call_once(once[dev], [dev] {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
         counts[dev] = n;
-    }
+    });
     return counts[dev];
 }
 
