@@ -401,11 +401,12 @@ def test_fused_decode_linear_equals_two_step_path(M, K, G):
     one to four rows) gives bit-identical outputs to ck_rotate_quant followed by
     ck_w4_gemv, for both bit widths and scale kinds, with a zero row and an input
     scale: one K slice with 2 active lanes, partial and full slices, up to eight
-    slices; N = 1024 (one 8-row block per workgroup), 4112 (three per workgroup,
-    the last workgroup partly empty) and 10240 (five)."""
+    slices; N = 16 and 48 (two and six workgroups), 1024 (one 8-row block per
+    workgroup), 4112 (three per workgroup, the last workgroup partly empty) and
+    10240 (five)."""
     if K % G:
         pytest.skip("K must be a multiple of G")
-    for N in (1024, 4112, 10240):
+    for N in (16, 48, 1024, 4112, 10240):
         for bits in (8, 4):
             for per_group in (True, False):
                 inp = workloads.linear_inputs(M, K, N, seed=G + M + bits, outliers=min(8, K // 8),
