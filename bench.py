@@ -165,6 +165,14 @@ PROFILE_WORKLOADS = {
     "awq_w4a16_gemv_m1_k3072_n18432": dict(
         kernel="w4a16_gemv_kernel", M=1, K=3072, N=18432, mops=None,
         alg_bytes=18432 * 3072 // 2 + 2 * 2 * 48 * 18432 + 3072 * 2 + 18432 * 2),
+    # The one-launch decode linear at M = 1 (the headline step), M = 4: packed
+    # weights, group scales, bf16 x, bf16 output.
+    "w4a8_decode_linear_m1_k3840_n10240_g64": dict(
+        kernel="w4_gemv_fused_kernel", M=1, K=3840, N=10240, mops=None,
+        alg_bytes=10240 * 3840 // 2 + 60 * 10240 * 2 + 1 * 3840 * 2 + 1 * 10240 * 2),
+    "w4a8_decode_linear_m4_k3840_n10240_g64": dict(
+        kernel="w4_gemv_fused_kernel", M=4, K=3840, N=10240, mops=None,
+        alg_bytes=10240 * 3840 // 2 + 60 * 10240 * 2 + 4 * 3840 * 2 + 4 * 10240 * 2),
     # The matmul half of the M = 32 W4A8 linear: packed weights, group scales, the
     # tiled codes and row scales, the bf16 output.
     "w4a8_skinny_m32_k3840_n3840_g64": dict(
@@ -179,6 +187,8 @@ KERNEL_SOURCES = {
     "w4a16_gemv_kernel": ["packed_int4_convrot_amd/csrc/w4a16_gemv.hip",
                           "packed_int4_convrot_amd/csrc/gemv_reduce.h"] + _COMMON,
     "w4_skinny_kernel": ["packed_int4_convrot_amd/csrc/w4_skinny.hip"] + _COMMON,
+    "w4_gemv_fused_kernel": ["packed_int4_convrot_amd/csrc/w4_gemv_fused.hip",
+                             "packed_int4_convrot_amd/csrc/gemv_reduce.h"] + _COMMON,
 }
 
 
@@ -222,6 +232,19 @@ def profile_workload(name, reps=5):
         scl = bf16(inp["w_scales"])
         out = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device=dev)
         work = torch.empty((ck.workspace_bytes(w["M"], w["K"], w["N"]),), dtype=torch.uint8, device=dev)
+
+        def fn():
+            ck.linear(x, w["G"], 8, packed, scl, True, out=out, workspace=work)
+    elif name.startswith("w4a8_decode_linear"):
+        wl = "w4a8_decode_gemv_k3840_n10240_g64"
+        w = workloads.WORKLOADS[wl]
+        M = PROFILE_WORKLOADS[name]["M"]
+        inp = workloads.workload_inputs(wl, M=M)
+        x = bf16(inp["x"])
+        packed = torch.from_numpy(inp["packed"]).to(dev)
+        scl = bf16(inp["w_scales"])
+        out = torch.empty((M, w["N"]), dtype=torch.bfloat16, device=dev)
+        work = torch.empty((ck.workspace_bytes(M, w["K"], w["N"]),), dtype=torch.uint8, device=dev)
 
         def fn():
             ck.linear(x, w["G"], 8, packed, scl, True, out=out, workspace=work)
