@@ -116,13 +116,12 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
         }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            int acc = 0;
+            int acc = -asum8[m];  // the code - 8 offset, subtracted up front
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc = __builtin_amdgcn_sdot4((int)lo[i], (int)alo[m][i], acc, false);
                 acc = __builtin_amdgcn_sdot4((int)hi[i], (int)ahi[m][i], acc, false);
             }
-            acc -= asum8[m];
             if constexpr (FSUM)
                 part[m][r] = __float_as_uint(__uint_as_float(r % 2 ? sv[r / 8][(r % 8) / 2] & 0xffff0000u
                                                                    : sv[r / 8][(r % 8) / 2] << 16) *

@@ -61,8 +61,10 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 }
 
 // Cross-lane butterfly on U chunks of 8 values: the lower lane of a pair keeps
-// a + b, the upper one a - b (fma(b, -1, a), one rounding).
-template <int MASK, int U>
+// a + b, the upper one a - b (fma(b, -1, a), one rounding).  SWZ: every
+// exchange through ds_swizzle (the LDS pipe) instead of a DPP move, one VALU
+// operation per value fewer where the rotation's VALU work is what counts.
+template <int MASK, int U, bool SWZ>
 __device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
 {
     const float sgn = (lane & MASK) ? -1.f : 1.f;
@@ -70,7 +72,9 @@ __device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float p = __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[u][r])));
+            const uint32_t b = __float_as_uint(v[u][r]);
+            const float p = __uint_as_float(
+                SWZ ? (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, 0x1F | (MASK << 10)) : lane_xor_u<MASK>(b));
             v[u][r] = __builtin_fmaf(v[u][r], sgn, p);
         }
 }
@@ -145,11 +149,15 @@ __device__ __forceinline__ void rotate_role(const uint16_t *__restrict__ x, int6
                     v[u][r] = a + b;
                     v[u][r + h] = a - b;
                 }
-    if constexpr (G >= 16) lane_stage8<1, M * CPR>(v, lane);
-    if constexpr (G >= 32) lane_stage8<2, M * CPR>(v, lane);
-    if constexpr (G >= 64) lane_stage8<4, M * CPR>(v, lane);
-    if constexpr (G >= 128) lane_stage8<8, M * CPR>(v, lane);
-    if constexpr (G >= 256) lane_stage8<16, M * CPR>(v, lane);
+    // DPP exchanges: ds_swizzle for every exchange (one VALU operation per
+    // value fewer) measured slower at M = 2 .. 4 (7.82 against 7.18 us at
+    // M = 2): the rotation's latency, not its VALU work, is what counts.
+    constexpr bool SWZ = false;
+    if constexpr (G >= 16) lane_stage8<1, M * CPR, SWZ>(v, lane);
+    if constexpr (G >= 32) lane_stage8<2, M * CPR, SWZ>(v, lane);
+    if constexpr (G >= 64) lane_stage8<4, M * CPR, SWZ>(v, lane);
+    if constexpr (G >= 128) lane_stage8<8, M * CPR, SWZ>(v, lane);
+    if constexpr (G >= 256) lane_stage8<16, M * CPR, SWZ>(v, lane);
     // Row absmax over the rotation waves: LDS atomic maximum, then an arrival
     // count that every rotation wave waits on (they are all resident in this
     // workgroup, so the wait ends).
@@ -262,13 +270,12 @@ __device__ __forceinline__ void stream_role(float qmax, int K, const uint8_t *__
         }
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            int acc = 0;
+            int acc = -asum8[m];  // the code - 8 offset, subtracted up front
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc = __builtin_amdgcn_sdot4((int)lo[i], (int)alo[m][i], acc, false);
                 acc = __builtin_amdgcn_sdot4((int)hi[i], (int)ahi[m][i], acc, false);
             }
-            acc -= asum8[m];
             if constexpr (FSUM)
                 part[m][r] = __float_as_uint(
                     __uint_as_float(r % 2 ? sv[r / 2] & 0xffff0000u : sv[r / 2] << 16) * (float)acc);
