@@ -61,10 +61,8 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 }
 
 // Cross-lane butterfly on U chunks of 8 values: the lower lane of a pair keeps
-// a + b, the upper one a - b (fma(b, -1, a), one rounding).  SWZ: every
-// exchange through ds_swizzle (the LDS pipe) instead of a DPP move, one VALU
-// operation per value fewer where the rotation's VALU work is what counts.
-template <int MASK, int U, bool SWZ>
+// a + b, the upper one a - b (fma(b, -1, a), one rounding).
+template <int MASK, int U>
 __device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
 {
     const float sgn = (lane & MASK) ? -1.f : 1.f;
@@ -72,9 +70,7 @@ __device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const uint32_t b = __float_as_uint(v[u][r]);
-            const float p = __uint_as_float(
-                SWZ ? (uint32_t)__builtin_amdgcn_ds_swizzle((int)b, 0x1F | (MASK << 10)) : lane_xor_u<MASK>(b));
+            const float p = __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[u][r])));
             v[u][r] = __builtin_fmaf(v[u][r], sgn, p);
         }
 }
@@ -149,15 +145,11 @@ __device__ __forceinline__ void rotate_role(const uint16_t *__restrict__ x, int6
                     v[u][r] = a + b;
                     v[u][r + h] = a - b;
                 }
-    // DPP exchanges: ds_swizzle for every exchange (one VALU operation per
-    // value fewer) measured slower at M = 2 .. 4 (7.82 against 7.18 us at
-    // M = 2): the rotation's latency, not its VALU work, is what counts.
-    constexpr bool SWZ = false;
-    if constexpr (G >= 16) lane_stage8<1, M * CPR, SWZ>(v, lane);
-    if constexpr (G >= 32) lane_stage8<2, M * CPR, SWZ>(v, lane);
-    if constexpr (G >= 64) lane_stage8<4, M * CPR, SWZ>(v, lane);
-    if constexpr (G >= 128) lane_stage8<8, M * CPR, SWZ>(v, lane);
-    if constexpr (G >= 256) lane_stage8<16, M * CPR, SWZ>(v, lane);
+    if constexpr (G >= 16) lane_stage8<1, M * CPR>(v, lane);
+    if constexpr (G >= 32) lane_stage8<2, M * CPR>(v, lane);
+    if constexpr (G >= 64) lane_stage8<4, M * CPR>(v, lane);
+    if constexpr (G >= 128) lane_stage8<8, M * CPR>(v, lane);
+    if constexpr (G >= 256) lane_stage8<16, M * CPR>(v, lane);
     // Row absmax over the rotation waves: LDS atomic maximum, then an arrival
     // count that every rotation wave waits on (they are all resident in this
     // workgroup, so the wait ends).
