@@ -328,6 +328,18 @@ ck_status ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t l
 ck_status ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                        float *xr, int64_t ldr, void *stream);
 
+/* The whole linear (bits 8: ck_w4a8_linear, bits 4: ck_w4a4_linear; same
+ * arguments without the workspace) always on its one-launch MFMA form, which
+ * those entry points choose only for 6 to 8 rows and N >= 8192, so that every
+ * launch shape of that kernel can be checked: 1 <= M <= 8, K <= 4096, any N
+ * (CK_ERR_UNSUPPORTED otherwise).  Results equal ck_rotate_quant followed by
+ * ck_w4_gemm_q on the few-row kernel bit for bit. */
+ck_status ck_test_linear_mfma_one_launch(int32_t bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                         int32_t G, const uint8_t *packed, int64_t ldw,
+                                         const uint16_t *w_scales, int32_t scale_kind, int32_t Gw, int64_t N,
+                                         const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
+                                         void *stream);
+
 /* The integer accumulators of ck_w4_gemm_q (kernel chosen by M exactly as
  * there): acc int32 [M, lda], acc[m,n] = sum_k codes[m,k] * (q[n,k] - 8). */
 ck_status ck_test_gemm_i32(const int8_t *codes, int64_t ldq, int64_t M, int64_t K,

@@ -54,6 +54,8 @@ SIGNATURES = {
     "ck_w4a4_gemm_packed": ([_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i32, _i64, _p, _p, _i64, _p],
                             ctypes.c_int),
     "ck_test_gemm_i32_a4": ([_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "ck_test_linear_mfma_one_launch": ([_i32, _p, _i64, _i64, _i64, _i32, _p, _i64, _p, _i32, _i32, _i64, _p,
+                                        _f32, _p, _i64, _p], ctypes.c_int),
 }
 
 
@@ -269,6 +271,25 @@ def linear(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
               CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL, 64, N, _ptr(bias), x_scale,
               _ptr(out), _ld(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
               _stream(x)))
+    return out
+
+
+def linear_mfma_one_launch(x, G: int, bits: int, packed, w_scales, per_group: bool, bias=None,
+                                x_scale: float = 1.0, out=None):
+    """ck_test_linear_mfma_one_launch: the whole linear forced onto its one-launch
+    MFMA kernel (1 <= M <= 8, K <= 4096, any N), for testing its launch shapes."""
+    _matrix(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    N = _weights(packed, w_scales, per_group, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if bias is not None:
+        _dense(bias, "bias", torch.bfloat16, (N,))
+    _out(out, "out", torch.bfloat16, M, N)
+    _same_device(x, ("packed", packed), ("w_scales", w_scales), ("bias", bias), ("out", out))
+    _check(lib.ck_test_linear_mfma_one_launch(bits, _ptr(x), M, K, _ld(x), G, _ptr(packed), _ld(packed),
+                                              _ptr(w_scales), CK_WS_PER_GROUP if per_group else CK_WS_PER_CHANNEL,
+                                              64, N, _ptr(bias), x_scale, _ptr(out), _ld(out), _stream(x)))
     return out
 
 

@@ -293,8 +293,19 @@ int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, c
 // codes bound for the tiled GEMM are stored two per byte, which halves the
 // codes traffic on both sides of the scratch; codes bound for the few-row
 // kernel are stored in its operand layout (whole 16-row tiles).
+// One launch in the MFMA form (w4_skinny_fused) from kMfmaFusedMinRows rows on
+// when the weights span at least kMfmaFusedMinN rows (32 or more per CU on a
+// 256-CU MI355X); the VALU GEMV form (w4_gemv_fused) up to 4 rows otherwise.
+// Measured on MI355X (K = 3840, graph replay, cold weights): at N = 10240 the
+// MFMA form takes 11.1 / 11.5 / 12.0 us at M = 6 / 7 / 8 against 12.2 / 12.5 /
+// 12.5 us for rotate-quant + the few-row kernel, but 9.1 / 9.8 / 10.5 us at M =
+// 2 / 3 / 4 against 7.1 / 8.2 / 9.5 us for the VALU form, and at N = 3840, M =
+// 8 it takes 9.9 us against 8.7 us: every CU rotates all the rows, which is
+// the longer part once the CU's share of the weights is small.
+constexpr int64_t kMfmaFusedMinRows = 6, kMfmaFusedMinN = 8192;
 struct LinearPlan {
-    bool fused;
+    bool fused;           // one launch (either form)
+    bool mfma_fused;      // ... the MFMA form
     GemmPath path;
     bool a4;
     bool tiled;           // codes in CodesLayout::kTiled16
@@ -303,10 +314,11 @@ struct LinearPlan {
     size_t used;          // scratch bytes the plan touches (0 when fused)
 };
 
-LinearPlan plan_linear(int bits, int64_t M, int64_t K)
+LinearPlan plan_linear(int bits, int64_t M, int64_t K, int64_t N)
 {
     LinearPlan p{};
-    p.fused = ck::w4_gemv_fused_supports(M, K);
+    p.mfma_fused = M >= kMfmaFusedMinRows && N >= kMfmaFusedMinN && ck::w4_skinny_fused_supports(M, K);
+    p.fused = p.mfma_fused || ck::w4_gemv_fused_supports(M, K);
     p.path = pick_path(M, K);
     p.a4 = !p.fused && bits == 4 && p.path == GemmPath::kTiled;
     p.tiled = !p.fused && p.path == GemmPath::kSkinny;
@@ -318,9 +330,12 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t K)
 
 // library_scratch: the scratch is the library's static device array
 // (ck_w4a4_linear_noalloc) instead of the caller's workspace ws.
+// force_mfma_one_launch: run the one-launch MFMA form whatever the plan (a test
+// hook for its launch shapes; it needs no scratch).
 int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                   int32_t G, const Weights &w, const uint16_t *bias, float x_scale, uint16_t *out,
-                  int64_t ldo, void *ws, size_t ws_bytes, void *stream, bool library_scratch = false)
+                  int64_t ldo, void *ws, size_t ws_bytes, void *stream, bool library_scratch = false,
+                  bool force_mfma_one_launch = false)
 {
     CK_TRY(check_m(fn, M));
     CK_TRY(check_k(fn, K));
@@ -339,7 +354,14 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
     if (overlap(ro, rx) || overlap(ro, span(w.packed, w.N, K / 2, w.ldw, 1)) ||
         overlap(ro, scales_span(w, K)) || overlap(ro, span(bias, 1, w.N, w.N, 2)))
         return fail(CK_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
-    const LinearPlan plan = plan_linear(bits, M, K);
+    LinearPlan plan = plan_linear(bits, M, K, w.N);
+    if (force_mfma_one_launch) {
+        if (!ck::w4_skinny_fused_supports(M, K))
+            return fail(CK_ERR_UNSUPPORTED, "%s: the one-launch MFMA form takes 1 <= M <= 8 and K <= 4096 "
+                        "(M=%lld, K=%lld)", fn, (long long)M, (long long)K);
+        plan.fused = plan.mfma_fused = true;
+        plan.used = 0;
+    }
     if (!plan.fused && plan.path == GemmPath::kTiled)
         CK_TRY(check_tiles(fn, M, w.N));
     if (library_scratch) {
@@ -354,7 +376,7 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
                 return fail(CK_ERR_HIP, "%s: static scratch unavailable on this device or stream "
                             "(hipError_t %d)", fn, e);
         }
-    } else {
+    } else if (!force_mfma_one_launch) {
         // The size asked of the caller does not depend on the path taken.
         const size_t need = workspace_bytes(M, K);
         if (!ws || ws_bytes < need)
@@ -373,9 +395,9 @@ int linear_common(const char *fn, int bits, const uint16_t *x, int64_t M, int64_
     const int qmax = bits == 8 ? 127 : 7;
     if (plan.fused) {
         // Decode shapes: one launch that rotates, quantises and multiplies.
-        const int e = ck::launch_w4_gemv_fused(x, ldx, G, qmax, (int)M, (int)K, w.packed, w.ldw, w.scales,
-                                               w.kind == CK_WS_PER_GROUP, (int)w.N, bias, x_scale, out, ldo,
-                                               stream);
+        const auto launch = plan.mfma_fused ? ck::launch_w4_skinny_fused : ck::launch_w4_gemv_fused;
+        const int e = launch(x, ldx, G, qmax, (int)M, (int)K, w.packed, w.ldw, w.scales, w.kind == CK_WS_PER_GROUP,
+                             (int)w.N, bias, x_scale, out, ldo, stream);
         return hip_status(e, fn);
     }
     int8_t *codes = static_cast<int8_t *>(ws);
@@ -565,6 +587,18 @@ int ck_w4a4_linear_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, in
                          ws_bytes, stream);
 }
 
+int ck_test_linear_mfma_one_launch_impl(int32_t bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                        int32_t G, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                                        int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                                        float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    const char *fn = "ck_test_linear_mfma_one_launch";
+    if (bits != 8 && bits != 4)
+        return fail(CK_ERR_INVALID_ARG, "%s: bits must be 8 or 4 (got %d)", fn, bits);
+    const Weights w{packed, ldw, w_scales, scale_kind, Gw, N};
+    return linear_common(fn, bits, x, M, K, ldx, G, w, bias, x_scale, out, ldo, nullptr, 0, stream, false, true);
+}
+
 int ck_w4a4_linear_noalloc_impl(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G,
                                 const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
                                 int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
@@ -702,6 +736,16 @@ ck_status ck_quantize_weights(const uint16_t *w, int64_t N, int64_t K, int64_t l
 {
     return static_cast<ck_status>(ck_quantize_weights_impl(w, N, K, ldw_in, G, scale_kind, packed,
             ldp, scales, stream));
+}
+
+ck_status ck_test_linear_mfma_one_launch(int32_t bits, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                         int32_t G, const uint8_t *packed, int64_t ldw, const uint16_t *w_scales,
+                                         int32_t scale_kind, int32_t Gw, int64_t N, const uint16_t *bias,
+                                         float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    return static_cast<ck_status>(ck_test_linear_mfma_one_launch_impl(bits, x, M, K, ldx, G, packed, ldw, w_scales,
+                                                                      scale_kind, Gw, N, bias, x_scale, out, ldo,
+                                                                      stream));
 }
 
 ck_status ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t G, float

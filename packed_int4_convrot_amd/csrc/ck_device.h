@@ -25,6 +25,10 @@ __device__ __forceinline__ u32x2 load_nt8(const void *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }
 
+// s_waitcnt vmcnt(0), the other counters untouched: this wave's vector memory
+// loads (global_load_lds DMA included) have landed.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by
 // index.  This renumbering gives every XCD a contiguous run of logical
 // blocks, so neighbouring blocks that share cache lines (weight-scale rows,

@@ -106,6 +106,55 @@ int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M,
                          int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
                          float x_scale, uint16_t *out, int64_t ldo, void *stream);
 
+// The whole linear in one launch on int8 MFMA (w4_skinny_fused.hip): rotate-quant
+// of 1 <= M <= 8 bf16 rows (K <= 4096) and the few-row matmul, one workgroup
+// per compute unit.  Workgroup shape: nws = t * s streaming waves (s = ceil(K /
+// 2048) slices of 32 K-groups for each of t tiles of 16 weight rows; the
+// workgroup's rows, a multiple of 8, fill t tiles except perhaps 8 rows of the
+// last) and kSfRotWaves rotation waves (one 8-column chunk per thread and row).
+// lds: t * s slices of 16 rows (kSfSlicePitch bytes apart), their partial sums
+// (2 KiB each) and the codes (kSfCodeGroup bytes per K-group, 32 s groups),
+// raised above half the CU's LDS when the grid fits the chip, so that no CU
+// runs two workgroups.
+constexpr int kSfMaxRows = 8, kSfRotWaves = 8, kSfGroupsPerWave = 32, kSfMaxStreamWaves = 8;
+constexpr int kSfSlicePitch = 1040, kSfCodeGroup = 576;
+constexpr int kSfMaxLds = 160 * 1024 - 512;  // the CU's LDS less the static counters (at most 288 bytes)
+struct SkinnyFusedShape {
+    int nb, rows, t, s, nws, lds;
+};
+inline bool w4_skinny_fused_shape(int64_t M, int64_t K, int64_t N, int ncu, SkinnyFusedShape &sh)
+{
+    if (M < 1 || M > kSfMaxRows || K < 64 || K % 64 != 0 || K > 8 * 64 * kSfRotWaves || N < 16 || N % 16 != 0 ||
+        ncu < 1)
+        return false;
+    const int64_t ng = K / 64, s = (ng + kSfGroupsPerWave - 1) / kSfGroupsPerWave;
+    const int64_t per_wave = 16 * kSfSlicePitch + 2 * 1024, codes = (int64_t)kSfCodeGroup * kSfGroupsPerWave * s;
+    int64_t tmax = (kSfMaxLds - codes) / (s * per_wave);
+    if (tmax * s > kSfMaxStreamWaves)
+        tmax = kSfMaxStreamWaves / s;
+    if (tmax < 1)
+        return false;
+    int64_t rows = ((N + ncu - 1) / ncu + 7) / 8 * 8;
+    if (rows > 16 * tmax)
+        rows = 16 * tmax;
+    const int64_t t = (rows + 15) / 16;
+    sh.rows = (int)rows, sh.t = (int)t, sh.s = (int)s, sh.nws = (int)(t * s);
+    sh.nb = (int)((N + rows - 1) / rows);
+    const int64_t lds = t * s * per_wave + codes;
+    constexpr int64_t kOneWorkgroupPerCu = 80 * 1024 + 16;
+    sh.lds = (int)(sh.nb <= ncu && lds < kOneWorkgroupPerCu ? kOneWorkgroupPerCu : lds);
+    return true;
+}
+inline bool w4_skinny_fused_supports(int64_t M, int64_t K)
+{
+    SkinnyFusedShape sh;
+    return w4_skinny_fused_shape(M, K, 16, 1, sh);
+}
+int launch_w4_skinny_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M, int K, const uint8_t *packed,
+                           int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
+                           float x_scale, uint16_t *out, int64_t ldo, void *stream);
+
+
 // Compute units of the current device (looked up once per device; 256 if the
 // query fails).
 int device_cu_count();

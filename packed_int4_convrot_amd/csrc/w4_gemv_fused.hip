@@ -45,47 +45,12 @@
 #include "ck_device.h"
 #include "gemv_reduce.h"
 #include "launch.h"
+#include "rotate_rows.h"
 
 namespace ck {
 namespace {
 
 constexpr int kRows = 8;  // weight rows per wave
-
-__device__ __forceinline__ uint32_t rne_byte(float t) { return __float_as_uint(t + 12582912.0f); }
-
-__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
-{
-    const uint32_t p01 = perm(b1, b0, 0x0C0C0400u);
-    const uint32_t p23 = perm(b3, b2, 0x0C0C0400u);
-    return perm(p23, p01, 0x05040100u);
-}
-
-// Cross-lane butterfly on U chunks of 8 values: the lower lane of a pair keeps
-// a + b, the upper one a - b (fma(b, -1, a), one rounding).
-template <int MASK, int U>
-__device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
-{
-    const float sgn = (lane & MASK) ? -1.f : 1.f;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float p = __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[u][r])));
-            v[u][r] = __builtin_fmaf(v[u][r], sgn, p);
-        }
-}
-
-__device__ __forceinline__ float wave_max(float am)
-{
-    am = fmaxf(am, __uint_as_float(lane_xor_u<1>(__float_as_uint(am))));
-    am = fmaxf(am, __uint_as_float(lane_xor_u<2>(__float_as_uint(am))));
-    am = fmaxf(am, __uint_as_float(lane_mirror8_u(__float_as_uint(am))));
-    am = fmaxf(am, __uint_as_float(lane_mirror16_u(__float_as_uint(am))));
-    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 0)),
-                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16))),
-                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 32)),
-                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 48))));
-}
 
 // LDS of a workgroup besides the codes.
 template <int M>
@@ -95,106 +60,6 @@ struct FusedShared {
     uint32_t arrived;                                // rotation waves whose maxima are in amax
     uint32_t done[kFusedMaxStreamWaves];             // slices of each row block summed into red
 };
-
-// Rotation waves: thread rt of the rstride rotation threads holds chunks
-// rt + j * rstride (j < CPR) of every row.  A G-column group is G / 8
-// consecutive chunks on neighbouring lanes of one wave (rstride and nchunk are
-// multiples of G / 8).  Barriers: the workgroup's two, in the same order as
-// the streaming waves.
-template <int M, int G, int CPR>
-__device__ __forceinline__ void rotate_role(const uint16_t *__restrict__ x, int64_t ldx, float qmax, int K,
-                                            int rt, int rstride, int nwr, int lane, uint8_t *s_codes,
-                                            FusedShared<M> &sh)
-{
-    const int nchunk = K / 8;
-    u32x4 xraw[M][CPR];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int j = 0; j < CPR; ++j) {
-            const int c = rt + j * rstride;
-            xraw[m][j] = *reinterpret_cast<const u32x4 *>(x + (int64_t)m * ldx + 8 * (c < nchunk ? c : nchunk - 1));
-        }
-    if (rt == 0) {
-        sh.arrived = 0;
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            sh.amax[m] = 0;
-    }
-    __syncthreads();  // the counters are published
-
-    float v[M * CPR][8];
-#pragma unroll
-    for (int u = 0; u < M * CPR; ++u) {
-        const bool live = rt + (u % CPR) * rstride < nchunk;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t w = live ? xraw[u / CPR][u % CPR][j] : 0u;
-            v[u][2 * j] = __uint_as_float(w << 16);
-            v[u][2 * j + 1] = __uint_as_float(w & 0xffff0000u);
-        }
-    }
-#pragma unroll
-    for (int h = 1; h < 8 && h < G; h <<= 1)
-#pragma unroll
-        for (int u = 0; u < M * CPR; ++u)
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if ((r & h) == 0) {
-                    const float a = v[u][r], b = v[u][r + h];
-                    v[u][r] = a + b;
-                    v[u][r + h] = a - b;
-                }
-    if constexpr (G >= 16) lane_stage8<1, M * CPR>(v, lane);
-    if constexpr (G >= 32) lane_stage8<2, M * CPR>(v, lane);
-    if constexpr (G >= 64) lane_stage8<4, M * CPR>(v, lane);
-    if constexpr (G >= 128) lane_stage8<8, M * CPR>(v, lane);
-    if constexpr (G >= 256) lane_stage8<16, M * CPR>(v, lane);
-    // Row absmax over the rotation waves: LDS atomic maximum, then an arrival
-    // count that every rotation wave waits on (they are all resident in this
-    // workgroup, so the wait ends).
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float am = 0.f;
-#pragma unroll
-        for (int j = 0; j < CPR; ++j)
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                am = fmaxf(am, fabsf(v[m * CPR + j][r]));
-        am = wave_max(am);
-        if (lane == 0)
-            atomicMax(&sh.amax[m], __float_as_uint(am));
-    }
-    if (lane == 0)
-        __hip_atomic_fetch_add(&sh.arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__builtin_amdgcn_readfirstlane(
-               __hip_atomic_load(&sh.arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < (uint32_t)nwr)
-        __builtin_amdgcn_s_sleep(1);
-    // Quantise: rne(y * qmax / absmax), the codes of the rotate-quant kernel
-    // bit for bit.  Chunk c is columns 8 (c % 4) .. + 7 of 32-column piece
-    // c / 4: its even columns go to bytes 4 (c % 4) .. + 3 of the piece's
-    // first 16 bytes, its odd columns to the same bytes of the next 16.
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const float am = __uint_as_float(sh.amax[m]);
-        const float inv = am > 0.f ? qmax / am : 0.f;
-#pragma unroll
-        for (int j = 0; j < CPR; ++j) {
-            const int c = rt + j * rstride;
-            const float(&y)[8] = v[m * CPR + j];
-            uint32_t b[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                b[r] = rne_byte(y[r] * inv);
-            if (c < nchunk) {
-                uint8_t *piece = s_codes + m * K + 32 * (c >> 2) + 4 * (c & 3);
-                *reinterpret_cast<uint32_t *>(piece) = pack4(b[0], b[2], b[4], b[6]);
-                *reinterpret_cast<uint32_t *>(piece + 16) = pack4(b[1], b[3], b[5], b[7]);
-            }
-        }
-    }
-    __syncthreads();  // the codes are in LDS
-}
 
 // Streaming waves: an 8-row block n0 .. n0 + 7 and the 2048-column slice of
 // wave % S; lane l owns columns kbase = 2048 (wave % S) + 32 l .. + 31.
@@ -321,8 +186,15 @@ __global__ __launch_bounds__(1024) void w4_gemv_fused_kernel(
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (wave >= NWS) {
         const int nwr = (int)blockDim.x / kWave - NWS;
-        rotate_role<M, G, CPR>(x, ldx, qmax, K, (int)threadIdx.x - kWave * NWS, kWave * nwr, nwr, lane, s_codes,
-                               sh);
+        // Chunk c is columns 8 (c % 4) .. + 7 of 32-column piece c / 4: its even
+        // columns go to bytes 4 (c % 4) .. + 3 of the piece's first 16 bytes, its
+        // odd columns to the same bytes of the next 16.
+        rotate_rows<M, G, CPR, false>(x, ldx, qmax, K, (int)threadIdx.x - kWave * NWS, kWave * nwr, nwr, lane, sh.amax,
+                               &sh.arrived, [&](int m, int c, uint32_t even, uint32_t odd) {
+                                   uint8_t *piece = s_codes + m * K + 32 * (c >> 2) + 4 * (c & 3);
+                                   *reinterpret_cast<uint32_t *>(piece) = even;
+                                   *reinterpret_cast<uint32_t *>(piece + 16) = odd;
+                               });
     } else {
         const int rb = xcd_block(blockIdx.x, gridDim.x) * RB + wave / S;
         const bool has_rows = rb < N / kRows;

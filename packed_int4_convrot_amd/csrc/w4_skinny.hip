@@ -49,9 +49,6 @@ constexpr int kMaxWaves = kSkinnyMaxWaves;  // 512 threads: up to 256 VGPRs per 
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// s_waitcnt vmcnt(0), other counters untouched.
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 template <int MT, int GPW, bool PER_GROUP, bool OUT_I32, bool TILED>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
     const int8_t *__restrict__ codes, int64_t ldq, const float *__restrict__ row_scales, int M,

@@ -216,6 +216,17 @@ stub::Kernel expected_kernel(int64_t M, int64_t K)
     return skinny ? stub::Kernel::kSkinny : stub::Kernel::kGemm;
 }
 
+// The whole linear in one launch: the MFMA form for 6 to 8 rows, K <= 4096 and
+// at least 8192 weight rows, else the VALU GEMV form (up to 4 rows).
+stub::Kernel expected_fused(int64_t M, int64_t K, int64_t N)
+{
+    if (M >= 6 && M <= 8 && K >= 64 && K <= 4096 && K % 64 == 0 && N >= 8192)
+        return stub::Kernel::kSkinnyFused;
+    if (ck::w4_gemv_fused_supports(M, K))
+        return stub::Kernel::kGemvFused;
+    return stub::Kernel::kNone;
+}
+
 void test_gemm_dispatch()
 {
     struct Case {
@@ -365,9 +376,9 @@ void test_linear()
             EXPECT(lin(x, c.M, c.K, ldx, c.G, w.packed, w.ldw, w.scales, 1, 64, N, nullptr, 0.5f, out, ldo, ws,
                        need, nullptr) == CK_OK);
             const stub::Kernel mm = expected_kernel(c.M, c.K);
-            if (ck::w4_gemv_fused_supports(c.M, c.K)) {
+            if (expected_fused(c.M, c.K, N) != stub::Kernel::kNone) {
                 // Decode: one fused launch rotates, quantises and multiplies.
-                EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kGemvFused);
+                EXPECT(stub::calls == 1 && stub::last.kernel == expected_fused(c.M, c.K, N));
                 EXPECT(stub::last.G == c.G && stub::last.x == x && stub::last.qmax == (bits == 8 ? 127 : 7));
                 EXPECT(stub::last.x_scale == 0.5f);
                 continue;
@@ -426,6 +437,68 @@ void test_fused_gemv_shapes()
     EXPECT(ck::w4_gemv_fused_shape(1, 3840, 10240, 256, sh) && sh.nb == 256 && sh.rb == 5 && sh.nwr == 4);
     EXPECT(ck::w4_gemv_fused_supports(4, 3840) && ck::w4_gemv_fused_supports(2, 16384));
     EXPECT(!ck::w4_gemv_fused_supports(3, 16384) && !ck::w4_gemv_fused_supports(5, 64));
+}
+
+// The one-launch MFMA linear: its workgroup shapes (one workgroup per CU,
+// every LDS byte inside the CU, the rows of N covered once), the linear's own
+// choice of it (6 to 8 rows, N >= 8192), and its test entry point for any N.
+void test_mfma_one_launch()
+{
+    for (int64_t M = 1; M <= 9; ++M)
+        for (int64_t K = 64; K <= 4096 + 64; K += 64)
+            for (int64_t N : {16, 48, 3840, 4112, 10240, 16384, 65536})
+                for (int ncu : {1, 80, 256}) {
+                    ck::SkinnyFusedShape sh;
+                    const bool ok = ck::w4_skinny_fused_shape(M, K, N, ncu, sh);
+                    EXPECT(ok == (M <= 8 && K <= 4096));
+                    EXPECT(ok == ck::w4_skinny_fused_supports(M, K));
+                    if (!ok)
+                        continue;
+                    const int64_t s = (K / 64 + 31) / 32;
+                    EXPECT(sh.s == s && sh.rows % 8 == 0 && sh.rows >= 8 && sh.t == (sh.rows + 15) / 16);
+                    EXPECT(sh.nws == sh.t * sh.s && sh.nws + ck::kSfRotWaves <= 16);
+                    EXPECT((int64_t)sh.nb * sh.rows >= N && (int64_t)(sh.nb - 1) * sh.rows < N);
+                    const int64_t need = (int64_t)sh.nws * (16 * ck::kSfSlicePitch + 2048) + ck::kSfCodeGroup * 32 * s;
+                    EXPECT(sh.lds >= need && sh.lds <= ck::kSfMaxLds);
+                    EXPECT(sh.nb > ncu || sh.lds > 80 * 1024);
+                }
+    // N = 10240 on 256 CUs: 40 rows (two tiles and a half tile) per workgroup.
+    ck::SkinnyFusedShape sh;
+    EXPECT(ck::w4_skinny_fused_shape(8, 3840, 10240, 256, sh) && sh.nb == 256 && sh.rows == 40 && sh.nws == 6);
+    for (int64_t M : {5, 6, 8})
+        for (int64_t N : {8176, 8192}) {
+            Pool pool;
+            const int64_t K = 3840, ldx = K, ldo = N;
+            const W w = make_weights(pool, N, K, CK_WS_PER_GROUP);
+            uint16_t *x = pool.get<uint16_t>(rows_bytes(M, K, ldx, 2));
+            uint16_t *out = pool.get<uint16_t>(rows_bytes(M, N, ldo, 2));
+            const size_t need = ck_linear_workspace_bytes(M, K, N);
+            uint8_t *ws = pool.get<uint8_t>(need);
+            stub::reset();
+            EXPECT(ck_w4a8_linear(x, M, K, ldx, 64, w.packed, w.ldw, w.scales, 1, 64, N, nullptr, 1.f, out, ldo,
+                                  ws, need, nullptr) == CK_OK);
+            const bool mfma = M >= 6 && N >= 8192;
+            EXPECT(mfma ? stub::calls == 1 && stub::last.kernel == stub::Kernel::kSkinnyFused
+                        : stub::calls == 2 && stub::last.kernel != stub::Kernel::kSkinnyFused);
+        }
+    {
+        Pool pool;
+        const int64_t M = 3, K = 256, N = 48;
+        const W w = make_weights(pool, N, K, CK_WS_PER_CHANNEL);
+        uint16_t *x = pool.get<uint16_t>(rows_bytes(8, 4160, 4160, 2));
+        uint16_t *out = pool.get<uint16_t>(rows_bytes(9, N, N, 2));
+        stub::reset();
+        EXPECT(ck_test_linear_mfma_one_launch(4, x, M, K, K, 16, w.packed, w.ldw, w.scales, 0, 64, N, nullptr, 2.f,
+                                              out, N, nullptr) == CK_OK);
+        EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kSkinnyFused && stub::last.qmax == 7 &&
+               stub::last.G == 16 && stub::last.x_scale == 2.f);
+        stub::reset();
+        EXPECT(ck_test_linear_mfma_one_launch(5, x, M, K, K, 16, w.packed, w.ldw, w.scales, 0, 64, N, nullptr, 1.f,
+                                              out, N, nullptr) == CK_ERR_INVALID_ARG);
+        EXPECT(ck_test_linear_mfma_one_launch(8, x, 9, K, K, 16, w.packed, w.ldw, w.scales, 0, 64, N, nullptr, 1.f,
+                                              out, N, nullptr) == CK_ERR_UNSUPPORTED);
+        EXPECT(stub::calls == 0);
+    }
 }
 
 void test_linear_invalid()
@@ -494,8 +567,8 @@ void test_noalloc()
             continue;
         }
         EXPECT(st == CK_OK);
-        if (ck::w4_gemv_fused_supports(c.M, c.K)) {
-            EXPECT(stub::calls == 1 && stub::last.kernel == stub::Kernel::kGemvFused && stub::last.G == 64);
+        if (expected_fused(c.M, c.K, N) != stub::Kernel::kNone) {
+            EXPECT(stub::calls == 1 && stub::last.kernel == expected_fused(c.M, c.K, N) && stub::last.G == 64);
             continue;
         }
         EXPECT(stub::calls == 2);
@@ -573,6 +646,7 @@ int main()
     test_gemm_packed();
     test_linear();
     test_fused_gemv_shapes();
+    test_mfma_one_launch();
     test_linear_invalid();
     test_noalloc();
     test_w4a16();

@@ -185,6 +185,24 @@ int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M,
     return finish(c);
 }
 
+int launch_w4_skinny_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M, int K, const uint8_t *packed,
+                           int64_t ldw, const uint16_t *w_scales, bool per_group, int N, const uint16_t *bias,
+                           float x_scale, uint16_t *out, int64_t ldo, void *stream)
+{
+    using namespace stub;
+    SkinnyFusedShape sh;
+    if (!w4_skinny_fused_shape(M, K, N, 256, sh))
+        return 1;  // hipErrorInvalidValue
+    read_rows(x, M, 2 * (int64_t)K, 2 * ldx);
+    touch_matmul(nullptr, 0, nullptr, M, K, packed, ldw, w_scales, per_group, N, bias, out, ldo, nullptr, 0,
+                 false);
+    Call c{};
+    c.kernel = Kernel::kSkinnyFused;
+    c.M = M, c.K = K, c.N = N, c.G = G, c.qmax = qmax, c.per_group = per_group;
+    c.x_scale = x_scale, c.x = x, c.out = out, c.stream = stream;
+    return finish(c);
+}
+
 int launch_w4_skinny(const int8_t *codes, int64_t ldq, bool tiled, const float *row_scales, int M, int K,
                      const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group, int N,
                      const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo, int32_t *acc_out,

@@ -9,7 +9,7 @@
 
 namespace stub {
 
-enum class Kernel { kNone, kRotateQuant, kAwqGemm, kQuantizeWeights, kGemv, kGemvFused, kSkinny, kGemm, kW4a16Gemv };
+enum class Kernel { kNone, kRotateQuant, kAwqGemm, kQuantizeWeights, kGemv, kGemvFused, kSkinnyFused, kSkinny, kGemm, kW4a16Gemv };
 
 struct Call {
     Kernel kernel = Kernel::kNone;

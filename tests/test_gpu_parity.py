@@ -394,16 +394,32 @@ FUSED_CASES = [(1, 3840), (2, 3840), (3, 3840), (4, 3840), (1, 64), (4, 64), (2,
                (4, 8192), (1, 16384), (2, 16384), (3, 16384)]
 
 
+def mfma_one_launch(M, K, N):
+    """The whole linear runs the one-launch MFMA kernel (6 to 8 rows, K <= 4096, N >= 8192)."""
+    return 6 <= M <= 8 and K <= 4096 and N >= 8192
+
+
+def padded_two_launch(xd, G, bits, wd, sd, per_group, bd, x_scale):
+    """rotate-quant + the few-row MFMA kernel on codes (ck_w4_gemm_q takes it from 6 rows
+    on), with x padded by zero rows to at least 6: rows are independent on that path, so
+    its first M rows are what the one-launch MFMA kernel must give bit for bit."""
+    M = xd.shape[0]
+    xp = torch.cat([xd, torch.zeros((max(0, 6 - M), xd.shape[1]), dtype=xd.dtype, device=xd.device)])
+    codes, scales = ck.rotate_quant(xp, G, bits)
+    return ck.gemm_q(codes, scales * np.float32(x_scale), wd, sd, per_group, bias=bd)[:M]
+
+
 @pytest.mark.parametrize("M,K", FUSED_CASES)
 @pytest.mark.parametrize("G", [16, 64, 256])
 def test_fused_decode_linear_equals_two_step_path(M, K, G):
-    """The one-launch decode linear (rotate-quant and GEMV in one workgroup per CU,
-    one to four rows) gives bit-identical outputs to ck_rotate_quant followed by
-    ck_w4_gemv, for both bit widths and scale kinds, with a zero row and an input
-    scale: one K slice with 2 active lanes, partial and full slices, up to eight
-    slices; N = 16 and 48 (two and six workgroups), 1024 (one 8-row block per
-    workgroup), 4112 (three per workgroup, the last workgroup partly empty) and
-    10240 (five)."""
+    """The one-launch decode linear gives the two-launch outputs bit for bit, for both
+    bit widths and scale kinds, with a zero row and an input scale.  The VALU form
+    (one row, or more rows beyond K = 4096; one workgroup per CU) equals
+    ck_rotate_quant followed by ck_w4_gemv: one K slice with 2 active lanes, partial
+    and full slices, up to eight slices.  The MFMA form (2 to 8 rows) equals
+    rotate-quant followed by the few-row kernel, and on per-channel scales (exact
+    integer sums) the GEMV too.  N = 16 and 48 (two and six workgroups), 1024, 4112
+    (the last workgroup partly empty) and 10240."""
     if K % G:
         pytest.skip("K must be a multiple of G")
     for N in (16, 48, 1024, 4112, 10240):
@@ -417,7 +433,49 @@ def test_fused_decode_linear_equals_two_step_path(M, K, G):
                 fused = ck.linear(xd, G, bits, wd, sd, per_group, bias=bd, x_scale=0.3)
                 codes, scales = ck.rotate_quant(xd, G, bits)
                 two = ck.gemv(codes, scales * np.float32(0.3), wd, sd, per_group, bias=bd)
+                if mfma_one_launch(M, K, N):
+                    assert torch.equal(fused, padded_two_launch(xd, G, bits, wd, sd, per_group, bd, 0.3)), \
+                        (N, bits, per_group)
+                    if per_group:
+                        continue
                 assert torch.equal(fused, two), (N, bits, per_group)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("K,G", [(64, 16), (64, 64), (256, 256), (2048, 64), (2112, 64), (3840, 16),
+                                 (3840, 64), (3840, 256), (4096, 256)])
+def test_mfma_decode_linear_launch_shapes(M, K, G):
+    """The one-launch MFMA linear (through its test entry point, which runs it for any
+    N) over its workgroup shapes: one or two K slices (the second with 1 to 32 groups),
+    workgroups of 8 to 48 weight rows (a half tile of 8 at N = 16, 48, 10240; a last
+    workgroup with 8 of its 24 rows at N = 4112; 342 workgroups of 48 rows, more than
+    the CUs, at N = 16384), both bit widths and scale kinds, a zero row, bias and an
+    input scale: bit for bit against rotate-quant + the few-row kernel, and against the
+    oracle's epilogue on the same codes.  Where the linear's own plan picks this kernel
+    (6 to 8 rows, N >= 8192), ck_w4a8_linear / ck_w4a4_linear give the same bits."""
+    Ns = [16, 48, 4112] + ([10240] if (K, G) == (3840, 64) else []) + ([16384] if K == 4096 else [])
+    for N in Ns:
+        for bits in (8, 4):
+            for per_group in (True, False):
+                inp = workloads.linear_inputs(M, K, N, seed=3 * M + K + bits, outliers=min(8, K // 8),
+                                              scale="group" if per_group else "channel",
+                                              zero_rows=(M - 1,) if M > 1 else (),
+                                              with_bias=True)
+                xd, wd = bf16_dev(inp["x"]), u8_dev(inp["packed"])
+                sd, bd = bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+                out = ck.linear_mfma_one_launch(xd, G, bits, wd, sd, per_group, bias=bd, x_scale=0.75)
+                ref = padded_two_launch(xd, G, bits, wd, sd, per_group, bd, 0.75)
+                assert torch.equal(out, ref), (N, bits, per_group)
+                if mfma_one_launch(M, K, N):
+                    assert torch.equal(ck.linear(xd, G, bits, wd, sd, per_group, bias=bd, x_scale=0.75), out)
+                if N <= 4112:
+                    codes, scales = ck.rotate_quant(xd, G, bits)
+                    ref = oracle.gemm_q(host(codes), host(scales) * np.float32(0.75), inp["packed"],
+                                        inp["w_scales"], per_group, bias=inp["bias"])
+                    assert_output_close(host(out), ref)
+                    if M > 1:
+                        h = host(out)
+                        assert np.array_equal(h[M - 1], workloads.bf16_bits_to_f32(inp["bias"]))  # zero row -> bias
 
 
 @pytest.mark.parametrize("G", [16, 64, 256])

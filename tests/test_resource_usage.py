@@ -27,7 +27,7 @@ def _report():
 def test_every_hot_kernel_is_reported():
     names = " ".join(k["kernel"] for k in _report()["kernels"])
     for kernel in ("rotate_quant_kernel", "w4_gemv_kernel", "w4_skinny_kernel", "w4_gemm_kernel",
-                   "w4a16_gemv_kernel", "awq_gemm_kernel"):
+                   "w4a16_gemv_kernel", "awq_gemm_kernel", "w4_gemv_fused_kernel", "w4_skinny_fused_kernel"):
         assert kernel in names, kernel
 
 
