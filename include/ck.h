@@ -191,8 +191,11 @@ size_t ck_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * both on `stream`; for 1 <= M <= 4 one launch instead (M <= 3 when
  * K > 8192), with one workgroup per compute unit, whose rotation waves
  * rotate and quantise the rows into LDS while its other waves stream the
- * weights (same codes, same results bit for bit).  For 6 <= M <= 64 the codes are held in the few-row
- * kernel's operand layout (16-row tiles) rather than row-major.  x_scale (> 0, finite; 1.0 for none) is the input-scale
+ * weights (same codes, same results bit for bit); for 6 <= M <= 8 with
+ * K <= 4096 and N >= 8192 one launch too, its products on int8 MFMA (the
+ * same results as ck_rotate_quant + ck_w4_gemm_q bit for bit).  Otherwise,
+ * for 6 <= M <= 64 the codes are held in the few-row kernel's operand layout
+ * (16-row tiles) rather than row-major.  x_scale (> 0, finite; 1.0 for none) is the input-scale
  * factor of [SD]: the result is the linear of x_scale * x, obtained by
  * multiplying each row scale by x_scale (the codes of x_scale * x equal those
  * of x whenever x_scale is a power of two).
@@ -234,7 +237,8 @@ ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, i
  *     ceil(M / 16) * 16 * K bytes (the few-row kernel's 16-row tiles) or M * K
  *     bytes (the GEMV), each rounded up to 256, plus 4 * M bytes of row
  *     scales rounded up to 256; the one-launch decode shapes (M <= 4, or
- *     M <= 3 when K > 8192) use no scratch.
+ *     M <= 3 when K > 8192; 6 <= M <= 8 with K <= 4096 and N >= 8192) use
+ *     no scratch.
  *     For example M = 8192 rows fit up to K = 16384, and M = 16384 rows up
  *     to K = 8192.
  *   - The call allocates nothing (no hipMalloc, no allocating library call).

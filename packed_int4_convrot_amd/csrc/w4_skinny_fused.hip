@@ -1,6 +1,8 @@
 // Whole W4A8/W4A4 linear for 1 <= M <= 8 activation rows in one launch: the
 // rotate-quant of the bf16 rows and the packed-int4 matmul on int8 MFMA, one
-// workgroup per compute unit.
+// workgroup per compute unit.  The linear takes it for 6 to 8 rows when the
+// weights span at least 8192 rows; every shape is reachable through a test
+// entry point.
 //
 // Prior art: the fused RotateQuant operator of "[PR #155] [Feat][Ascend] Add
 // fused RotateQuant backend" ("What this PR does") and the register-side int4
@@ -8,26 +10,35 @@
 // GEMV and fused GatedDeltaNet decode" (description).
 //
 // The one-launch decode GEMV (w4_gemv_fused.hip) forms its dot products on the
-// VALU, whose work grows with the row count, and its rotation of the rows
-// (once per CU) competes for the same VALU.  Here the products run on
-// v_mfma_i32_16x16x64_i8 as in the few-row kernel (w4_skinny.hip), which
-// leaves the VALU to the rotation and the nibble decode.
+// VALU, whose work grows with the row count (and its rotation threads hold at
+// most 4 rows).  Here the products run on v_mfma_i32_16x16x64_i8 as in the
+// few-row kernel (w4_skinny.hip).  The group loop still costs about 15 VALU
+// instructions per MFMA (nibble decode, int -> fp32, the per-group scale fold),
+// so below 5 rows the VALU GEMV, which folds one scale per 32 weights, stays
+// faster; and every CU rotates all M rows, which is what bounds the kernel at
+// 8 rows once a CU's share of the weights is small.
 //
-// Workgroup: nws = T * S streaming waves, then kSfRotWaves rotation waves.
+// Workgroup: kSfRotWaves rotation waves first, then nws = T * S streaming waves.
+//   * rotation waves: rotate_rows() with one 8-column chunk per thread and row
+//     (K <= 4096); each wave posts its row maxima to LDS, the first barrier
+//     publishes them, and the codes go to LDS in the MFMA operand order below
+//     before the second barrier.  Being first in the workgroup, their x loads
+//     enter the CU's memory pipeline ahead of the weight stream;
 //   * the workgroup owns `rows` consecutive weight rows (a multiple of 8): T
-//     tiles of 16 rows, the last possibly of 8; wave (t, s) = (w / S, w % S)
-//     streams K-groups 32 s .. 32 s + 31 of tile t: one global_load_lds_dwordx4
-//     per tile row, each a contiguous 1 KiB of that row, to LDS rows 1040
-//     bytes apart (so the 8-byte fragment reads of 16 rows hit 16 bank
-//     groups), plus the per-group weight scales;
-//   * rotation waves: rotate_rows() with one 8-column chunk per thread and
-//     row (K <= 4096), codes stored to LDS in the MFMA operand order below;
-//   * after the second barrier each streaming wave multiplies its groups,
-//     A = codes of rows 0 .. M - 1 (rows M .. 15 zero), B = decoded weights.
-//     A per-group scale is folded in right after the MFMA of its group, into
-//     one fp32 sum per 16 groups: the sums, and the order in which they are
-//     added, are those of the few-row kernel (16 groups per wave there), so
-//     the outputs equal rotate-quant + few-row kernel bit for bit;
+//     tiles of 16 rows, the last possibly of 8; streaming wave (t, s) streams
+//     K-groups 32 s .. 32 s + 31 of tile t from its first instructions on: the
+//     per-group weight scales, then one global_load_lds_dwordx4 per tile row,
+//     each a contiguous 1 KiB of that row, to LDS rows 1040 bytes apart (so the
+//     8-byte fragment reads of 16 rows hit 16 bank groups).  It meets the two
+//     barriers without waiting for that DMA (barrier_lds_only), then waits for
+//     its own loads;
+//   * each streaming wave multiplies its groups, A = codes (rows M .. 15 are
+//     whatever LDS holds there: MFMA rows are independent and those outputs
+//     are never stored; groups past K are zero codes), B = decoded weights.  A
+//     per-group scale is folded in right after the MFMA of its group, into one
+//     fp32 sum per 16 groups: the sums, and the order in which they are added,
+//     are those of the few-row kernel (16 groups per wave there), so the
+//     outputs equal rotate-quant + few-row kernel bit for bit;
 //   * the last of a tile's S waves to finish (an LDS arrival count) adds the
 //     partial sums in group order, applies the row scale, x_scale and bias and
 //     stores bf16.
