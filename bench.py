@@ -42,7 +42,8 @@ BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a8_decode_gemv_m1_k3840_n10240_traffic.txt")
 GEMV_SOURCES = ["packed_int4_convrot_amd/csrc/w4_gemv_fused.hip", "packed_int4_convrot_amd/csrc/gemv_reduce.h",
-                "packed_int4_convrot_amd/csrc/ck_device.h", "packed_int4_convrot_amd/csrc/launch.h"]
+                "packed_int4_convrot_amd/csrc/rotate_rows.h", "packed_int4_convrot_amd/csrc/ck_device.h",
+                "packed_int4_convrot_amd/csrc/launch.h"]
 
 
 def log(msg):
@@ -173,6 +174,11 @@ PROFILE_WORKLOADS = {
     "w4a8_decode_linear_m4_k3840_n10240_g64": dict(
         kernel="w4_gemv_fused_kernel", M=4, K=3840, N=10240, mops=None,
         alg_bytes=10240 * 3840 // 2 + 60 * 10240 * 2 + 4 * 3840 * 2 + 4 * 10240 * 2),
+    # The one-launch MFMA linear at M = 8 (same bytes as above; its MFMAs cover 16
+    # activation rows and 48 weight rows per 40-row workgroup).
+    "w4a8_decode_linear_m8_k3840_n10240_g64": dict(
+        kernel="w4_skinny_fused_kernel", M=8, K=3840, N=10240, mops="SQ_INSTS_VALU_MFMA_MOPS_I8",
+        alg_bytes=10240 * 3840 // 2 + 60 * 10240 * 2 + 8 * 3840 * 2 + 8 * 10240 * 2),
     # The matmul half of the M = 32 W4A8 linear: packed weights, group scales, the
     # tiled codes and row scales, the bf16 output.
     "w4a8_skinny_m32_k3840_n3840_g64": dict(
@@ -188,7 +194,11 @@ KERNEL_SOURCES = {
                           "packed_int4_convrot_amd/csrc/gemv_reduce.h"] + _COMMON,
     "w4_skinny_kernel": ["packed_int4_convrot_amd/csrc/w4_skinny.hip"] + _COMMON,
     "w4_gemv_fused_kernel": ["packed_int4_convrot_amd/csrc/w4_gemv_fused.hip",
-                             "packed_int4_convrot_amd/csrc/gemv_reduce.h"] + _COMMON,
+                             "packed_int4_convrot_amd/csrc/gemv_reduce.h",
+                             "packed_int4_convrot_amd/csrc/rotate_rows.h"] + _COMMON,
+    "w4_skinny_fused_kernel": ["packed_int4_convrot_amd/csrc/w4_skinny_fused.hip",
+                               "packed_int4_convrot_amd/csrc/gemv_reduce.h",
+                               "packed_int4_convrot_amd/csrc/rotate_rows.h"] + _COMMON,
 }
 
 
