@@ -568,6 +568,29 @@ def _graph_replays_equal_eager(fn, out):
         torch.mm(torch.ones(64, 64, device=DEV), torch.ones(64, 64, device=DEV))  # unrelated eager work
 
 
+def test_mfma_one_launch_in_the_linear_graph_strided_noalloc():
+    """Where the linear itself takes the one-launch MFMA kernel (6 to 8 rows, N >= 8192):
+    a HIP graph replays it bit-identically with eager work between replays; a strided x
+    (NaN padding past K) gives the dense result; and the allocation-free W4A4 entry,
+    which needs no scratch on this path, equals the workspace entry."""
+    M, K, N = 7, 3840, 8192
+    inp = workloads.linear_inputs(M, K, N, seed=77, outliers=8, scale="group", zero_rows=(2,), with_bias=True)
+    xd, wd, sd, bd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+    ref = padded_two_launch(xd, 64, 8, wd, sd, True, bd, 1.0)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((ck.workspace_bytes(M, K, N),), dtype=torch.uint8, device=DEV)
+    _graph_replays_equal_eager(lambda: ck.linear(xd, 64, 8, wd, sd, True, bias=bd, out=out, workspace=ws), out)
+    assert torch.equal(out, ref)
+    padded = workloads.activations(M, K, seed=77, outliers=8, ld=K + 256)
+    xs = bf16_dev(padded)
+    xs[:, K:] = float("nan")
+    assert torch.equal(ck.linear(xs[:, :K], 64, 8, wd, sd, True, bias=bd), ck.linear(bf16_dev(padded[:, :K]), 64, 8,
+                                                                                     wd, sd, True, bias=bd))
+    lin4 = ck.linear(xd, 64, 4, wd, sd, True, bias=bd)
+    assert torch.equal(ck.w4a4_linear_noalloc(xd, 64, wd, sd, True, bias=bd), lin4)
+    assert torch.equal(lin4, padded_two_launch(xd, 64, 4, wd, sd, True, bd, 1.0))
+
+
 def test_graph_replay_packed_w4a4_and_awq_gemm():
     """The packed W4A4 path (M > 64), the weight producer and the AWQ prefill GEMM
     replay from a HIP graph bit-identically."""
