@@ -25,8 +25,11 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 }
 
 // Cross-lane butterfly on U chunks of 8 values: the lower lane of a pair keeps
-// a + b, the upper one a - b (fma(b, -1, a), one rounding).
-template <int MASK, int U>
+// a + b, the upper one a - b (fma(b, -1, a), one rounding).  SWIZZLE: the
+// partner's value through ds_swizzle (the LDS pipe) for every lane distance,
+// one VALU operation per value; otherwise DPP for distances 1 and 2 (a VALU
+// move each, but shorter latency).
+template <int MASK, int U, bool SWIZZLE>
 __device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
 {
     const float sgn = (lane & MASK) ? -1.f : 1.f;
@@ -34,7 +37,8 @@ __device__ __forceinline__ void lane_stage8(float (&v)[U][8], int lane)
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float p = __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[u][r])));
+            const float p = SWIZZLE ? __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[u][r]), 0x1F | (MASK << 10)))
+                                    : __uint_as_float(lane_xor_u<MASK>(__float_as_uint(v[u][r])));
             v[u][r] = __builtin_fmaf(v[u][r], sgn, p);
         }
 }
@@ -88,12 +92,15 @@ __device__ __forceinline__ uint32_t row_max_bits_wave(const uint32_t *wave_max_b
 //     first barrier publishes them, and every reader takes the maximum over
 //     the waves (as unsigned integers, which orders non-negative floats; at
 //     most 8 waves); the other waves may then meet the first barrier whenever
-//     they like.  Each chunk's 8 codes go out
-// through store(m, c, even, odd): even holds the codes of columns 8c + 0, 2,
-// 4, 6 (bytes 0..3), odd those of 8c + 1, 3, 5, 7.  Barriers: the
-// workgroup's two (counters published; codes stored), met by every other wave
-// in the same order.
-template <int M, int G, int CPR, bool WAVE_MAXIMA, typename Store>
+//     they like.
+// SWIZZLE: every cross-lane butterfly stage through ds_swizzle (lane_stage8),
+// one VALU operation fewer per value at lane distances 1 and 2 (for a rotation
+// bounded by its VALU work rather than its latency).  Each chunk's 8 codes go
+// out through store(m, c, even, odd): even holds the codes of columns 8c + 0,
+// 2, 4, 6 (bytes 0..3), odd those of 8c + 1, 3, 5, 7.  Barriers: the
+// workgroup's two (counters published or maxima published; codes stored), met
+// by every other wave in the same order.
+template <int M, int G, int CPR, bool WAVE_MAXIMA, bool SWIZZLE, typename Store>
 __device__ __forceinline__ void rotate_rows(const uint16_t *__restrict__ x, int64_t ldx, float qmax, int K,
                                             int rt, int rstride, int nwr, int lane, uint32_t *amax,
                                             uint32_t *arrived, Store store)
@@ -139,11 +146,11 @@ __device__ __forceinline__ void rotate_rows(const uint16_t *__restrict__ x, int6
                     v[u][r] = a + b;
                     v[u][r + h] = a - b;
                 }
-    if constexpr (G >= 16) lane_stage8<1, M * CPR>(v, lane);
-    if constexpr (G >= 32) lane_stage8<2, M * CPR>(v, lane);
-    if constexpr (G >= 64) lane_stage8<4, M * CPR>(v, lane);
-    if constexpr (G >= 128) lane_stage8<8, M * CPR>(v, lane);
-    if constexpr (G >= 256) lane_stage8<16, M * CPR>(v, lane);
+    if constexpr (G >= 16) lane_stage8<1, M * CPR, SWIZZLE>(v, lane);
+    if constexpr (G >= 32) lane_stage8<2, M * CPR, SWIZZLE>(v, lane);
+    if constexpr (G >= 64) lane_stage8<4, M * CPR, SWIZZLE>(v, lane);
+    if constexpr (G >= 128) lane_stage8<8, M * CPR, SWIZZLE>(v, lane);
+    if constexpr (G >= 256) lane_stage8<16, M * CPR, SWIZZLE>(v, lane);
     // Row absmax over the rotation waves.  Atomic form: LDS atomic maximum, then
     // an arrival count that every rotation wave waits on (they are all resident
     // in this workgroup, so the wait ends).  Per-wave form: each wave's maxima,

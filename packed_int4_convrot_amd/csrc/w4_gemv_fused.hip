@@ -189,7 +189,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_fused_kernel(
         // Chunk c is columns 8 (c % 4) .. + 7 of 32-column piece c / 4: its even
         // columns go to bytes 4 (c % 4) .. + 3 of the piece's first 16 bytes, its
         // odd columns to the same bytes of the next 16.
-        rotate_rows<M, G, CPR, false>(x, ldx, qmax, K, (int)threadIdx.x - kWave * NWS, kWave * nwr, nwr, lane, sh.amax,
+        rotate_rows<M, G, CPR, false, false>(x, ldx, qmax, K, (int)threadIdx.x - kWave * NWS, kWave * nwr, nwr, lane, sh.amax,
                                &sh.arrived, [&](int m, int c, uint32_t even, uint32_t odd) {
                                    uint8_t *piece = s_codes + m * K + 32 * (c >> 2) + 4 * (c & 3);
                                    *reinterpret_cast<uint32_t *>(piece) = even;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(1024) void w4_skinny_fused_kernel(
                 *(__attribute__((address_space(3))) u32x2 *)(codes + code_offset(rt >> 3, (rt >> 1) & 3, m) +
                                                              8 * (rt & 1)) = u32x2{0u, 0u};
         }
-        rotate_rows<M, G, 1, true>(x, ldx, qmax, K, rt, kWave * kSfRotWaves, kSfRotWaves, lane, &sh.wmax[0][0],
+        rotate_rows<M, G, 1, true, true>(x, ldx, qmax, K, rt, kWave * kSfRotWaves, kSfRotWaves, lane, &sh.wmax[0][0],
                                    nullptr, [&](int m, int c, uint32_t even, uint32_t odd) {
                                  *(__attribute__((address_space(3))) u32x2 *)(codes + code_offset(c >> 3, (c >> 1) & 3, m) +
                                                                               8 * (c & 1)) = u32x2{even, odd};
