@@ -191,7 +191,7 @@ size_t ck_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * both on `stream`; for 1 <= M <= 4 one launch instead (M <= 3 when
  * K > 8192), with one workgroup per compute unit, whose rotation waves
  * rotate and quantise the rows into LDS while its other waves stream the
- * weights (same codes, same results bit for bit); for 6 <= M <= 8 with
+ * weights (same codes, same results bit for bit); for 5 <= M <= 8 with
  * K <= 4096 and N >= 8192 one launch too, its products on int8 MFMA (the
  * same results as ck_rotate_quant + ck_w4_gemm_q bit for bit).  Otherwise,
  * for 6 <= M <= 64 the codes are held in the few-row kernel's operand layout
@@ -237,7 +237,7 @@ ck_status ck_w4a4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, i
  *     ceil(M / 16) * 16 * K bytes (the few-row kernel's 16-row tiles) or M * K
  *     bytes (the GEMV), each rounded up to 256, plus 4 * M bytes of row
  *     scales rounded up to 256; the one-launch decode shapes (M <= 4, or
- *     M <= 3 when K > 8192; 6 <= M <= 8 with K <= 4096 and N >= 8192) use
+ *     M <= 3 when K > 8192; 5 <= M <= 8 with K <= 4096 and N >= 8192) use
  *     no scratch.
  *     For example M = 8192 rows fit up to K = 16384, and M = 16384 rows up
  *     to K = 8192.
@@ -334,7 +334,7 @@ ck_status ck_test_rotate_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ld
 
 /* The whole linear (bits 8: ck_w4a8_linear, bits 4: ck_w4a4_linear; same
  * arguments without the workspace) always on its one-launch MFMA form, which
- * those entry points choose only for 6 to 8 rows and N >= 8192, so that every
+ * those entry points choose only for 5 to 8 rows and N >= 8192, so that every
  * launch shape of that kernel can be checked: 1 <= M <= 8, K <= 4096, any N
  * (CK_ERR_UNSUPPORTED otherwise).  Results equal ck_rotate_quant followed by
  * ck_w4_gemm_q on the few-row kernel bit for bit. */

@@ -297,12 +297,13 @@ int gemm_q_common(const char *fn, bool gemv, const int8_t *codes, int64_t ldq, c
 // when the weights span at least kMfmaFusedMinN rows (32 or more per CU on a
 // 256-CU MI355X); the VALU GEMV form (w4_gemv_fused) up to 4 rows otherwise.
 // Measured on MI355X (K = 3840, graph replay, cold weights): at N = 10240 the
-// MFMA form takes 10.8 / 11.3 / 11.7 us at M = 6 / 7 / 8 against 12.2 / 12.5 /
-// 12.5 us for rotate-quant + the few-row kernel, but 9.1 / 9.8 / 10.5 us at M =
-// 2 / 3 / 4 against 7.1 / 8.2 / 9.5 us for the VALU form, and at N = 3840, M =
-// 8 it takes 9.9 us against 8.7 us: every CU rotates all the rows, which is
-// the longer part once the CU's share of the weights is small.
-constexpr int64_t kMfmaFusedMinRows = 6, kMfmaFusedMinN = 8192;
+// MFMA form takes 10.0 / 10.3 / 10.8 / 11.2 us at M = 5 / 6 / 7 / 8 against
+// 10.8 / 12.2 / 12.5 / 12.5 us for two launches (rotate-quant + the VALU GEMV at
+// M = 5, + the few-row kernel above), but 8.9 / 9.3 / 9.8 us at M = 2 / 3 / 4
+// against 7.1 / 8.2 / 9.5 us for the VALU form, and at N = 3840, M = 8 it
+// takes 9.6 us against 8.5 us: every CU rotates all the rows, which is the
+// longer part once the CU's share of the weights is small.
+constexpr int64_t kMfmaFusedMinRows = 5, kMfmaFusedMinN = 8192;
 struct LinearPlan {
     bool fused;           // one launch (either form)
     bool mfma_fused;      // ... the MFMA form

@@ -112,12 +112,13 @@ int launch_w4_gemv_fused(const uint16_t *x, int64_t ldx, int G, int qmax, int M,
 // 2048) slices of 32 K-groups for each of t tiles of 16 weight rows; the
 // workgroup's rows, a multiple of 8, fill t tiles except perhaps 8 rows of the
 // last) and kSfRotWaves rotation waves (one 8-column chunk per thread and row).
-// lds: t * s slices of 16 rows (kSfSlicePitch bytes apart), their partial sums
-// (2 KiB each) and the codes (kSfCodeGroup bytes per K-group, 32 s groups),
+// lds: t * s slices of 16 rows (kSfSlicePitch bytes apart), their weight scales
+// (kSfScaleDwords each) and partial sums (2 KiB each: two 16-group blocks), and
+// the codes (kSfCodeGroup bytes per K-group, 32 s groups),
 // raised above half the CU's LDS when the grid fits the chip, so that no CU
 // runs two workgroups.
 constexpr int kSfMaxRows = 8, kSfRotWaves = 8, kSfGroupsPerWave = 32, kSfMaxStreamWaves = 8;
-constexpr int kSfSlicePitch = 1040, kSfCodeGroup = 576;
+constexpr int kSfSlicePitch = 1040, kSfCodeGroup = 576, kSfScaleDwords = 256;
 constexpr int kSfMaxLds = 160 * 1024 - 512;  // the CU's LDS less the static counters (at most 288 bytes)
 struct SkinnyFusedShape {
     int nb, rows, t, s, nws, lds;
@@ -128,7 +129,8 @@ inline bool w4_skinny_fused_shape(int64_t M, int64_t K, int64_t N, int ncu, Skin
         ncu < 1)
         return false;
     const int64_t ng = K / 64, s = (ng + kSfGroupsPerWave - 1) / kSfGroupsPerWave;
-    const int64_t per_wave = 16 * kSfSlicePitch + 2 * 1024, codes = (int64_t)kSfCodeGroup * kSfGroupsPerWave * s;
+    const int64_t per_wave = 16 * kSfSlicePitch + 4 * kSfScaleDwords + 2 * 1024;
+    const int64_t codes = (int64_t)kSfCodeGroup * kSfGroupsPerWave * s;
     int64_t tmax = (kSfMaxLds - codes) / (s * per_wave);
     if (tmax * s > kSfMaxStreamWaves)
         tmax = kSfMaxStreamWaves / s;

@@ -1,6 +1,6 @@
 // Whole W4A8/W4A4 linear for 1 <= M <= 8 activation rows in one launch: the
 // rotate-quant of the bf16 rows and the packed-int4 matmul on int8 MFMA, one
-// workgroup per compute unit.  The linear takes it for 6 to 8 rows when the
+// workgroup per compute unit.  The linear takes it for 5 to 8 rows when the
 // weights span at least 8192 rows; every shape is reachable through a test
 // entry point.
 //
@@ -94,7 +94,12 @@ __global__ __launch_bounds__(1024) void w4_skinny_fused_kernel(
     const int ng = K / 64;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     lds_u8 *codes = smem + NWS * kSlice;  // [32 S groups][576]
-    uint32_t *red = reinterpret_cast<uint32_t *>(smem_generic + NWS * kSlice + kSfCodeGroup * kGpw * S);  // [NWS][2][64][4]
+    // [NWS][kSwLd][64] scale dwords, then [units][64][4] partial sums
+    constexpr int kSwLd = PER_GROUP ? kGpw / 8 : 1;
+    uint32_t *scl = reinterpret_cast<uint32_t *>(smem_generic + NWS * kSlice + kSfCodeGroup * kGpw * S);
+    uint32_t *red = scl + NWS * kSfScaleDwords;
+    const int n0 = xcd_block(blockIdx.x, gridDim.x) * rows;
+    const int nrows = min(rows, N - n0);
 
     if (wave < kSfRotWaves) {
         // Chunks past K up to the last slice's end hold zero codes, so that
@@ -107,164 +112,168 @@ __global__ __launch_bounds__(1024) void w4_skinny_fused_kernel(
                                                              8 * (rt & 1)) = u32x2{0u, 0u};
         }
         rotate_rows<M, G, 1, true, true>(x, ldx, qmax, K, rt, kWave * kSfRotWaves, kSfRotWaves, lane, &sh.wmax[0][0],
-                                   nullptr, [&](int m, int c, uint32_t even, uint32_t odd) {
-                                 *(__attribute__((address_space(3))) u32x2 *)(codes + code_offset(c >> 3, (c >> 1) & 3, m) +
-                                                                              8 * (c & 1)) = u32x2{even, odd};
-                             });
-        return;
-    }
-
-    const int n0 = xcd_block(blockIdx.x, gridDim.x) * rows;
-    const int nrows = min(rows, N - n0);
-    const int sw = wave - kSfRotWaves;  // streaming wave
-    const int t = sw / S, g0 = (sw % S) * kGpw;
-    const int tr0 = 16 * t;  // the tile's first row in the workgroup
-    const int cnt = max(0, min(kGpw, ng - g0));
-    const int col = lane % 16, kb = lane / 16;
-    lds_u8 *slice = smem + sw * kSlice;
-
-    if (sw == 0 && lane < kSfMaxStreamWaves)
-        sh.done[lane] = 0;  // read after the second barrier
-
-    // Per-group weight scales, one dword per lane and 8 groups: lane l holds
-    // the scales of columns 2 (l % 8) and + 1 of the tile in group g0 + l / 8
-    // (+ 8 q); each lane takes its column's scale from that lane by ds_bpermute.
-    constexpr int kSwLd = PER_GROUP ? kGpw / 8 : 1;
-    uint32_t swd[kSwLd];
-    if constexpr (PER_GROUP) {
-        const int cs = min(n0 + tr0 + 2 * (lane % 8), N - 2);  // a half tile at the end of N reads column N - 2
-#pragma unroll
-        for (int q = 0; q < kSwLd; ++q)
-            swd[q] = *reinterpret_cast<const uint32_t *>(w_scales + (int64_t)min(g0 + 8 * q + lane / 8, ng - 1) * N + cs);
-    }
-    // The weight slice: instruction r copies row r's 1 KiB (lane l: chunk l).
-    // Rows past the workgroup's end are not loaded (their outputs are not stored).
-    const uint8_t *wrow = packed + (int64_t)(n0 + tr0) * ldw + 32 * g0 + 16 * lane;
-    const bool wlive = lane < 2 * cnt;
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        if (wlive && tr0 + r < nrows)
-            __builtin_amdgcn_global_load_lds(wrow + r * ldw, slice + kPitch * r, 16, 0, 0);
-    // The weights are requested from the first instructions on; the rotation
-    // waves' two barriers (maxima published, codes stored) are met here.
-    barrier_lds_only();
-    barrier_lds_only();
-    wait_vmcnt0();  // this wave's scales and slice have landed
-
-    // Every group runs without a branch: past K the slice holds stale bytes and
-    // the activation operand is zero.  Groups go in batches of kBatch, software
-    // pipelined: the LDS reads of batch b + 1 are issued before the MFMAs and
-    // scale folds of batch b, so each batch waits only for reads issued a
-    // batch earlier.
-    // Rows M .. 15 of the activation operand hold whatever the LDS holds there:
-    // MFMA rows are independent, and those rows' outputs are never stored.
-    const lds_u8 *abase = codes + code_offset(g0, kb, col & 7);
-    const lds_u8 *bbase = slice + col * kPitch + 16 * (kb >> 1) + 8 * (kb & 1);
-    float y[2][4];
-    v4i acc = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            y[h][i] = 0.f;
-    constexpr int kBatch = 4, kNb = kGpw / kBatch;
-    // This lane's bf16 scale from a pair of columns, into the high half.
-    const uint32_t ssel = (col & 1) ? 0x03020C0Cu : 0x01000C0Cu;
-    u32x4 ar[2][kBatch];
-    u32x2 wq[2][kBatch];
-    uint32_t pair[2][kBatch];
-    auto read_batch = [&](int b) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int j = b * kBatch + u;
-            // groups past K read the allocated but unwritten codes (zeroed below)
-            ar[b & 1][u] = *(const __attribute__((address_space(3))) u32x4 *)(abase + kSfCodeGroup * j);
-            wq[b & 1][u] = *(const __attribute__((address_space(3))) u32x2 *)(bbase + 32 * j);
-            if constexpr (PER_GROUP)
-                pair[b & 1][u] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * ((j % 8) * 8 + col / 2), (int)swd[j / 8]);
-        }
-    };
-    read_batch(0);
-#pragma unroll
-    for (int b = 0; b < kNb; ++b) {
-        if (b + 1 < kNb)
-            read_batch(b + 1);
-        v4i d[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int j = b * kBatch + u;
-            const u32x4 &ra = ar[b & 1][u];
-            const v4i a = v4i{(int)ra[0], (int)ra[1], (int)ra[2], (int)ra[3]};
-            const v4i bw = w4_operand_x16(wq[b & 1][u][0], wq[b & 1][u][1]);
-            if constexpr (PER_GROUP)
-                d[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw, v4i{0, 0, 0, 0}, 0, 0, 0);
-            else
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw, acc, 0, 0, 0);
-        }
-        if constexpr (PER_GROUP) {
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int j = b * kBatch + u;
-                const float sc = __uint_as_float(perm(0u, pair[b & 1][u], ssel));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    y[j / kHalf][i] = __builtin_fmaf(sc, (float)d[u][i], y[j / kHalf][i]);
-            }
-            // Keep each batch's scale folds with its MFMAs: left alone, the
-            // compiler issued all 32 MFMAs first and folded afterwards, which
-            // needs more registers than 16 waves per CU leave (60-65 spilled).
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    asm volatile("" : "+v"(y[h][i]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // Partials to LDS; the last of the tile's S waves sums them in group order.
-    uint32_t *mine = red + (sw * 2 * kWave + lane) * 4;
-    if constexpr (PER_GROUP) {
-        *reinterpret_cast<float4 *>(mine) = make_float4(y[0][0], y[0][1], y[0][2], y[0][3]);
-        *reinterpret_cast<float4 *>(mine + 4 * kWave) = make_float4(y[1][0], y[1][1], y[1][2], y[1][3]);
+                                         nullptr, [&](int m, int c, uint32_t even, uint32_t odd) {
+                                             *(__attribute__((address_space(3))) u32x2 *)(
+                                                 codes + code_offset(c >> 3, (c >> 1) & 3, m) + 8 * (c & 1)) =
+                                                 u32x2{even, odd};
+                                         });
+        barrier_lds_only();  // every slice and its scales are in LDS
     } else {
-        *reinterpret_cast<int4 *>(mine) = make_int4(acc[0], acc[1], acc[2], acc[3]);
-    }
-    uint32_t prior = 0;
-    if (lane == 0)
-        prior = __hip_atomic_fetch_add(&sh.done[t], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(prior) != (uint32_t)(S - 1))
-        return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // Lane (col, kb) holds D[4 kb + i][col]: activation rows 4 kb + i, weight row col.
-    if (tr0 + col >= nrows)
-        return;
-    const int n = n0 + tr0 + col;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * kb + i;
-        if (m >= M)
-            break;
-        float yv;
+        const int sw = wave - kSfRotWaves;  // streaming wave: tile sw / S, K-slice sw % S
+        const int t = sw / S, g0 = (sw % S) * kGpw, tr0 = 16 * t;
+        const int cnt = max(0, min(kGpw, ng - g0));
+        lds_u8 *slice = smem + sw * kSlice;
+        if (sw == 0 && lane < kSfMaxStreamWaves)
+            sh.done[lane] = 0;  // read after the workgroup's last barrier
+        // Per-group weight scales, one dword per lane and 8 groups: lane l holds
+        // the scales of columns 2 (l % 8) and + 1 of the tile in group g0 + l / 8
+        // (+ 8 q); they go to LDS for whichever wave multiplies these groups.
+        uint32_t swd[kSwLd];
         if constexpr (PER_GROUP) {
-            float s = 0.f;
-            for (int w = t * S; w < t * S + S; ++w)
-                for (int h = 0; h < 2; ++h)
-                    if ((w % S) * kGpw + h * kHalf < ng)  // the few-row kernel's waves that hold groups
-                        s += __uint_as_float(red[((w * 2 + h) * kWave + lane) * 4 + i]);
-            yv = s * 0.0625f;
-        } else {
-            int s = 0;
-            for (int w = t * S; w < t * S + S; ++w)
-                s += (int)red[(w * 2 * kWave + lane) * 4 + i];
-            yv = bf16_to_f32(w_scales[n]) * ((float)s * 0.0625f);
+            const int cs = min(n0 + tr0 + 2 * (lane % 8), N - 2);  // a half tile at the end of N reads column N - 2
+#pragma unroll
+            for (int q = 0; q < kSwLd; ++q)
+                swd[q] = *reinterpret_cast<const uint32_t *>(w_scales + (int64_t)min(g0 + 8 * q + lane / 8, ng - 1) * N +
+                                                             cs);
         }
-        const float am = __uint_as_float(row_max_bits(&sh.wmax[0][0], m, M, kSfRotWaves));
-        const float sx = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;  // the rotate-quant kernel's row scale
-        yv *= sx * x_scale;
-        if (bias)
-            yv += bf16_to_f32(bias[n]);
-        out[(int64_t)m * ldo + n] = f32_to_bf16(yv);
+        // The weight slice: instruction r copies row r's 1 KiB (lane l: chunk l).
+        // Rows past the workgroup's end are not loaded (their outputs are not stored).
+        const uint8_t *wrow = packed + (int64_t)(n0 + tr0) * ldw + 32 * g0 + 16 * lane;
+        const bool wlive = lane < 2 * cnt;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (wlive && tr0 + r < nrows)
+                __builtin_amdgcn_global_load_lds(wrow + r * ldw, slice + kPitch * r, 16, 0, 0);
+        // The weights are requested from the first instructions on; the rotation
+        // waves' two barriers (maxima published, codes stored) are met here
+        // without waiting for them.
+        barrier_lds_only();
+        barrier_lds_only();
+        wait_vmcnt0();  // this wave's scales and slice have landed
+        if constexpr (PER_GROUP) {
+#pragma unroll
+            for (int q = 0; q < kSwLd; ++q)
+                scl[(sw * kSwLd + q) * kWave + lane] = swd[q];
+        }
+        barrier_lds_only();  // every slice and its scales are in LDS
+    }
+
+    // Every wave now multiplies: unit u = (tile u / nh, block u % nh) covers 16
+    // K-groups of one tile, the groups of one wave of the few-row kernel, so its
+    // fp32 partial sum (per-group scales folded in group order) is one of that
+    // kernel's, and the last unit of a tile to finish adds them in block order.
+    // Groups past K multiply zero codes.  Rows M .. 15 of the activation operand
+    // hold whatever the LDS holds there: MFMA rows are independent, and those
+    // rows' outputs are never stored.
+    const int nh = (ng + kHalf - 1) / kHalf, units = (NWS / S) * nh;
+    for (int u = wave; u < units; u += (int)blockDim.x / kWave) {
+        // The lane's role, derived here rather than kept live through the
+        // rotation above (at 8 rows that spilled a register).
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int col = tid % 16, kb = (tid % kWave) / 16;
+        // This lane's bf16 scale from a pair of columns, into the high half.
+        const uint32_t ssel = (col & 1) ? 0x03020C0Cu : 0x01000C0Cu;
+        const int t = u / nh, h = u % nh, tr0 = 16 * t;
+        const int sl = t * S + h / 2;                 // the slice (streaming wave) holding these groups
+        const int jo = (h % 2) * kHalf;               // their first group within the slice
+        const lds_u8 *abase = codes + code_offset(kGpw * (h / 2) + jo, kb, col & 7);
+        const lds_u8 *bbase = smem + sl * kSlice + col * kPitch + 32 * jo + 16 * (kb >> 1) + 8 * (kb & 1);
+        const uint32_t *sbase = scl + sl * kSwLd * kWave + col / 2;
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        v4i acc = v4i{0, 0, 0, 0};
+        constexpr int kBatch = 4, kNb = kHalf / kBatch;
+        u32x4 ar[2][kBatch];
+        u32x2 wq[2][kBatch];
+        uint32_t pair[2][kBatch];
+        // Software pipelined: the LDS reads of batch b + 1 are issued before the
+        // MFMAs and scale folds of batch b.
+        auto read_batch = [&](int b) {
+#pragma unroll
+            for (int e = 0; e < kBatch; ++e) {
+                const int j = b * kBatch + e;         // group jo + j of the slice
+                ar[b & 1][e] = *(const __attribute__((address_space(3))) u32x4 *)(abase + kSfCodeGroup * j);
+                wq[b & 1][e] = *(const __attribute__((address_space(3))) u32x2 *)(bbase + 32 * j);
+                if constexpr (PER_GROUP) {
+                    const int js = jo + j;             // lane (js % 8) * 8 + col / 2 of dword js / 8 holds the pair
+                    pair[b & 1][e] = sbase[(js / 8) * kWave + (js % 8) * 8];
+                }
+            }
+        };
+        read_batch(0);
+#pragma unroll
+        for (int b = 0; b < kNb; ++b) {
+            if (b + 1 < kNb)
+                read_batch(b + 1);
+            v4i d[kBatch];
+#pragma unroll
+            for (int e = 0; e < kBatch; ++e) {
+                const u32x4 &ra = ar[b & 1][e];
+                const v4i a = v4i{(int)ra[0], (int)ra[1], (int)ra[2], (int)ra[3]};
+                const v4i bw = w4_operand_x16(wq[b & 1][e][0], wq[b & 1][e][1]);
+                if constexpr (PER_GROUP)
+                    d[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw, v4i{0, 0, 0, 0}, 0, 0, 0);
+                else
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw, acc, 0, 0, 0);
+            }
+            if constexpr (PER_GROUP) {
+#pragma unroll
+                for (int e = 0; e < kBatch; ++e) {
+                    const float sc = __uint_as_float(perm(0u, pair[b & 1][e], ssel));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        y[i] = __builtin_fmaf(sc, (float)d[e][i], y[i]);
+                }
+                // Keep each batch's scale folds with its MFMAs: left alone, the
+                // compiler issued all the MFMAs first and folded afterwards, which
+                // needs more registers than 16 waves per CU leave.
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    asm volatile("" : "+v"(y[i]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // The partial to LDS; the last of the tile's nh units adds them in block order.
+        uint32_t *mine = red + (u * kWave + lane) * 4;
+        if constexpr (PER_GROUP)
+            *reinterpret_cast<float4 *>(mine) = make_float4(y[0], y[1], y[2], y[3]);
+        else
+            *reinterpret_cast<int4 *>(mine) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+        uint32_t prior = 0;
+        if (lane == 0)
+            prior = __hip_atomic_fetch_add(&sh.done[t], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(prior) != (uint32_t)(nh - 1))
+            continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // Lane (col, kb) holds D[4 kb + i][col]: activation rows 4 kb + i, weight row col.
+        if (tr0 + col < nrows) {
+            const int n = n0 + tr0 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * kb + i;
+                if (m >= M)
+                    break;
+                float yv;
+                if constexpr (PER_GROUP) {
+                    float sum = 0.f;
+                    for (int hh = 0; hh < nh; ++hh)
+                        sum += __uint_as_float(red[((t * nh + hh) * kWave + lane) * 4 + i]);
+                    yv = sum * 0.0625f;
+                } else {
+                    int sum = 0;
+                    for (int hh = 0; hh < nh; ++hh)
+                        sum += (int)red[((t * nh + hh) * kWave + lane) * 4 + i];
+                    yv = bf16_to_f32(w_scales[n]) * ((float)sum * 0.0625f);
+                }
+                const float am = __uint_as_float(row_max_bits(&sh.wmax[0][0], m, M, kSfRotWaves));
+                const float sx = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;  // the rotate-quant kernel's row scale
+                yv *= sx * x_scale;
+                if (bias)
+                    yv += bf16_to_f32(bias[n]);
+                out[(int64_t)m * ldo + n] = f32_to_bf16(yv);
+            }
+        }
     }
 }
 

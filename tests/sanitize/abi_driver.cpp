@@ -216,11 +216,11 @@ stub::Kernel expected_kernel(int64_t M, int64_t K)
     return skinny ? stub::Kernel::kSkinny : stub::Kernel::kGemm;
 }
 
-// The whole linear in one launch: the MFMA form for 6 to 8 rows, K <= 4096 and
+// The whole linear in one launch: the MFMA form for 5 to 8 rows, K <= 4096 and
 // at least 8192 weight rows, else the VALU GEMV form (up to 4 rows).
 stub::Kernel expected_fused(int64_t M, int64_t K, int64_t N)
 {
-    if (M >= 6 && M <= 8 && K >= 64 && K <= 4096 && K % 64 == 0 && N >= 8192)
+    if (M >= 5 && M <= 8 && K >= 64 && K <= 4096 && K % 64 == 0 && N >= 8192)
         return stub::Kernel::kSkinnyFused;
     if (ck::w4_gemv_fused_supports(M, K))
         return stub::Kernel::kGemvFused;
@@ -441,7 +441,7 @@ void test_fused_gemv_shapes()
 
 // The one-launch MFMA linear: its workgroup shapes (one workgroup per CU,
 // every LDS byte inside the CU, the rows of N covered once), the linear's own
-// choice of it (6 to 8 rows, N >= 8192), and its test entry point for any N.
+// choice of it (5 to 8 rows, N >= 8192), and its test entry point for any N.
 void test_mfma_one_launch()
 {
     for (int64_t M = 1; M <= 9; ++M)
@@ -458,14 +458,15 @@ void test_mfma_one_launch()
                     EXPECT(sh.s == s && sh.rows % 8 == 0 && sh.rows >= 8 && sh.t == (sh.rows + 15) / 16);
                     EXPECT(sh.nws == sh.t * sh.s && sh.nws + ck::kSfRotWaves <= 16);
                     EXPECT((int64_t)sh.nb * sh.rows >= N && (int64_t)(sh.nb - 1) * sh.rows < N);
-                    const int64_t need = (int64_t)sh.nws * (16 * ck::kSfSlicePitch + 2048) + ck::kSfCodeGroup * 32 * s;
+                    const int64_t need = (int64_t)sh.nws * (16 * ck::kSfSlicePitch + 4 * ck::kSfScaleDwords + 2048) +
+                                        ck::kSfCodeGroup * 32 * s;
                     EXPECT(sh.lds >= need && sh.lds <= ck::kSfMaxLds);
                     EXPECT(sh.nb > ncu || sh.lds > 80 * 1024);
                 }
     // N = 10240 on 256 CUs: 40 rows (two tiles and a half tile) per workgroup.
     ck::SkinnyFusedShape sh;
     EXPECT(ck::w4_skinny_fused_shape(8, 3840, 10240, 256, sh) && sh.nb == 256 && sh.rows == 40 && sh.nws == 6);
-    for (int64_t M : {5, 6, 8})
+    for (int64_t M : {4, 5, 6, 8})
         for (int64_t N : {8176, 8192}) {
             Pool pool;
             const int64_t K = 3840, ldx = K, ldo = N;
@@ -477,9 +478,14 @@ void test_mfma_one_launch()
             stub::reset();
             EXPECT(ck_w4a8_linear(x, M, K, ldx, 64, w.packed, w.ldw, w.scales, 1, 64, N, nullptr, 1.f, out, ldo,
                                   ws, need, nullptr) == CK_OK);
-            const bool mfma = M >= 6 && N >= 8192;
-            EXPECT(mfma ? stub::calls == 1 && stub::last.kernel == stub::Kernel::kSkinnyFused
-                        : stub::calls == 2 && stub::last.kernel != stub::Kernel::kSkinnyFused);
+            // 4 rows: the VALU one-launch form; 5 to 8 rows and N >= 8192: the MFMA one;
+            // otherwise two launches.
+            const stub::Kernel one = M >= 5 && N >= 8192 ? stub::Kernel::kSkinnyFused
+                                     : M <= 4            ? stub::Kernel::kGemvFused
+                                                         : stub::Kernel::kNone;
+            EXPECT(one == expected_fused(M, K, N));
+            EXPECT(one != stub::Kernel::kNone ? stub::calls == 1 && stub::last.kernel == one
+                                              : stub::calls == 2 && stub::last.kernel != stub::Kernel::kSkinnyFused);
         }
     {
         Pool pool;

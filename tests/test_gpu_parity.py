@@ -395,8 +395,8 @@ FUSED_CASES = [(1, 3840), (2, 3840), (3, 3840), (4, 3840), (1, 64), (4, 64), (2,
 
 
 def mfma_one_launch(M, K, N):
-    """The whole linear runs the one-launch MFMA kernel (6 to 8 rows, K <= 4096, N >= 8192)."""
-    return 6 <= M <= 8 and K <= 4096 and N >= 8192
+    """The whole linear runs the one-launch MFMA kernel (5 to 8 rows, K <= 4096, N >= 8192)."""
+    return 5 <= M <= 8 and K <= 4096 and N >= 8192
 
 
 def padded_two_launch(xd, G, bits, wd, sd, per_group, bd, x_scale):
@@ -452,7 +452,7 @@ def test_mfma_decode_linear_launch_shapes(M, K, G):
     the CUs, at N = 16384), both bit widths and scale kinds, a zero row, bias and an
     input scale: bit for bit against rotate-quant + the few-row kernel, and against the
     oracle's epilogue on the same codes.  Where the linear's own plan picks this kernel
-    (6 to 8 rows, N >= 8192), ck_w4a8_linear / ck_w4a4_linear give the same bits."""
+    (5 to 8 rows, N >= 8192), ck_w4a8_linear / ck_w4a4_linear give the same bits."""
     Ns = [16, 48, 4112] + ([10240] if (K, G) == (3840, 64) else []) + ([16384] if K == 4096 else [])
     for N in Ns:
         for bits in (8, 4):
@@ -569,7 +569,7 @@ def _graph_replays_equal_eager(fn, out):
 
 
 def test_mfma_one_launch_in_the_linear_graph_strided_noalloc():
-    """Where the linear itself takes the one-launch MFMA kernel (6 to 8 rows, N >= 8192):
+    """Where the linear itself takes the one-launch MFMA kernel (5 to 8 rows, N >= 8192):
     a HIP graph replays it bit-identically with eager work between replays; a strided x
     (NaN padding past K) gives the dense result; and the allocation-free W4A4 entry,
     which needs no scratch on this path, equals the workspace entry."""
