@@ -31,17 +31,17 @@
 //     each a contiguous 1 KiB of that row, to LDS rows 1040 bytes apart (so the
 //     8-byte fragment reads of 16 rows hit 16 bank groups).  It meets the two
 //     barriers without waiting for that DMA (barrier_lds_only), then waits for
-//     its own loads;
-//   * each streaming wave multiplies its groups, A = codes (rows M .. 15 are
-//     whatever LDS holds there: MFMA rows are independent and those outputs
-//     are never stored; groups past K are zero codes), B = decoded weights.  A
-//     per-group scale is folded in right after the MFMA of its group, into one
-//     fp32 sum per 16 groups: the sums, and the order in which they are added,
-//     are those of the few-row kernel (16 groups per wave there), so the
-//     outputs equal rotate-quant + few-row kernel bit for bit;
-//   * the last of a tile's S waves to finish (an LDS arrival count) adds the
-//     partial sums in group order, applies the row scale, x_scale and bias and
-//     stores bf16.
+//     its own loads and copies its scales to LDS;
+//   * after a third barrier (every slice and its scales in LDS) every wave,
+//     the rotation waves included, multiplies units of 16 K-groups of one
+//     tile, A = codes (rows M .. 15 are whatever LDS holds there: MFMA rows are
+//     independent and those outputs are never stored; groups past K are zero
+//     codes), B = decoded weights.  A per-group scale is folded in right after
+//     the MFMA of its group: a unit's fp32 sum is one wave's sum of the
+//     few-row kernel (16 groups per wave there), in the same order;
+//   * the last unit of a tile to finish (an LDS arrival count) adds the units'
+//     sums in group order, applies the row scale, x_scale and bias and stores
+//     bf16, so the outputs equal rotate-quant + few-row kernel bit for bit.
 // Codes in LDS: the 16 codes of row r (< 8) and k-block kb of 64-column group
 // g (columns 64 g + 16 kb .. + 15, in the nibble decode's order 0,2,4,6,
 // 1,3,5,7, 8,10,12,14, 9,11,13,15) sit at 576 g + 144 kb + 16 r.  A rotation
@@ -70,7 +70,7 @@ static_assert(kP == 64 * 16 && kGpw == 2 * kHalf, "one DMA instruction per tile 
 template <int M>
 struct SfShared {
     uint32_t wmax[kSfRotWaves][M];     // each rotation wave's row absmax (fp32 bits)
-    uint32_t done[kSfMaxStreamWaves];  // waves of each tile whose partials are in LDS
+    uint32_t done[kSfMaxStreamWaves];  // units of each tile whose partial sums are in LDS
 };
 static_assert(sizeof(SfShared<kSfMaxRows>) + kSfMaxLds <= 160 * 1024, "static and dynamic LDS fit the CU");
 
