@@ -645,14 +645,14 @@ def launch_floor(torch, dev, stream):
 
 def extras(ck, workloads, torch, dev, bf16, u8, stream):
     res = {}
-    # decode GEMV at M = 4, 8 (cold weights)
+    # decode GEMV at M = 4, 5, 6, 8 (cold weights)
     name = "w4a8_decode_gemv_k3840_n10240_g64"
     w = workloads.WORKLOADS[name]
     K, N = w["K"], w["N"]
     base = workloads.workload_inputs(name, M=8)
     packs = [u8(base["packed"]) for _ in range(32)]
     scl = bf16(base["w_scales"])
-    for M in (4, 8):
+    for M in (4, 5, 6, 8):
         x = bf16(base["x"][:M])
         codes, rs = ck.rotate_quant(x, 64, 8)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
