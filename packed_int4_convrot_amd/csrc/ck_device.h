@@ -44,6 +44,17 @@ __device__ __forceinline__ int xcd_block(int b, int nblocks)
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Per-channel scale epilogue of every W4 matmul kernel: acc * (s_w * r) + b,
+// r = row scale * input scale, b = bias or 0, with one rounding for s_w * r and
+// one for the fused multiply-add.  With one formula in every kernel an output
+// row has the same bits whichever kernel, and so whichever batch size, computed
+// it.  acc is the exact integer dot product; a kernel that holds 2^k times it
+// passes s_w * 2^-k (the same products, as scaling by 2^k is exact).
+__device__ __forceinline__ float epilogue_channel(float acc, float sw, float r, float b)
+{
+    return __builtin_fmaf(acc, sw * r, b);
+}
+
 // fp32 -> bf16 bit pattern, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {

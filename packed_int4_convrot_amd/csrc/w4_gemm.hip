@@ -499,7 +499,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void w4_gemm_kernel(
                         float v[4];
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            v[t] = __builtin_fmaf((float)acc[i][j][4 * q + t], cs[q][t] * rsc[i], bc[q][t]);
+                            v[t] = epilogue_channel((float)acc[i][j][4 * q + t], cs[q][t], rsc[i], bc[q][t]);
                         const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                         *(__attribute__((address_space(3))) u32x2 *)(wt + ml * PITCH + (j * 32 + 8 * q + 4 * h) * 2) = pk;
                     }

@@ -148,10 +148,15 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_gemv_kernel(
         if constexpr (OUT_I32) {
             acc_out[(int64_t)m * lda + n] = (int32_t)t;
         } else {
-            float y = FSUM ? __uint_as_float(t) : bf16_to_f32(w_scales[n]) * (float)(int32_t)t;
-            y *= sx[m] * x_scale;
-            if (bias)
-                y += bf16_to_f32(bias[n]);
+            float y;
+            if constexpr (FSUM) {
+                y = __uint_as_float(t) * (sx[m] * x_scale);
+                if (bias)
+                    y += bf16_to_f32(bias[n]);
+            } else {
+                y = epilogue_channel((float)(int32_t)t, bf16_to_f32(w_scales[n]), sx[m] * x_scale,
+                                     bias ? bf16_to_f32(bias[n]) : 0.f);
+            }
             out[(int64_t)m * ldo + n] = f32_to_bf16(y);
         }
     }

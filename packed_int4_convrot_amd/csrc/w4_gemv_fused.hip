@@ -162,10 +162,15 @@ __device__ __forceinline__ void stream_role(float qmax, int K, const uint8_t *__
             t = add32<FSUM>(t, sh.red[rbl * S + k][r][m]);
         const float am = __uint_as_float(sh.amax[m]);
         const float sx = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;
-        float y = FSUM ? __uint_as_float(t) : bf16_to_f32(w_scales[n]) * (float)(int32_t)t;
-        y *= sx * x_scale;
-        if (bias)
-            y += bf16_to_f32(bias[n]);
+        float y;
+        if constexpr (FSUM) {
+            y = __uint_as_float(t) * (sx * x_scale);
+            if (bias)
+                y += bf16_to_f32(bias[n]);
+        } else {
+            y = epilogue_channel((float)(int32_t)t, bf16_to_f32(w_scales[n]), sx * x_scale,
+                                 bias ? bf16_to_f32(bias[n]) : 0.f);
+        }
         out[(int64_t)m * ldo + n] = f32_to_bf16(y);
     }
 }

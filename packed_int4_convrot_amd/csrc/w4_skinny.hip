@@ -228,16 +228,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
                     float s = 0.f;
                     for (int w = 0; w < ks; ++w)
                         s += __int_as_float(red_smem[w * MT * kWave * 4 + e]);
-                    yv = s * 0.0625f;
+                    yv = s * 0.0625f * (row_scales[m] * x_scale);
+                    if (bias)
+                        yv += bf16_to_f32(bias[nn]);
                 } else {
                     int s = 0;
                     for (int w = 0; w < ks; ++w)
                         s += red_smem[w * MT * kWave * 4 + e];
-                    yv = bf16_to_f32(w_scales[nn]) * ((float)s * 0.0625f);
+                    yv = epilogue_channel((float)s, 0.0625f * bf16_to_f32(w_scales[nn]), row_scales[m] * x_scale,
+                                          bias ? bf16_to_f32(bias[nn]) : 0.f);  // s = 16 * sum
                 }
-                yv *= row_scales[m] * x_scale;
-                if (bias)
-                    yv += bf16_to_f32(bias[nn]);
                 out[(int64_t)m * ldo + nn] = f32_to_bf16(yv);
             }
         }

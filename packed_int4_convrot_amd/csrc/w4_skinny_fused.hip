@@ -254,23 +254,23 @@ __global__ __launch_bounds__(1024) void w4_skinny_fused_kernel(
                 const int m = 4 * kb + i;
                 if (m >= M)
                     break;
+                const float am = __uint_as_float(row_max_bits(&sh.wmax[0][0], m, M, kSfRotWaves));
+                const float sx = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;  // the rotate-quant kernel's row scale
                 float yv;
                 if constexpr (PER_GROUP) {
                     float sum = 0.f;
                     for (int hh = 0; hh < nh; ++hh)
                         sum += __uint_as_float(red[((t * nh + hh) * kWave + lane) * 4 + i]);
-                    yv = sum * 0.0625f;
+                    yv = sum * 0.0625f * (sx * x_scale);
+                    if (bias)
+                        yv += bf16_to_f32(bias[n]);
                 } else {
                     int sum = 0;
                     for (int hh = 0; hh < nh; ++hh)
                         sum += (int)red[((t * nh + hh) * kWave + lane) * 4 + i];
-                    yv = bf16_to_f32(w_scales[n]) * ((float)sum * 0.0625f);
+                    yv = epilogue_channel((float)sum, 0.0625f * bf16_to_f32(w_scales[n]), sx * x_scale,
+                                          bias ? bf16_to_f32(bias[n]) : 0.f);  // sum = 16 * dot
                 }
-                const float am = __uint_as_float(row_max_bits(&sh.wmax[0][0], m, M, kSfRotWaves));
-                const float sx = am > 0.f ? (am / qmax) * kInvSqrtG : 1.0f;  // the rotate-quant kernel's row scale
-                yv *= sx * x_scale;
-                if (bias)
-                    yv += bf16_to_f32(bias[n]);
                 out[(int64_t)m * ldo + n] = f32_to_bf16(yv);
             }
         }

@@ -591,6 +591,38 @@ def test_mfma_one_launch_in_the_linear_graph_strided_noalloc():
     assert torch.equal(lin4, padded_two_launch(xd, 64, 4, wd, sd, True, bd, 1.0))
 
 
+@pytest.mark.parametrize("K,G,N", [(3840, 64, 10240), (3840, 16, 4112), (16384, 256, 4112)])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_per_channel_rows_same_bits_for_every_batch_size(K, G, N, bits):
+    """Per-channel scales: every kernel applies one epilogue, acc * (s_w * r) + b with
+    the exact integer sum acc, so a row's output does not depend on the batch it came
+    in, that is on which kernel the batch size picked.  On the same codes: the tiled
+    GEMM (72 rows) against the VALU GEMV (1 to 5 rows), the few-row MFMA kernel (6 to
+    32 rows at K = 3840; the GEMV at K = 16384).  Through the whole linear: 72 rows (the
+    tiled GEMM; W4A4 on packed codes) against the one-launch VALU linear (1 to 4 rows),
+    the one-launch MFMA linear (5 to 8 rows at N = 10240), the two-launch forms and the
+    few-row kernel on tiled codes (32 rows).  Per-group scales are folded in a different
+    order by each kernel and are held to the oracle's bar instead."""
+    Mbig = 72
+    inp = workloads.linear_inputs(Mbig, K, N, seed=K + G + bits, outliers=min(8, K // 8), scale="channel",
+                                  zero_rows=(2, 70), with_bias=True)
+    xd, wd = bf16_dev(inp["x"]), u8_dev(inp["packed"])
+    sd, bd = bf16_dev(inp["w_scales"]), bf16_dev(inp["bias"])
+    codes, scales = ck.rotate_quant(xd, G, bits)
+    rs = scales * np.float32(0.3)
+    ref = ck.gemm_q(codes, rs, wd, sd, False, bias=bd)
+    for m in (1, 2, 4, 5, 6, 8, 32):
+        sub = ck.gemm_q(codes[:m], rs[:m], wd, sd, False, bias=bd)
+        assert torch.equal(sub, ref[:m]), ("codes", m)
+        if m <= 8:
+            assert torch.equal(ck.gemv(codes[:m], rs[:m], wd, sd, False, bias=bd), sub), ("gemv", m)
+    lin = ck.linear(xd, G, bits, wd, sd, False, bias=bd, x_scale=0.3)
+    for m in (1, 3, 4, 5, 7, 8, 32):
+        assert torch.equal(ck.linear(xd[:m], G, bits, wd, sd, False, bias=bd, x_scale=0.3), lin[:m]), ("linear", m)
+    assert_output_close(host(lin[:8]), oracle.gemm_q(host(codes[:8]), host(scales[:8]), inp["packed"], inp["w_scales"],
+                                                      False, bias=inp["bias"], x_scale=0.3))
+
+
 def test_graph_replay_packed_w4a4_and_awq_gemm():
     """The packed W4A4 path (M > 64), the weight producer and the AWQ prefill GEMM
     replay from a HIP graph bit-identically."""
