@@ -143,6 +143,21 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
         load_weights();
     }
 
+    // The epilogue factors of this thread's first output (row scale, weight
+    // scale, bias), loaded after the operands and waited for with them, so
+    // that their latency does not follow the reduction barrier.
+    const int e0 = threadIdx.x;
+    const int m_e0 = min((e0 / (kWave * 4)) * 16 + 4 * ((e0 / 4) % kWave / 16) + e0 % 4, M - 1);
+    const int n_e0 = n0 + (e0 / 4) % kWave % 16;
+    float rs_e0 = 0.f, sw_e0 = 0.f, b_e0 = 0.f;
+    if constexpr (!OUT_I32) {
+        rs_e0 = row_scales[m_e0];
+        if constexpr (!PER_GROUP)
+            sw_e0 = bf16_to_f32(w_scales[n_e0]);
+        if (bias)
+            b_e0 = bf16_to_f32(bias[n_e0]);
+    }
+
     // 2. Activation operands in the decode order (tiled codes already are),
     //    zero for rows past M and groups past K.
     v4i a[GPW][MT];
@@ -210,7 +225,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
             *reinterpret_cast<int4 *>(dst) = make_int4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < MT * kWave * 4; e += blockDim.x) {
+    // Output e = (mt, lane l, i): row mt * 16 + 4 (l / 16) + i, column n0 + l % 16.
+    auto finish = [&](int e, float rsm, float swm, float bm) {
         const int mt = e / (kWave * 4);
         const int l = (e / 4) % kWave;
         const int i = e % 4;
@@ -228,19 +244,34 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4_skinny_kernel(
                     float s = 0.f;
                     for (int w = 0; w < ks; ++w)
                         s += __int_as_float(red_smem[w * MT * kWave * 4 + e]);
-                    yv = s * 0.0625f * (row_scales[m] * x_scale);
+                    yv = s * 0.0625f * (rsm * x_scale);
                     if (bias)
-                        yv += bf16_to_f32(bias[nn]);
+                        yv += bm;
                 } else {
                     int s = 0;
                     for (int w = 0; w < ks; ++w)
                         s += red_smem[w * MT * kWave * 4 + e];
-                    yv = epilogue_channel((float)s, 0.0625f * bf16_to_f32(w_scales[nn]), row_scales[m] * x_scale,
-                                          bias ? bf16_to_f32(bias[nn]) : 0.f);  // s = 16 * sum
+                    yv = epilogue_channel((float)s, 0.0625f * swm, rsm * x_scale, bm);  // s = 16 * sum
                 }
                 out[(int64_t)m * ldo + nn] = f32_to_bf16(yv);
             }
         }
+    };
+    if (e0 < MT * kWave * 4)
+        finish(e0, rs_e0, sw_e0, b_e0);
+    for (int e = e0 + blockDim.x; e < MT * kWave * 4; e += blockDim.x) {
+        const int l = (e / 4) % kWave;
+        const int m = min((e / (kWave * 4)) * 16 + 4 * (l / 16) + e % 4, M - 1);
+        const int nn = n0 + l % 16;
+        float rsm = 0.f, swm = 0.f, bm = 0.f;
+        if constexpr (!OUT_I32) {
+            rsm = row_scales[m];
+            if constexpr (!PER_GROUP)
+                swm = bf16_to_f32(w_scales[nn]);
+            if (bias)
+                bm = bf16_to_f32(bias[nn]);
+        }
+        finish(e, rsm, swm, bm);
     }
 }
 
