@@ -598,13 +598,14 @@ def _time_eager(torch, fn, stream, iters, warmup=3):
 WARM_S = 0.2   # seconds of the same work before each secondary measurement
 
 
-def _time(fn, stream, iters, warmup=3, warm_s=None):
-    """Microseconds per call, from a HIP graph of `iters` calls replayed once, after a
-    graph of `warmup` calls has been replayed for at least `warm_s` seconds (WARM_S by
-    default).  Under sustained load the chip's clocks keep rising for tens of
-    milliseconds: the M = 8192 GEMM at K = 3840 times 116 us per call after 3 warm-up
-    calls, 107 us after 100 and 97 us from 300 on, so each measurement first runs
-    long enough to reach that steady state."""
+def _time(fn, stream, iters, warmup=3, warm_s=None, reps=5):
+    """Microseconds per call: the median over `reps` timed replays of a HIP graph of
+    `iters` calls, after a graph of `warmup` calls has been replayed for at least
+    `warm_s` seconds (WARM_S by default).  Under sustained load the chip's clocks keep
+    rising for tens of milliseconds: the M = 8192 GEMM at K = 3840 times 116 us per
+    call after 3 warm-up calls, 107 us after 100 and 97 us from 300 on, so each
+    measurement first runs long enough to reach that steady state; the median keeps
+    one replay caught in a transient clock drop from setting the figure."""
     import torch
     g_w = capture(torch, fn, warmup)
     g = capture(torch, fn, iters)
@@ -615,11 +616,14 @@ def _time(fn, stream, iters, warmup=3, warm_s=None):
         if time.perf_counter() - t0 >= (WARM_S if warm_s is None else warm_s):
             break
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    g.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters * 1e3
+    per_call = []
+    for _ in range(reps):
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(a.elapsed_time(b) / iters * 1e3)
+    return sorted(per_call)[len(per_call) // 2]
 
 
 def same_bytes_copy(torch, dev, stream, nbytes, copies):
