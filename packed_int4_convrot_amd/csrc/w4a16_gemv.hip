@@ -8,9 +8,13 @@
 // and both sums split over any partition of the group's columns.
 //
 // The product streams the weights once, so the kernel is laid out for HBM:
-//   * wave w of a block owns columns k in [2048 w, 2048 w + 2048); lane l owns
-//     the 32 columns from 2048 w + 32 l (half a group), i.e. 16 packed bytes of
-//     every weight row, so each load instruction reads 1 KiB of one row;
+//   * lanes own KL = 32 or 16 columns: wave w of a block owns columns k in
+//     [64 KL w, 64 KL (w + 1)); lane l owns the KL columns from 64 KL w + KL l
+//     (half or a quarter of a group), i.e. KL / 2 packed bytes of every weight
+//     row, so each load instruction reads 1 KiB or 512 bytes of one row.  The
+//     launcher takes the width that leaves fewer lanes past K (K = 3072: three
+//     waves of 16-column lanes, all busy, instead of two waves of 32-column
+//     lanes with half of the second idle);
 //   * a block owns 8 consecutive weight rows n0 .. n0 + 7; a lane loads its
 //     activations, then the 8 scales and 8 zero points of its group for those
 //     rows (one 16-byte load each, N contiguous), then the 8 weight rows.
@@ -42,21 +46,23 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
 }
 
-template <int M>
+template <int M, int KL>
 __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int K, const uint8_t *__restrict__ packed, int64_t ldw,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros, int N,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int64_t ldo)
 {
     constexpr int R = kRows;
+    constexpr int NQ = KL / 8;  // 8-column units (weight dwords) per lane
+    static_assert(KL == 32 || KL == 16, "lane width");
     __shared__ uint32_t s_red[kMaxWaves][R][M];
 
     const int nw = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int n0 = xcd_block(blockIdx.x, gridDim.x) * R;
-    const int kbase = 2048 * wave + 32 * lane;
+    const int kbase = kWave * KL * wave + KL * lane;
     const bool active = kbase < K;
-    const int kc = active ? kbase : K - 32;  // clamped: every address stays inside the row
+    const int kc = active ? kbase : K - KL;  // clamped: every address stays inside the row
     const int64_t g = kc / 64;
 
     // Activation rows are handled in passes of up to 4 against the weight
@@ -66,22 +72,30 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
 
     // 1. Loads: the first pass's activations, then the group's scales and zero
     //    points, then the weights.
-    u32x4 xr[MC][4];
+    u32x4 xr[MC][NQ];
     auto load_x = [&](int mb) {
 #pragma unroll
         for (int m = 0; m < MC; ++m)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < NQ; ++c)
                 xr[m][c] = mb + m < M ? *reinterpret_cast<const u32x4 *>(x + (int64_t)(mb + m) * ldx + kc + 8 * c)
                                       : u32x4{0u, 0u, 0u, 0u};
     };
     load_x(0);
     const u32x4 sv = *reinterpret_cast<const u32x4 *>(scales + g * N + n0);
     const u32x4 zv = *reinterpret_cast<const u32x4 *>(zeros + g * N + n0);
-    u32x4 wv[R];
+    uint32_t wv[R][NQ];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        wv[r] = load_nt16(packed + (int64_t)(n0 + r) * ldw + kc / 2);
+    for (int r = 0; r < R; ++r) {
+        const uint8_t *src = packed + (int64_t)(n0 + r) * ldw + kc / 2;
+        if constexpr (KL == 32) {
+            const u32x4 t = load_nt16(src);
+            wv[r][0] = t[0], wv[r][1] = t[1], wv[r][2] = t[2], wv[r][3] = t[3];
+        } else {
+            const u32x2 t = load_nt8(src);
+            wv[r][0] = t[0], wv[r][1] = t[1];
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads in this order
 
     const int row = lane >> 3;
@@ -95,12 +109,12 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
             load_x(mb);
         }
         // 2. Activation pairs in the nibble order, and the lane's activation sums.
-        uint32_t xp[MC][16];
+        uint32_t xp[MC][4 * NQ];
         float xs[MC];
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NQ; ++i) {
                 const u32x4 w = xr[m][i];  // bf16 of columns kc + 8 i .. + 7
                 xp[m][4 * i + 0] = active ? perm(w[1], w[0], 0x05040100u) : 0u;  // (x0, x2)
                 xp[m][4 * i + 1] = active ? perm(w[3], w[2], 0x05040100u) : 0u;  // (x4, x6)
@@ -109,7 +123,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
             }
             float t = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
+            for (int j = 0; j < 4 * NQ; ++j)
                 t = dot2(xp[m][j], 0x3F803F80u, t);  // bf16 (1, 1)
             xs[m] = t;
         }
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void w4a16_gemv_kernel(
             for (int m = 0; m < MC; ++m)
                 acc[m] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NQ; ++i) {
                 const uint32_t lo = wv[r][i] & 0x0f0f0f0fu;         // q of k = 0, 2, 4, 6
                 const uint32_t hi = (wv[r][i] >> 4) & 0x0f0f0f0fu;  // q of k = 1, 3, 5, 7
                 const uint32_t w0 = perm(0x43434343u, lo, 0x04010400u);  // bf16(128+q) of (k0, k2)
@@ -177,10 +191,18 @@ hipError_t launch_m(const uint16_t *x, int64_t ldx, int K, const uint8_t *packed
                     const uint16_t *scales, const uint16_t *zeros, int N, const uint16_t *bias,
                     uint16_t *out, int64_t ldo, hipStream_t s)
 {
+    // Lane width: 16 columns where that leaves fewer lanes past K and the block
+    // stays within kMaxWaves waves, else 32.
+    const int w32 = (K + 2047) / 2048, w16 = (K + 1023) / 1024;
+    const bool narrow = w16 <= kMaxWaves && 1024 * w16 - K < 2048 * w32 - K;
     const dim3 grid((unsigned)(N / kRows));
-    const dim3 block((unsigned)(kWave * ((K + 2047) / 2048)));
-    hipLaunchKernelGGL((w4a16_gemv_kernel<M>), grid, block, 0, s, x, ldx, K, packed, ldw, scales, zeros,
-                       N, bias, out, ldo);
+    const dim3 block((unsigned)(kWave * (narrow ? w16 : w32)));
+    if (narrow)
+        hipLaunchKernelGGL((w4a16_gemv_kernel<M, 16>), grid, block, 0, s, x, ldx, K, packed, ldw, scales, zeros,
+                           N, bias, out, ldo);
+    else
+        hipLaunchKernelGGL((w4a16_gemv_kernel<M, 32>), grid, block, 0, s, x, ldx, K, packed, ldw, scales, zeros,
+                           N, bias, out, ldo);
     return hipGetLastError();
 }
 

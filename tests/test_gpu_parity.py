@@ -748,8 +748,11 @@ def test_binding_rejects_mis_sized_tensors():
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 3072, 1024), (3, 1024, 272), (8, 4096, 64), (1, 64, 16),
-                                   (2, 10240, 48), (5, 3072, 32), (7, 16384, 16), (4, 2112, 80)])
+                                   (2, 10240, 48), (5, 3072, 32), (7, 16384, 16), (4, 2112, 80),
+                                   (2, 7168, 32), (6, 1088, 48)])
 def test_awq_gemv_matches_oracle(M, K, N):
+    """Both lane widths: 16-column lanes where they leave fewer lanes past K (K = 64,
+    1024, 1088, 2112, 3072, 7168), 32-column lanes otherwise (K = 4096, 10240, 16384)."""
     d = workloads.awq_inputs(M, K, N, seed=K + N, with_bias=(M == 3))
     out = ck.w4a16_gemv(bf16_dev(d["x"]), u8_dev(d["packed"]), bf16_dev(d["scales"]), bf16_dev(d["zeros"]),
                         bias=None if d["bias"] is None else bf16_dev(d["bias"]))
