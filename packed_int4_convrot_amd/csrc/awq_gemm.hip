@@ -337,11 +337,17 @@ int launch_awq_gemm(const uint16_t *x, int M, int K, int64_t ldx, const uint8_t 
         return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // 256 x 256 tiles (one wave per SIMD, each dequantised weight fragment
-    // reused for 8 row tiles) when they fill the chip; 128 x 128 tiles for
-    // fewer rows, where the larger tiles leave most CUs idle.
-    constexpr int kCus = 256;
-    const int big = ((M + 255) / 256) * ((N + 255) / 256);
-    if (big >= kCus)
+    // reused for 8 row tiles) or 128 x 128 tiles (two blocks per CU).  The
+    // time is about the tiles per CU times the time of one tile, and a large
+    // tile measured about 3.1 times a small one (four times the work), so the
+    // large tiles win unless their last round leaves much of the chip idle:
+    // M = 1024, N = 18432 makes 288 large tiles (two rounds, 185 us) or 1152
+    // small ones (4.5 per CU, 151 us); M = 4096 makes 1152 large tiles (475 us)
+    // or 4608 small ones (550 us).
+    constexpr int64_t kCus = 256;
+    const int64_t big = ((M + 255) / 256) * (int64_t)((N + 255) / 256);
+    const int64_t small = ((M + 127) / 128) * (int64_t)((N + 127) / 128);
+    if (31 * ((big + kCus - 1) / kCus) <= 10 * ((small + kCus - 1) / kCus))
         return (int)launch_shape<8, 2, 4>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
     return (int)launch_shape<4, 1, 4>(x, M, K, ldx, packed, ldw, scales, zeros, N, bias, out, ldo, s);
 }

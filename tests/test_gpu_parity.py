@@ -881,10 +881,12 @@ def test_awq_gemm_without_bias_strided_and_near_the_gemv():
     assert (np.abs(g - v) <= bound + 2.0 ** -7 * np.abs(v)).all()
 
 
-@pytest.mark.parametrize("M,K,N", [(4096, 512, 4096), (4100, 320, 4112)])
+@pytest.mark.parametrize("M,K,N", [(4096, 512, 4096), (4100, 320, 18448), (1024, 320, 18448)])
 def test_awq_gemm_large_tiles_sampled_rows(M, K, N):
-    """Shapes that fill the chip with 256 x 256 tiles (the prefill configuration),
-    ragged in M and N, checked on sampled rows that include the last tile's."""
+    """Shapes that fill the chip: 256 x 256 tiles (the prefill configuration; one
+    round, and five rounds ragged in M and N) and 128 x 128 tiles where the large
+    ones would leave most of their second round idle (1024 x 18448), checked on
+    sampled rows that include the last tile's."""
     x, packed, s, z, bias = _awq_inputs(M, K, N, seed=M + N)
     out = host(ck.w4a16_gemm(bf16_dev(x), u8_dev(packed), bf16_dev(s), bf16_dev(z), bias=bf16_dev(bias)))
     rows = np.unique(np.concatenate([np.arange(0, M, 97), np.arange(M - 8, M), [255, 256]]))
