@@ -562,6 +562,22 @@ hipError_t launch_t(const int8_t *codes, int64_t ldq, const float *rs, int M, in
 
 }  // namespace
 
+// Per-channel results: 256 x 256 tiles, or 128 x 128 tiles (two blocks per
+// CU) where the large ones would leave much of the chip idle.  The time is
+// about the tiles per CU times the time of one tile; kSmallTileCost is a small
+// tile's time in tenths of a large tile's (W4A4, K = 3840, N = 3840: about 16.5
+// against 48 us, a quarter of the work).  Measured there: M = 1024 18.5
+// against 39.2 us, M = 2048 33.5 against 41.0; M = 3072 / 4096 / 8192 keep the
+// large tiles (43.0 / 49.0 / 96 against 49.2 / 64 / 123 us).
+constexpr int64_t kSmallTileCost = 4;
+bool small_tiles(int M, int N)
+{
+    constexpr int64_t kCus = 256;
+    const int64_t big = ((M + 255) / 256) * (int64_t)((N + 255) / 256);
+    const int64_t small = ((M + 127) / 128) * (int64_t)((N + 127) / 128);
+    return kSmallTileCost * ((small + kCus - 1) / kCus) < 10 * ((big + kCus - 1) / kCus);
+}
+
 int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, int M, int K,
                    const uint8_t *packed, int64_t ldw, const uint16_t *w_scales, bool per_group,
                    int N, const uint16_t *bias, float x_scale, uint16_t *out, int64_t ldo,
@@ -579,6 +595,10 @@ int launch_w4_gemm(const int8_t *codes, int64_t ldq, const float *row_scales, in
         return (int)launch_t<2, 4, 2, 2, 2, true, false, A4>(codes, ldq, row_scales, M, K, packed, ldw, \
                                                              w_scales, N, bias, x_scale, out, ldo,      \
                                                              acc_out, lda, s);                          \
+    if (small_tiles(M, N))                                                                              \
+        return (int)launch_t<2, 4, 2, 1, (A4 ? 4 : 2), false, false, A4>(codes, ldq, row_scales, M, K, packed, \
+                                                              ldw, w_scales, N, bias, x_scale, out, ldo, \
+                                                              acc_out, lda, s);                         \
     return (int)launch_t<2, 4, 4, 2, (A4 ? 4 : 2), false, false, A4>(codes, ldq, row_scales, M, K, packed, ldw,    \
                                                           w_scales, N, bias, x_scale, out, ldo,         \
                                                           acc_out, lda, s);

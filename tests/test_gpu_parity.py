@@ -881,6 +881,25 @@ def test_awq_gemm_without_bias_strided_and_near_the_gemv():
     assert (np.abs(g - v) <= bound + 2.0 ** -7 * np.abs(v)).all()
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M,K,N", [(8200, 320, 3856), (1000, 448, 3856)])
+def test_gemm_tile_choice_ragged_sampled_rows(M, K, N, bits):
+    """Per-channel tiled GEMM on both tile sizes with ragged M and N: 8200 x 3856 takes
+    the 256 x 256 tiles (three rounds), 1000 x 3856 the 128 x 128 ones; byte codes
+    (ck_w4_gemm_q) and packed W4A4 codes (the whole linear).  Checked on sampled rows
+    that include the last tile's against the oracle, and the two code forms against
+    each other bit for bit."""
+    inp = workloads.linear_inputs(M, K, N, seed=M + N + bits, outliers=4, scale="channel", zero_rows=(M - 1,))
+    xd, wd, sd = bf16_dev(inp["x"]), u8_dev(inp["packed"]), bf16_dev(inp["w_scales"])
+    codes, scales = ck.rotate_quant(xd, 64, bits)
+    out = ck.gemm_q(codes, scales, wd, sd, False)
+    rows = np.unique(np.concatenate([np.arange(0, M, 131), np.arange(M - 8, M), [127, 128, 255, 256]]))
+    ref = oracle.gemm_q(host(codes)[rows], host(scales)[rows], inp["packed"], inp["w_scales"], False)
+    assert_output_close(host(out)[rows], ref)
+    if bits == 4:
+        assert torch.equal(ck.linear(xd, 64, 4, wd, sd, False), out)
+
+
 @pytest.mark.parametrize("M,K,N", [(4096, 512, 4096), (4100, 320, 18448), (1024, 320, 18448)])
 def test_awq_gemm_large_tiles_sampled_rows(M, K, N):
     """Shapes that fill the chip: 256 x 256 tiles (the prefill configuration; one
